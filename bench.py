@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the virtual-rank all-reduce on one MI355X.
+
+Default workload: fused all-reduce (sum) of 8 virtual ranks x 512 MiB bf16
+(268,435,456 elements per rank, N(0, 0.01^2) with 1% +-100 outliers), all
+buffers resident in the GPU's HBM before timing starts.  One step = one call
+of vrc_allreduce (chunk partition on the host, one fused launch that reads
+every input once and writes every output once).
+
+Prints ONE JSON line.  `value` is algorithmic HBM throughput of the whole
+timed region: 2*N*S bytes per step (read N inputs, write N outputs) over the
+wall time per step.  `roofline.achieved` uses the average kernel time from
+HIP events recorded on the launch stream; `roofline.traffic` is the measured
+HBM bytes per launch from the committed rocprofv3 counter summary, reported
+only while the kernel sources still hash to the value recorded with it.
+`cpu_baseline` times the CPU oracle (single thread) on a bounded slice of the
+same inputs.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode fused|ring]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+CSRC = os.path.join(ROOT, "ring_all_reduce_virtual_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def alg_bytes(mode: str, n: int, size_bytes: int) -> int:
+    """Bytes each mode must move per all-reduce.  Fused: read N inputs and
+    write N outputs.  Ring: N-1 reduce-scatter steps read two chunks and
+    write one per rank (3S per step), N-1 all-gather steps read and write one
+    chunk per rank (2S per step)."""
+    if mode == "fused":
+        return 2 * n * size_bytes
+    return 5 * (n - 1) * size_bytes
+
+
+def recorded_traffic(workload: str, mode: str):
+    """Measured HBM bytes per launch from profiles/<kernel>_<workload>_counters.md,
+    if those counters were taken on the current kernel sources."""
+    path = os.path.join(PROFILES, f"{mode}_allreduce_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_fetch = re.search(r"fetch_bytes_per_launch:\s*([0-9]+)", text)
+    m_write = re.search(r"write_bytes_per_launch:\s*([0-9]+)", text)
+    if not (m_hash and m_fetch and m_write) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return int(m_fetch.group(1)) + int(m_write.group(1))
+
+
+def time_calls(fn, steps: int, warmup: int, torch):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        starts[k].record(stream)
+        fn()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, kms
+
+
+def cpu_baseline(xs, w, mode: str):
+    """The oracle as it stands, single-threaded, on the first 1/8 of every
+    rank's buffer (inputs copied to the host beforehand, not timed)."""
+    import oracle
+    import workloads
+
+    orc = oracle.get()
+    sample = max(1, w.count // 8)
+    hx = [workloads.to_numpy(x.reshape(-1)[:sample]) for x in xs]
+    fn = orc.fused_allreduce if mode == "fused" else orc.ring_allreduce
+    t0 = time.perf_counter()
+    fn(hx, w.dtype)
+    dt = time.perf_counter() - t0
+    gbs = alg_bytes(mode, w.n, sample * w.esize) / dt / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {sample} of {w.count} elements of each of the {w.n} ranks "
+                   f"({mode} oracle, {dt:.2f} s single-threaded; same algorithmic-byte numerator)"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 8 x 512 MiB bf16 all-reduce)")
+    ap.add_argument("--mode", default="fused", choices=["fused", "ring"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra ring-mode timing")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs N virtual ranks on ONE GPU; --gpus must be 1 "
+              f"(got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+
+    import ring_all_reduce_virtual_amd as vrc
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr, flush=True)
+        return 1
+    w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+    if w.collective != "allreduce":
+        print("bench.py: only all-reduce workloads are benchmarked", file=sys.stderr, flush=True)
+        return 2
+    dev = "cuda:0"
+    size = w.count * w.esize
+    log(f"workload {w.name}: {w.n} ranks x {size / 2**20:.0f} MiB {w.dtype}, mode {args.mode}")
+    xs = workloads.make_inputs(w, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    torch.cuda.synchronize()
+    log("inputs resident in HBM")
+
+    def step():
+        vrc.vrc_allreduce(xs, recv=ys, mode=args.mode)
+
+    wall, kms = time_calls(step, args.steps, args.warmup, torch)
+    nbytes = alg_bytes(args.mode, w.n, size)
+    ms_per_step = wall * 1e3 / args.steps
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    kavg = sum(kms) / len(kms)
+    achieved = nbytes / (kavg * 1e-3) / 1e9
+    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel avg {kavg:.4f} ms "
+        f"min {min(kms):.4f} ms -> {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of peak)")
+
+    extra = {"kernel_ms_avg": round(kavg, 5), "kernel_ms_min": round(min(kms), 5),
+             "alg_bytes_per_step": nbytes, "kernel_source_sha256_16": kernel_source_hash()}
+    if not args.no_extra:
+        other = "ring" if args.mode == "fused" else "fused"
+
+        def step_other():
+            vrc.vrc_allreduce(xs, recv=ys, mode=other)
+
+        k2 = max(3, min(args.steps, 10))
+        wall2, kms2 = time_calls(step_other, k2, 2, torch)
+        nb2 = alg_bytes(other, w.n, size)
+        extra[f"{other}_mode"] = {
+            "steps": k2, "ms_per_step": round(wall2 * 1e3 / k2, 5),
+            "GB_per_s": round(nb2 / (wall2 / k2) / 1e9, 2), "alg_bytes_per_step": nb2,
+            "launches_per_step": 2 * (w.n - 1) if other == "ring" else 1,
+        }
+        log(f"{other} mode: {extra[f'{other}_mode']}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a slice of the inputs")
+        cpu = cpu_baseline(xs, w, args.mode)
+        log(f"cpu baseline {cpu['value']} GB/s")
+
+    out = {
+        "metric": "emulated all-reduce HBM GB/s and % of peak, 8 ranks x 512 MB; bit-exact/tol",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "collective": "allreduce", "mode": args.mode, "n_ranks": w.n,
+                   "elements_per_rank": w.count, "bytes_per_rank": size, "values": w.note,
+                   "parallelism": f"{w.n} virtual ranks in one GPU's HBM"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(w.name, args.mode)},
+        "cpu_baseline": cpu,
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,162 @@
+/*
+ * vrc.h -- virtual-rank collectives on one AMD Instinct MI355X (gfx950).
+ *
+ * N "virtual ranks" are N equally sized buffers that all live in the HBM of
+ * the one GPU the calls run on.  The library runs the ring all-reduce and
+ * its reduce-scatter and all-gather halves over them with hand-written HIP
+ * kernels.  Two kernel families are offered:
+ *
+ *   VRC_RING  - step-faithful ring: one chunk-add launch per reduce-scatter
+ *               step and one chunk-copy launch per all-gather step, in the
+ *               chunk order of the ring schedule below;
+ *   VRC_FUSED - one launch that reads every input once, accumulates in fp32
+ *               (uint32 for int32) and writes every output once (the naive
+ *               "one collector sums and hands the result back" all-reduce).
+ *
+ * Sources (pages are named by address; sections by their heading):
+ *   [RS]    ai6s.net/6a102b5410ee7a33f2746c06.html, "hcomm 与 HCCL 的关系":
+ *           AllReduce = ReduceScatter + AllGather; the simplified
+ *           ReduceScatter listing (send/recv one chunk per step, add the
+ *           received chunk, move both chunk indices down by one).
+ *   [RING]  hwcomputing.csdn.net/6a0dc11a10ee7a33f273f7fd.html, "Ring
+ *           通信为什么常见": logical ring 0->1->..->N-1->0, N blocks, N-1
+ *           reduce-scatter steps and N-1 all-gather steps, traffic
+ *           2(N-1)*S/N per rank.
+ *   [NAIVE] same page, "为什么大模型训练离不开通信": the collector all-reduce.
+ *   [REM]   ai6s.net/6a157e6510ee7a33f27553e9.html, "自定义通信模式": equal
+ *           chunks, the last chunk takes the remainder.
+ *   [TP]    ai6s.net/6a0dd5b5662f9a54cb75ef90.html, "TP 通信": all-reduce of
+ *           activations and all-gather along a dimension.
+ *   [INFER] ai6s.net/6a102b5410ee7a33f2746c06.html, "分布式推理中的通信" and
+ *           "hcomm 在推理场景中的使用": all-gather of attention-head slices;
+ *           AllGather(send_buf, recv_buf, count, comm).
+ *   [OVERLAP] www.bjdmk.com.cn/news/5966809/, section 4 (compute/comm
+ *           overlap): collectives are enqueued on a stream.
+ *
+ * Chunking.  A buffer of `count` elements has chunks c = 0..N-1: with
+ * base = count / N, chunk c is [c*base, (c+1)*base) for c < N-1 and the last
+ * chunk is [(N-1)*base, count) [REM].  Chunks are empty when count < N.
+ *
+ * Ring schedule [RS][RING].  Reduce-scatter step s = 0..N-2: rank r adds
+ * the partial of chunk (r-1-s) held by rank r-1 into its own copy.  After
+ * step N-2 rank r holds the complete chunk r+1.  All-gather step s: rank r
+ * copies chunk (r-s) from rank r-1.  Every chunk c is therefore summed as
+ * ((x_c + x_{c+1}) + x_{c+2}) + ... + x_{c+N-1} (indices mod N), each
+ * partial rounded to the storage type.
+ *
+ * Arithmetic.  int32: two's-complement wrap.  fp32: IEEE add, round to
+ * nearest even, no FMA, denormals kept.  fp16/bf16: widen exactly to fp32,
+ * add in fp32, round to nearest even into the storage type (ring mode
+ * rounds every partial; fused mode rounds once after the rank-order fold
+ * x_0 + x_1 + ... + x_{N-1}).
+ *
+ * Conventions shared by all calls.
+ *   send, recv  Host arrays of `nranks` DEVICE pointers (rank r's input and
+ *               output).  The arrays are read during the call only; the
+ *               buffers stay owned by the caller.  The library allocates no
+ *               memory and keeps no pointer after returning.
+ *   count       Elements per rank INPUT buffer.
+ *   stream      A hipStream_t (NULL = the null stream) on the current device.
+ *               Work is enqueued asynchronously; the call returns before it
+ *               finishes.  Errors raised by running kernels surface at the
+ *               caller's next synchronisation, not here.
+ *   Alignment   Any element-aligned pointer works.  16-byte vector loads and
+ *               stores are used where every operand of a chunk shares the
+ *               same address offset modulo 16; otherwise a scalar path runs.
+ *   Errors      Argument errors return before anything is enqueued.
+ *   Threads     Calls are re-entrant and thread-safe; calls that overlap on
+ *               the same buffers race like any two kernels would.
+ */
+#ifndef VRC_H
+#define VRC_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VRC_VERSION 100 /* 1.0.0 */
+#define VRC_MAX_RANKS 16
+
+struct ihipStream_t;
+typedef struct ihipStream_t* vrc_stream_t; /* the same type as hipStream_t */
+
+typedef enum { VRC_INT32 = 0, VRC_FP32 = 1, VRC_FP16 = 2, VRC_BF16 = 3 } vrc_dtype_t;
+typedef enum { VRC_SUM = 0 } vrc_op_t;
+typedef enum { VRC_RING = 0, VRC_FUSED = 1 } vrc_mode_t;
+
+typedef enum {
+    VRC_OK = 0,
+    VRC_ERR_INVALID_ARG = 1, /* null array/pointer, nranks out of range, bad shape */
+    VRC_ERR_UNSUPPORTED = 2, /* unknown dtype, op or mode */
+    VRC_ERR_ALIAS = 3,       /* buffers overlap in a way the call does not allow */
+    VRC_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} vrc_status_t;
+
+/*
+ * All-reduce (sum) [RS][RING][NAIVE][TP].
+ *   recv[r][i] = sum over ranks q of send[q][i], for every rank r.
+ *   send[r], recv[r]: `count` elements each, flat.
+ *   nranks in [1, VRC_MAX_RANKS].  nranks == 1 copies (no-op in place).
+ *   In place is allowed per rank (recv[r] == send[r]); any other overlap
+ *   between a recv buffer and any other buffer returns VRC_ERR_ALIAS.
+ *   VRC_RING enqueues 2*(nranks-1) kernels (nranks-1 adds, nranks-1 copies);
+ *   VRC_FUSED enqueues one.
+ *   count == 0 returns VRC_OK and enqueues nothing (null pointers allowed).
+ */
+vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
+                           vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, vrc_stream_t stream);
+
+/*
+ * Reduce-scatter (sum) [RS][REM][TP].
+ *   Each send[r] holds `count` elements viewed as [outer, count/outer].
+ *   outer == 1: recv[c] receives the reduced flat chunk c (its length is the
+ *               chunk length above; the last rank takes the remainder).
+ *   outer  > 1: (count/outer) must be divisible by nranks; chunk c is the
+ *               column block [c*w, (c+1)*w) of every row, w = count/outer/
+ *               nranks, and recv[c] is [outer, w] row-major.  This is the
+ *               reduce-scatter of a tensor along a dimension, with outer =
+ *               the product of the sizes before that dimension.
+ *   VRC_RING adds the chunk in the ring order ((x_c + x_{c+1}) + ...) and
+ *   keeps the running partial of chunk c in recv[c] (nranks-1 launches).
+ *   VRC_FUSED folds x_0 + ... + x_{N-1} in fp32 and rounds once (1 launch).
+ *   recv buffers must not overlap each other or any send buffer.
+ */
+vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int nranks,
+                                size_t count, size_t outer, vrc_dtype_t dtype, vrc_op_t op,
+                                vrc_mode_t mode, vrc_stream_t stream);
+
+/*
+ * All-gather [RING][INFER][TP].
+ *   Each send[r] holds `count` elements viewed as [outer, row], row =
+ *   count/outer.  Each recv[r] is [outer, nranks*row]: rank q's input lands
+ *   in columns [q*row, (q+1)*row).  outer == 1 is plain concatenation; outer
+ *   > 1 is concatenation along a dimension (outer = product of the sizes
+ *   before it).  Every rank receives the same bytes.
+ *   VRC_RING relays slabs around the ring (nranks-1 launches: rank r copies
+ *   slab (r-1-s) from rank r-1 at step s, and its own slab in step 0).
+ *   VRC_FUSED reads each input once and writes it to all outputs.
+ *   recv buffers must not overlap each other or any send buffer.
+ */
+vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nranks, size_t count,
+                            size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_stream_t stream);
+
+/* Offset and length (elements) of chunk `chunk` of a flat buffer of `count`
+ * elements split over `nranks` [REM].  Host-only; touches no GPU. */
+vrc_status_t vrc_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* length);
+
+/* Static, human-readable text for a status code. */
+const char* vrc_status_string(vrc_status_t status);
+
+/* HIP error code of the most recent VRC_ERR_HIP on the calling thread (0 if none). */
+int vrc_last_hip_error(void);
+
+/* VRC_VERSION of the loaded library. */
+int vrc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VRC_H */

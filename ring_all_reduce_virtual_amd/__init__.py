@@ -1,0 +1,262 @@
+"""Virtual-rank ring collectives on one MI355X: Python binding of include/vrc.h.
+
+N virtual ranks are N equally sized device buffers in one GPU's HBM.  The
+functions named like the C entry points (``vrc_allreduce``,
+``vrc_reduce_scatter``, ``vrc_all_gather``) take lists of torch tensors, one
+per rank, check shapes and marshal pointers, sizes and the current HIP
+stream into the C ABI of ``libvrc.so``; every step of the computation runs in
+that library's HIP kernels.  PyTorch only allocates memory and supplies the
+stream.  The library must have been built (``ring_all_reduce_virtual_amd.build``);
+importing the package fails loudly otherwise.
+
+Modes: ``"ring"`` is the step-faithful ring (one launch per reduce-scatter
+and per all-gather step), ``"fused"`` the single-launch N-way kernel.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvrc.so")
+
+VRC_INT32, VRC_FP32, VRC_FP16, VRC_BF16 = 0, 1, 2, 3
+VRC_SUM = 0
+VRC_RING, VRC_FUSED = 0, 1
+VRC_OK, VRC_ERR_INVALID_ARG, VRC_ERR_UNSUPPORTED, VRC_ERR_ALIAS, VRC_ERR_HIP = range(5)
+MAX_RANKS = 16
+
+MODES = {"ring": VRC_RING, "fused": VRC_FUSED}
+
+
+class VrcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.vrc_status_string(status).decode()
+        if status == VRC_ERR_HIP:
+            msg += f" (hipError {_lib.vrc_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python ring_all_reduce_virtual_amd/build.py, or __graft_entry__.build())")
+    L = C.CDLL(LIB_PATH)
+    vp, sz, i = C.c_void_p, C.c_size_t, C.c_int
+    ptrs = C.POINTER(C.c_void_p)
+    L.vrc_allreduce.argtypes = [ptrs, ptrs, i, sz, i, i, i, vp]
+    L.vrc_allreduce.restype = i
+    L.vrc_reduce_scatter.argtypes = [ptrs, ptrs, i, sz, sz, i, i, i, vp]
+    L.vrc_reduce_scatter.restype = i
+    L.vrc_all_gather.argtypes = [ptrs, ptrs, i, sz, sz, i, i, vp]
+    L.vrc_all_gather.restype = i
+    L.vrc_chunk_range.argtypes = [sz, i, i, C.POINTER(sz), C.POINTER(sz)]
+    L.vrc_chunk_range.restype = i
+    L.vrc_status_string.argtypes = [i]
+    L.vrc_status_string.restype = C.c_char_p
+    L.vrc_last_hip_error.argtypes = []
+    L.vrc_last_hip_error.restype = i
+    L.vrc_version.argtypes = []
+    L.vrc_version.restype = i
+    return L
+
+
+_lib = _load()
+
+
+def lib() -> C.CDLL:
+    """The loaded libvrc.so."""
+    return _lib
+
+
+def _ptr_array(addrs):
+    arr = (C.c_void_p * max(len(addrs), 1))()
+    for k, a in enumerate(addrs):
+        arr[k] = a
+    return arr
+
+
+# ---------------------------------------------------------------------------
+# Raw C ABI mirrors: integer device addresses in, status out.
+# ---------------------------------------------------------------------------
+def raw_allreduce(send, recv, count, dtype, mode, stream=0, op=VRC_SUM) -> int:
+    return _lib.vrc_allreduce(_ptr_array(send), _ptr_array(recv), len(send), count, dtype, op, mode,
+                              stream or None)
+
+
+def raw_reduce_scatter(send, recv, count, outer, dtype, mode, stream=0, op=VRC_SUM) -> int:
+    return _lib.vrc_reduce_scatter(_ptr_array(send), _ptr_array(recv), len(send), count, outer, dtype, op,
+                                   mode, stream or None)
+
+
+def raw_all_gather(send, recv, count, outer, dtype, mode, stream=0) -> int:
+    return _lib.vrc_all_gather(_ptr_array(send), _ptr_array(recv), len(send), count, outer, dtype, mode,
+                               stream or None)
+
+
+def chunk_range(count: int, nranks: int, chunk: int) -> tuple[int, int]:
+    off, ln = C.c_size_t(), C.c_size_t()
+    st = _lib.vrc_chunk_range(count, nranks, chunk, C.byref(off), C.byref(ln))
+    if st != VRC_OK:
+        raise VrcError(st, "vrc_chunk_range")
+    return off.value, ln.value
+
+
+def version() -> int:
+    return _lib.vrc_version()
+
+
+# ---------------------------------------------------------------------------
+# Tensor-level binding (marshalling only).
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch  # imported lazily so the raw ABI needs no torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.int32: VRC_INT32, torch.float32: VRC_FP32, torch.float16: VRC_FP16,
+             torch.bfloat16: VRC_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check_ranks(tensors, what):
+    if not isinstance(tensors, (list, tuple)) or not tensors:
+        raise ValueError(f"{what}: expected a non-empty list of tensors, one per rank")
+    if len(tensors) > MAX_RANKS:
+        raise ValueError(f"{what}: at most {MAX_RANKS} ranks")
+    t0 = tensors[0]
+    for t in tensors:
+        if t.dtype != t0.dtype or t.shape != t0.shape or t.device != t0.device:
+            raise ValueError(f"{what}: all ranks need the same dtype, shape and device")
+        if t.device.type != "cuda":
+            raise ValueError(f"{what}: tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: tensors must be contiguous")
+
+
+def _mode(mode) -> int:
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {sorted(MODES)}")
+    return MODES[mode]
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _outer(shape, dim) -> int:
+    nd = len(shape)
+    if nd == 0:
+        raise ValueError("tensors need at least one dimension")
+    d = dim % nd
+    outer = 1
+    for k in shape[:d]:
+        outer *= k
+    return outer, d
+
+
+def vrc_allreduce(send, recv=None, mode: str = "fused", stream=None):
+    """recv[r] = sum over ranks of send[r] (every rank gets the sum).
+
+    ``recv=None`` allocates outputs; ``recv=send`` runs in place.
+    """
+    torch = _torch()
+    _check_ranks(send, "vrc_allreduce")
+    if recv is None:
+        recv = [torch.empty_like(t) for t in send]
+    _check_ranks(recv, "vrc_allreduce")
+    if len(recv) != len(send) or recv[0].shape != send[0].shape or recv[0].dtype != send[0].dtype:
+        raise ValueError("vrc_allreduce: recv must match send")
+    st = raw_allreduce([t.data_ptr() for t in send], [t.data_ptr() for t in recv], send[0].numel(),
+                       _dtype_code(send[0]), _mode(mode), _stream(stream))
+    if st != VRC_OK:
+        raise VrcError(st, "vrc_allreduce")
+    return recv
+
+
+def reduce_scatter_shape(shape, nranks: int, dim: int = 0):
+    """Output shape of rank c for the reduce-scatter of `shape` along `dim`.
+
+    The last dimension of a flat (outer == 1) split may be uneven: the last
+    rank takes the remainder, so its shape is returned separately."""
+    outer, d = _outer(shape, dim)
+    if outer == 1:
+        count = 1
+        for k in shape:
+            count *= k
+        return [(chunk_range(count, nranks, c)[1],) for c in range(nranks)]
+    if shape[d] % nranks != 0:
+        raise ValueError(f"dimension {dim} ({shape[d]}) is not divisible by {nranks} ranks")
+    out = list(shape)
+    out[d] = shape[d] // nranks
+    return [tuple(out)] * nranks
+
+
+def vrc_reduce_scatter(send, recv=None, dim: int = 0, mode: str = "fused", stream=None):
+    """recv[c] = sum over ranks of chunk c of send[r].
+
+    The chunks split dimension `dim` when the sizes before it multiply to
+    more than one (``outer > 1``); otherwise the flat buffer is split into
+    equal chunks with the remainder on the last rank (recv is then 1-D)."""
+    torch = _torch()
+    _check_ranks(send, "vrc_reduce_scatter")
+    n = len(send)
+    outer, _ = _outer(send[0].shape, dim)
+    shapes = reduce_scatter_shape(tuple(send[0].shape), n, dim)
+    if recv is None:
+        recv = [torch.empty(shapes[c], dtype=send[0].dtype, device=send[0].device) for c in range(n)]
+    if len(recv) != n:
+        raise ValueError("vrc_reduce_scatter: one output per rank")
+    for c, t in enumerate(recv):
+        if t.numel() != _prod(shapes[c]) or t.dtype != send[0].dtype or not t.is_contiguous():
+            raise ValueError(f"vrc_reduce_scatter: output {c} must be contiguous {shapes[c]} {send[0].dtype}")
+    st = raw_reduce_scatter([t.data_ptr() for t in send], [t.data_ptr() for t in recv], send[0].numel(),
+                            outer, _dtype_code(send[0]), _mode(mode), _stream(stream))
+    if st != VRC_OK:
+        raise VrcError(st, "vrc_reduce_scatter")
+    return recv
+
+
+def vrc_all_gather(send, recv=None, dim: int = 0, mode: str = "fused", stream=None):
+    """recv[r] = concatenation of all send tensors along `dim`, for every rank."""
+    torch = _torch()
+    _check_ranks(send, "vrc_all_gather")
+    n = len(send)
+    outer, d = _outer(send[0].shape, dim)
+    out_shape = list(send[0].shape)
+    out_shape[d] *= n
+    if recv is None:
+        recv = [torch.empty(out_shape, dtype=send[0].dtype, device=send[0].device) for _ in range(n)]
+    if len(recv) != n:
+        raise ValueError("vrc_all_gather: one output per rank")
+    for t in recv:
+        if list(t.shape) != out_shape or t.dtype != send[0].dtype or not t.is_contiguous():
+            raise ValueError(f"vrc_all_gather: outputs must be contiguous {out_shape} {send[0].dtype}")
+    st = raw_all_gather([t.data_ptr() for t in send], [t.data_ptr() for t in recv], send[0].numel(), outer,
+                        _dtype_code(send[0]), _mode(mode), _stream(stream))
+    if st != VRC_OK:
+        raise VrcError(st, "vrc_all_gather")
+    return recv
+
+
+def _prod(shape) -> int:
+    p = 1
+    for k in shape:
+        p *= k
+    return p
+
+
+__all__ = [
+    "vrc_allreduce", "vrc_reduce_scatter", "vrc_all_gather", "reduce_scatter_shape", "chunk_range",
+    "version", "raw_allreduce", "raw_reduce_scatter", "raw_all_gather", "lib", "VrcError",
+    "VRC_INT32", "VRC_FP32", "VRC_FP16", "VRC_BF16", "VRC_SUM", "VRC_RING", "VRC_FUSED", "VRC_OK",
+    "VRC_ERR_INVALID_ARG", "VRC_ERR_UNSUPPORTED", "VRC_ERR_ALIAS", "VRC_ERR_HIP", "MAX_RANKS",
+]

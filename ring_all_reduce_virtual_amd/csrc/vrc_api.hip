@@ -1,0 +1,616 @@
+// vrc_api.hip -- the C ABI of include/vrc.h: argument checks, chunk
+// partition, ring schedule, launch sizing and dtype/N dispatch.
+//
+// The schedule follows the pages cited in vrc.h: reduce-scatter step s has
+// rank r add the partial of chunk (r-1-s) held by rank r-1 into its own
+// copy (ai6s.net/6a102b5410ee7a33f2746c06.html, "hcomm 与 HCCL 的关系",
+// ReduceScatter listing; hwcomputing.csdn.net/6a0dc11a10ee7a33f273f7fd.html,
+// "Ring 通信为什么常见"), and all-gather step s has rank r copy chunk (r-s)
+// from rank r-1.  A "send" is the receiving rank's kernel reading the
+// neighbour's buffer in place (the zero-copy path of the first page's
+// "hcomm 的数据传输路径" section): every virtual rank lives in this GPU's HBM.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "vrc.h"
+#include "vrc_kernels.hpp"
+
+namespace {
+
+using vrc::kBlock;
+using vrc::kMaxRanks;
+using vrc::RowSplit;
+
+thread_local int g_last_hip_error = 0;
+
+// ----------------------------------------------------------------------------
+// Device facts and launch tuning
+// ----------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int env_int(const char* name, int dflt, int lo, int hi)
+{
+    const char* s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    char* end = nullptr;
+    long v = std::strtol(s, &end, 10);
+    if (end == s || v < lo || v > hi) return dflt;
+    return (int)v;
+}
+
+struct Tuning {
+    int blocks_per_cu;  // resident workgroups per CU the grid is sized for
+    int unroll;         // independent vectors per lane per fused iteration
+    int nontemporal;    // 1: streaming loads/stores carry the non-temporal hint
+};
+
+const Tuning& tuning()
+{
+    static const Tuning t = {env_int("VRC_BLOCKS_PER_CU", 8, 1, 64), env_int("VRC_UNROLL", 1, 1, 4),
+                             env_int("VRC_NT", 1, 0, 1)};
+    return t;
+}
+
+hipError_t cu_count(int* out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) {
+        int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (c < 1) c = 1;
+    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
+    *out = c;
+    return hipSuccess;
+}
+
+// Grid x for `ops` operations of at most `work` lane-items each.
+unsigned grid_x(int cus, uint64_t work, int ops)
+{
+    const uint64_t want = (work + kBlock - 1) / kBlock;
+    uint64_t cap = (uint64_t)cus * (uint64_t)tuning().blocks_per_cu / (uint64_t)(ops > 0 ? ops : 1);
+    if (cap < 1) cap = 1;
+    uint64_t g = want < cap ? want : cap;
+    if (g < 1) g = 1;
+    if (g > 0x7fffffffull) g = 0x7fffffffull;
+    return (unsigned)g;
+}
+
+vrc_status_t check_launch()
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return VRC_ERR_HIP;
+    }
+    return VRC_OK;
+}
+
+vrc_status_t hip_fail(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return VRC_ERR_HIP;
+}
+
+// ----------------------------------------------------------------------------
+// Element sizes, chunking, alignment split
+// ----------------------------------------------------------------------------
+int esize(vrc_dtype_t dt)
+{
+    switch (dt) {
+    case VRC_INT32: return 4;
+    case VRC_FP32: return 4;
+    case VRC_FP16: return 2;
+    case VRC_BF16: return 2;
+    }
+    return 0;
+}
+
+int mod(int a, int n) { return ((a % n) + n) % n; }
+
+// Flat chunk c of `count` elements over n ranks: equal chunks of count/n,
+// the last one takes the remainder.
+void chunk_range(uint64_t count, int n, int c, uint64_t* off, uint64_t* len)
+{
+    const uint64_t base = count / (uint64_t)n;
+    *off = (uint64_t)c * base;
+    *len = (c == n - 1) ? count - base * (uint64_t)(n - 1) : base;
+}
+
+// Split rows of `width` elements whose operands start at `addr[0..np)` into
+// a scalar head, 16-byte vectors and a scalar tail.  Vectors are only used
+// when every operand has the same address offset modulo 16 and (for more
+// than one row) every row stride is a multiple of 16 bytes.
+RowSplit split_rows(const uintptr_t* addr, int np, uint64_t rows, const uint64_t* stride_bytes, int ns,
+                    uint64_t width, int esz)
+{
+    RowSplit g = {width, 0, 0};
+    const uintptr_t res = addr[0] & 15u;
+    if (res % (uintptr_t)esz) return g;
+    for (int i = 1; i < np; i++)
+        if ((addr[i] & 15u) != res) return g;
+    if (rows > 1)
+        for (int i = 0; i < ns; i++)
+            if (stride_bytes[i] & 15u) return g;
+    uint64_t head = ((16u - res) & 15u) / (uint64_t)esz;
+    if (head > width) head = width;
+    const uint64_t vec = 16u / (uint64_t)esz;
+    g.head = head;
+    g.nvb = (width - head) / vec;
+    g.tail = width - head - g.nvb * vec;
+    return g;
+}
+
+bool overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb)
+{
+    if (na == 0 || nb == 0) return false;
+    return a < b + nb && b < a + na;
+}
+
+// Validation shared by the three calls.  recv_bytes[r] is rank r's output
+// size.  allow_in_place: recv[r] == send[r] is accepted (all-reduce only).
+vrc_status_t check_buffers(const void* const* send, void* const* recv, int n, uint64_t send_bytes,
+                           const uint64_t* recv_bytes, bool allow_in_place)
+{
+    for (int r = 0; r < n; r++) {
+        if (send_bytes && !send[r]) return VRC_ERR_INVALID_ARG;
+        if (recv_bytes[r] && !recv[r]) return VRC_ERR_INVALID_ARG;
+    }
+    for (int r = 0; r < n; r++) {
+        const uintptr_t d = (uintptr_t)recv[r];
+        for (int q = 0; q < n; q++) {
+            const uintptr_t s = (uintptr_t)send[q];
+            if (q == r && allow_in_place && s == d) continue;
+            if (overlap(d, recv_bytes[r], s, send_bytes)) return VRC_ERR_ALIAS;
+            if (q != r && overlap(d, recv_bytes[r], (uintptr_t)recv[q], recv_bytes[q])) return VRC_ERR_ALIAS;
+        }
+    }
+    return VRC_OK;
+}
+
+vrc_status_t check_common(const void* const* send, void* const* recv, int n, vrc_dtype_t dtype)
+{
+    if (!send || !recv) return VRC_ERR_INVALID_ARG;
+    if (n < 1 || n > kMaxRanks) return VRC_ERR_INVALID_ARG;
+    if (esize(dtype) == 0) return VRC_ERR_UNSUPPORTED;
+    return VRC_OK;
+}
+
+// ----------------------------------------------------------------------------
+// Typed launchers
+// ----------------------------------------------------------------------------
+template <class T>
+struct Launch {
+    static constexpr int E = T::ESZ;
+
+    template <bool ADD>
+    static vrc_status_t step(const vrc::StepArgs& args, int nops, uint64_t work, int cus, hipStream_t st)
+    {
+        const dim3 grid(grid_x(cus, work, nops), (unsigned)nops);
+        if (tuning().nontemporal)
+            hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true>), grid, dim3(kBlock), 0, st, args);
+        else
+            hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, false>), grid, dim3(kBlock), 0, st, args);
+        return check_launch();
+    }
+
+    // Work items of one operation: vectors plus scalar slots.
+    static uint64_t op_work(const vrc::StepOp& op) { return op.rows * (op.g.nvb + op.g.head + op.g.tail); }
+
+    static vrc::StepOp make_op(const char* a, const char* b, char* d, uint64_t rows, uint64_t width,
+                               uint64_t sa, uint64_t sb, uint64_t sd)
+    {
+        vrc::StepOp op;
+        op.a = a;
+        op.b = b ? b : a;
+        op.d = d;
+        op.rows = rows;
+        op.width = width;
+        op.sa = sa;
+        op.sb = b ? sb : sa;
+        op.sd = sd;
+        const uintptr_t addr[3] = {(uintptr_t)a, (uintptr_t)op.b, (uintptr_t)d};
+        const uint64_t strides[3] = {sa * E, op.sb * E, sd * E};
+        op.g = split_rows(addr, 3, rows, strides, 3, width, E);
+        return op;
+    }
+
+    static vrc_status_t copy(const char* a, char* d, uint64_t rows, uint64_t width, uint64_t sa, uint64_t sd,
+                             int cus, hipStream_t st)
+    {
+        vrc::StepArgs args;
+        args.op[0] = make_op(a, nullptr, d, rows, width, sa, 0, sd);
+        return step<false>(args, 1, op_work(args.op[0]), cus, st);
+    }
+
+    // Ring all-reduce: N-1 reduce-scatter launches, then N-1 all-gather launches.
+    static vrc_status_t ring_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
+                                       hipStream_t st)
+    {
+        if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc::StepArgs args;
+        for (int s = 0; s < n - 1; s++) {
+            uint64_t work = 0;
+            for (int r = 0; r < n; r++) {
+                const int c = mod(r - 1 - s, n);
+                const int p = mod(r - 1, n);
+                uint64_t off, len;
+                chunk_range(count, n, c, &off, &len);
+                const char* partial = (s == 0 ? x[p] : y[p]) + off * E;
+                args.op[r] = make_op(partial, x[r] + off * E, y[r] + off * E, 1, len, 0, 0, 0);
+                const uint64_t w = op_work(args.op[r]);
+                if (w > work) work = w;
+            }
+            vrc_status_t rc = step<true>(args, n, work, cus, st);
+            if (rc) return rc;
+        }
+        for (int s = 0; s < n - 1; s++) {
+            uint64_t work = 0;
+            for (int r = 0; r < n; r++) {
+                const int c = mod(r - s, n);
+                uint64_t off, len;
+                chunk_range(count, n, c, &off, &len);
+                args.op[r] = make_op(y[mod(r - 1, n)] + off * E, nullptr, y[r] + off * E, 1, len, 0, 0, 0);
+                const uint64_t w = op_work(args.op[r]);
+                if (w > work) work = w;
+            }
+            vrc_status_t rc = step<false>(args, n, work, cus, st);
+            if (rc) return rc;
+        }
+        return VRC_OK;
+    }
+
+    // Chunk c of an input viewed as [outer, row]: element offset of its
+    // (0,0), rows, width and the input row stride.
+    struct Chunk {
+        uint64_t off, rows, width, stride;
+    };
+    static Chunk rs_chunk(uint64_t count, uint64_t outer, int n, int c)
+    {
+        Chunk k;
+        if (outer == 1) {
+            chunk_range(count, n, c, &k.off, &k.width);
+            k.rows = 1;
+            k.stride = 0;
+        } else {
+            const uint64_t row = count / outer, w = row / (uint64_t)n;
+            k.off = (uint64_t)c * w;
+            k.rows = outer;
+            k.width = w;
+            k.stride = row;
+        }
+        return k;
+    }
+
+    // Ring reduce-scatter: step s adds rank (c+1+s)'s chunk c into the
+    // running partial of chunk c, which lives in output c.
+    static vrc_status_t ring_reduce_scatter(const char* const* x, char* const* y, int n, uint64_t count,
+                                            uint64_t outer, int cus, hipStream_t st)
+    {
+        if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc::StepArgs args;
+        for (int s = 0; s < n - 1; s++) {
+            uint64_t work = 0;
+            for (int c = 0; c < n; c++) {
+                const Chunk k = rs_chunk(count, outer, n, c);
+                const int r = mod(c + 1 + s, n);
+                const char* partial = (s == 0) ? x[c] + k.off * E : y[c];
+                const uint64_t sp = (s == 0) ? k.stride : k.width;
+                args.op[c] = make_op(partial, x[r] + k.off * E, y[c], k.rows, k.width, sp, k.stride, k.width);
+                const uint64_t w = op_work(args.op[c]);
+                if (w > work) work = w;
+            }
+            vrc_status_t rc = step<true>(args, n, work, cus, st);
+            if (rc) return rc;
+        }
+        return VRC_OK;
+    }
+
+    // Ring all-gather: step 0 places every rank's own slab and the slab of
+    // its predecessor; step s >= 1 relays slab (r-1-s) from rank r-1.
+    static vrc_status_t ring_all_gather(const char* const* x, char* const* y, int n, uint64_t count,
+                                        uint64_t outer, int cus, hipStream_t st)
+    {
+        const uint64_t row = count / outer, sy = (uint64_t)n * row;
+        if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc::StepArgs args;
+        uint64_t work = 0;
+        for (int r = 0; r < n; r++) {
+            const int p = mod(r - 1, n);
+            args.op[2 * r] = make_op(x[r], nullptr, y[r] + (uint64_t)r * row * E, outer, row, row, 0, sy);
+            args.op[2 * r + 1] = make_op(x[p], nullptr, y[r] + (uint64_t)p * row * E, outer, row, row, 0, sy);
+            const uint64_t w = op_work(args.op[2 * r]) > op_work(args.op[2 * r + 1]) ? op_work(args.op[2 * r])
+                                                                                      : op_work(args.op[2 * r + 1]);
+            if (w > work) work = w;
+        }
+        vrc_status_t rc = step<false>(args, 2 * n, work, cus, st);
+        if (rc) return rc;
+        for (int s = 1; s < n - 1; s++) {
+            work = 0;
+            for (int r = 0; r < n; r++) {
+                const int slab = mod(r - 1 - s, n);
+                const uint64_t off = (uint64_t)slab * row * E;
+                args.op[r] = make_op(y[mod(r - 1, n)] + off, nullptr, y[r] + off, outer, row, sy, 0, sy);
+                const uint64_t w = op_work(args.op[r]);
+                if (w > work) work = w;
+            }
+            rc = step<false>(args, n, work, cus, st);
+            if (rc) return rc;
+        }
+        return VRC_OK;
+    }
+
+    // ---- fused family ----------------------------------------------------
+    template <int N, int U>
+    static void launch_fused_ar_nu(const vrc::FusedArArgs& a, dim3 grid, hipStream_t st)
+    {
+        if (tuning().nontemporal)
+            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, U, true>), grid, dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, U, false>), grid, dim3(kBlock), 0, st, a);
+    }
+
+    template <int N>
+    static void launch_fused_ar_n(const vrc::FusedArArgs& a, dim3 grid, hipStream_t st)
+    {
+        switch (tuning().unroll) {
+        case 4: launch_fused_ar_nu<N, 4>(a, grid, st); break;
+        case 2: launch_fused_ar_nu<N, 2>(a, grid, st); break;
+        default: launch_fused_ar_nu<N, 1>(a, grid, st); break;
+        }
+    }
+
+    static vrc_status_t fused_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
+                                        hipStream_t st)
+    {
+        if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc::FusedArArgs a;
+        uintptr_t addr[2 * kMaxRanks];
+        for (int r = 0; r < n; r++) {
+            a.src[r] = x[r];
+            a.dst[r] = y[r];
+            addr[2 * r] = (uintptr_t)x[r];
+            addr[2 * r + 1] = (uintptr_t)y[r];
+        }
+        for (int r = n; r < kMaxRanks; r++) {
+            a.src[r] = nullptr;
+            a.dst[r] = nullptr;
+        }
+        a.count = count;
+        a.g = split_rows(addr, 2 * n, 1, nullptr, 0, count, E);
+        const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
+        const dim3 grid(grid_x(cus, work, 1));
+        switch (n) {
+#define VRC_CASE(K) \
+    case K: launch_fused_ar_n<K>(a, grid, st); break;
+            VRC_CASE(2) VRC_CASE(3) VRC_CASE(4) VRC_CASE(5) VRC_CASE(6) VRC_CASE(7) VRC_CASE(8) VRC_CASE(9)
+            VRC_CASE(10) VRC_CASE(11) VRC_CASE(12) VRC_CASE(13) VRC_CASE(14) VRC_CASE(15) VRC_CASE(16)
+#undef VRC_CASE
+        default: return VRC_ERR_INVALID_ARG;
+        }
+        return check_launch();
+    }
+
+    template <int N>
+    static void launch_fused_rs_n(const vrc::FusedRsArgs& a, dim3 grid, hipStream_t st)
+    {
+        if (tuning().nontemporal)
+            hipLaunchKernelGGL((vrc::k_fused_reduce_scatter<T, N, true>), grid, dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((vrc::k_fused_reduce_scatter<T, N, false>), grid, dim3(kBlock), 0, st, a);
+    }
+
+    static vrc_status_t fused_reduce_scatter(const char* const* x, char* const* y, int n, uint64_t count,
+                                             uint64_t outer, int cus, hipStream_t st)
+    {
+        if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc::FusedRsArgs a;
+        uint64_t work = 0;
+        for (int r = 0; r < kMaxRanks; r++) a.src[r] = r < n ? x[r] : nullptr;
+        for (int c = 0; c < n; c++) {
+            const Chunk k = rs_chunk(count, outer, n, c);
+            vrc::RsChunk& ch = a.ch[c];
+            ch.src_off = k.off;
+            ch.d = y[c];
+            ch.rows = k.rows;
+            ch.width = k.width;
+            ch.s_src = k.stride;
+            ch.s_dst = k.width;
+            uintptr_t addr[kMaxRanks + 1];
+            for (int r = 0; r < n; r++) addr[r] = (uintptr_t)(x[r] + k.off * E);
+            addr[n] = (uintptr_t)y[c];
+            const uint64_t strides[2] = {k.stride * E, k.width * E};
+            ch.g = split_rows(addr, n + 1, k.rows, strides, 2, k.width, E);
+            const uint64_t w = k.rows * (ch.g.nvb + ch.g.head + ch.g.tail);
+            if (w > work) work = w;
+        }
+        const dim3 grid(grid_x(cus, work, n), (unsigned)n);
+        switch (n) {
+#define VRC_CASE(K) \
+    case K: launch_fused_rs_n<K>(a, grid, st); break;
+            VRC_CASE(2) VRC_CASE(3) VRC_CASE(4) VRC_CASE(5) VRC_CASE(6) VRC_CASE(7) VRC_CASE(8) VRC_CASE(9)
+            VRC_CASE(10) VRC_CASE(11) VRC_CASE(12) VRC_CASE(13) VRC_CASE(14) VRC_CASE(15) VRC_CASE(16)
+#undef VRC_CASE
+        default: return VRC_ERR_INVALID_ARG;
+        }
+        return check_launch();
+    }
+
+    static vrc_status_t fused_all_gather(const char* const* x, char* const* y, int n, uint64_t count,
+                                         uint64_t outer, int cus, hipStream_t st)
+    {
+        vrc::FusedAgArgs a;
+        const uint64_t row = count / outer;
+        a.rows = outer;
+        a.width = row;
+        a.n = n;
+        uint64_t work = 0;
+        for (int r = 0; r < kMaxRanks; r++) {
+            a.src[r] = r < n ? x[r] : nullptr;
+            a.dst[r] = r < n ? y[r] : nullptr;
+        }
+        for (int q = 0; q < n; q++) {
+            uintptr_t addr[kMaxRanks + 1];
+            addr[0] = (uintptr_t)x[q];
+            for (int r = 0; r < n; r++) addr[r + 1] = (uintptr_t)(y[r] + (uint64_t)q * row * E);
+            const uint64_t strides[2] = {row * E, (uint64_t)n * row * E};
+            a.g[q] = split_rows(addr, n + 1, outer, strides, 2, row, E);
+            const uint64_t w = outer * (a.g[q].nvb + a.g[q].head + a.g[q].tail);
+            if (w > work) work = w;
+        }
+        const dim3 grid(grid_x(cus, work, n), (unsigned)n);
+        if (tuning().nontemporal)
+            hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((vrc::k_fused_all_gather<T, false>), grid, dim3(kBlock), 0, st, a);
+        return check_launch();
+    }
+};
+
+enum class Op { AR_RING, AR_FUSED, RS_RING, RS_FUSED, AG_RING, AG_FUSED };
+
+template <class T>
+vrc_status_t run_typed(Op op, const char* const* x, char* const* y, int n, uint64_t count, uint64_t outer,
+                       int cus, hipStream_t st)
+{
+    switch (op) {
+    case Op::AR_RING: return Launch<T>::ring_allreduce(x, y, n, count, cus, st);
+    case Op::AR_FUSED: return Launch<T>::fused_allreduce(x, y, n, count, cus, st);
+    case Op::RS_RING: return Launch<T>::ring_reduce_scatter(x, y, n, count, outer, cus, st);
+    case Op::RS_FUSED: return Launch<T>::fused_reduce_scatter(x, y, n, count, outer, cus, st);
+    case Op::AG_RING: return Launch<T>::ring_all_gather(x, y, n, count, outer, cus, st);
+    case Op::AG_FUSED: return Launch<T>::fused_all_gather(x, y, n, count, outer, cus, st);
+    }
+    return VRC_ERR_UNSUPPORTED;
+}
+
+vrc_status_t run(Op op, vrc_dtype_t dt, const void* const* send, void* const* recv, int n, uint64_t count,
+                 uint64_t outer, hipStream_t st)
+{
+    int cus = 0;
+    hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return hip_fail(e);
+    (void)hipGetLastError();  // start from a clean per-thread error state
+    const char* x[kMaxRanks];
+    char* y[kMaxRanks];
+    for (int r = 0; r < n; r++) {
+        x[r] = static_cast<const char*>(send[r]);
+        y[r] = static_cast<char*>(recv[r]);
+    }
+    switch (dt) {
+    case VRC_INT32: return run_typed<vrc::I32>(op, x, y, n, count, outer, cus, st);
+    case VRC_FP32: return run_typed<vrc::F32>(op, x, y, n, count, outer, cus, st);
+    case VRC_FP16: return run_typed<vrc::F16>(op, x, y, n, count, outer, cus, st);
+    case VRC_BF16: return run_typed<vrc::BF16>(op, x, y, n, count, outer, cus, st);
+    }
+    return VRC_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
+                           vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, vrc_stream_t stream)
+{
+    vrc_status_t rc = check_common(send, recv, nranks, dtype);
+    if (rc) return rc;
+    if (op != VRC_SUM || (mode != VRC_RING && mode != VRC_FUSED)) return VRC_ERR_UNSUPPORTED;
+    const uint64_t bytes = (uint64_t)count * (uint64_t)esize(dtype);
+    uint64_t rb[kMaxRanks];
+    for (int r = 0; r < nranks; r++) rb[r] = bytes;
+    rc = check_buffers(send, recv, nranks, bytes, rb, true);
+    if (rc) return rc;
+    if (count == 0) return VRC_OK;
+    return run(mode == VRC_RING ? Op::AR_RING : Op::AR_FUSED, dtype, send, recv, nranks, count, 1,
+               (hipStream_t)stream);
+}
+
+vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int nranks, size_t count,
+                                size_t outer, vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode,
+                                vrc_stream_t stream)
+{
+    vrc_status_t rc = check_common(send, recv, nranks, dtype);
+    if (rc) return rc;
+    if (op != VRC_SUM || (mode != VRC_RING && mode != VRC_FUSED)) return VRC_ERR_UNSUPPORTED;
+    if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
+    if (outer > 1 && (count / outer) % (uint64_t)nranks != 0) return VRC_ERR_INVALID_ARG;
+    const int E = esize(dtype);
+    uint64_t rb[kMaxRanks];
+    for (int c = 0; c < nranks; c++) {
+        if (outer == 1) {
+            uint64_t off, len;
+            chunk_range(count, nranks, c, &off, &len);
+            rb[c] = len * E;
+        } else {
+            rb[c] = (uint64_t)count / (uint64_t)nranks * E;
+        }
+    }
+    rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, false);
+    if (rc) return rc;
+    if (count == 0) return VRC_OK;
+    return run(mode == VRC_RING ? Op::RS_RING : Op::RS_FUSED, dtype, send, recv, nranks, count, outer,
+               (hipStream_t)stream);
+}
+
+vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nranks, size_t count,
+                            size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_stream_t stream)
+{
+    vrc_status_t rc = check_common(send, recv, nranks, dtype);
+    if (rc) return rc;
+    if (mode != VRC_RING && mode != VRC_FUSED) return VRC_ERR_UNSUPPORTED;
+    if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
+    const int E = esize(dtype);
+    uint64_t rb[kMaxRanks];
+    for (int r = 0; r < nranks; r++) rb[r] = (uint64_t)count * (uint64_t)nranks * E;
+    rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, false);
+    if (rc) return rc;
+    if (count == 0) return VRC_OK;
+    return run(mode == VRC_RING ? Op::AG_RING : Op::AG_FUSED, dtype, send, recv, nranks, count, outer,
+               (hipStream_t)stream);
+}
+
+vrc_status_t vrc_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* length)
+{
+    if (nranks < 1 || chunk < 0 || chunk >= nranks || !offset || !length) return VRC_ERR_INVALID_ARG;
+    uint64_t off, len;
+    chunk_range(count, nranks, chunk, &off, &len);
+    *offset = (size_t)off;
+    *length = (size_t)len;
+    return VRC_OK;
+}
+
+const char* vrc_status_string(vrc_status_t status)
+{
+    switch (status) {
+    case VRC_OK: return "VRC_OK: success";
+    case VRC_ERR_INVALID_ARG: return "VRC_ERR_INVALID_ARG: invalid argument (null pointer, nranks or shape)";
+    case VRC_ERR_UNSUPPORTED: return "VRC_ERR_UNSUPPORTED: unknown dtype, op or mode";
+    case VRC_ERR_ALIAS: return "VRC_ERR_ALIAS: buffers overlap in a way the call does not allow";
+    case VRC_ERR_HIP: return "VRC_ERR_HIP: a HIP runtime call or kernel launch failed";
+    }
+    return "unknown vrc status";
+}
+
+int vrc_last_hip_error(void) { return g_last_hip_error; }
+
+int vrc_version(void) { return VRC_VERSION; }
+
+}  // extern "C"

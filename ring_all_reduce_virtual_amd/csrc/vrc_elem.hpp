@@ -1,0 +1,156 @@
+// vrc_elem.hpp -- element types for the virtual-rank collective kernels.
+//
+// Every kernel moves data in 16-byte vectors (one global_load_dwordx4 /
+// global_store_dwordx4 per lane) and computes in an accumulator type:
+//   int32 -> uint32 (two's-complement wrap), fp32 -> float,
+//   fp16  -> float (exact widening, round-to-nearest-even narrowing),
+//   bf16  -> float (exact widening, round-to-nearest-even narrowing).
+// A ring step adds two stored values and rounds once to the storage type;
+// the fused kernels fold N values in the accumulator and round once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vrc {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load/store, optionally with the non-temporal hint (streaming data
+// that is never re-read should not displace other lines from the caches).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const char* p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(char* p, u32x4 v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+}
+
+struct I32 {
+    using S = uint32_t;  // stored bits
+    using A = uint32_t;  // accumulator
+    static constexpr int ESZ = 4, VEC = 4;
+    __device__ static A widen(S s) { return s; }
+    __device__ static S narrow(A a) { return a; }
+    __device__ static A add(A a, A b) { return a + b; }
+    __device__ static void unpack(u32x4 v, A* a) { a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w; }
+    __device__ static u32x4 pack(const A* a) { return u32x4{a[0], a[1], a[2], a[3]}; }
+};
+
+struct F32 {
+    using S = uint32_t;
+    using A = float;
+    static constexpr int ESZ = 4, VEC = 4;
+    __device__ static A widen(S s) { return __uint_as_float(s); }
+    __device__ static S narrow(A a) { return __float_as_uint(a); }
+    __device__ static A add(A a, A b) { return a + b; }
+    __device__ static void unpack(u32x4 v, A* a)
+    {
+        a[0] = __uint_as_float(v.x); a[1] = __uint_as_float(v.y);
+        a[2] = __uint_as_float(v.z); a[3] = __uint_as_float(v.w);
+    }
+    __device__ static u32x4 pack(const A* a)
+    {
+        return u32x4{__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
+                     __float_as_uint(a[3])};
+    }
+};
+
+struct F16 {
+    using S = uint16_t;
+    using A = float;
+    static constexpr int ESZ = 2, VEC = 8;
+    __device__ static A widen(S s) { return (float)__builtin_bit_cast(_Float16, s); }
+    // The hardware conversion rounds to nearest even (the default mode),
+    // keeps fp16 subnormals and overflows to infinity.
+    __device__ static S narrow(A a) { return __builtin_bit_cast(uint16_t, (_Float16)a); }
+    __device__ static A add(A a, A b) { return a + b; }
+    __device__ static void unpack(u32x4 v, A* a)
+    {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            a[2 * i] = widen((S)(w[i] & 0xffffu));
+            a[2 * i + 1] = widen((S)(w[i] >> 16));
+        }
+    }
+    __device__ static u32x4 pack(const A* a)
+    {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) w[i] = (uint32_t)narrow(a[2 * i]) | ((uint32_t)narrow(a[2 * i + 1]) << 16);
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+};
+
+struct BF16 {
+    using S = uint16_t;
+    using A = float;
+    static constexpr int ESZ = 2, VEC = 8;
+    // bfloat16 is the upper half of an IEEE binary32.
+    __device__ static A widen(S s) { return __uint_as_float((uint32_t)s << 16); }
+    // Round to nearest even on the 16 discarded bits; NaN stays a quiet NaN.
+    __device__ static S narrow(A a)
+    {
+        uint32_t u = __float_as_uint(a);
+        if ((u & 0x7fffffffu) > 0x7f800000u) return (S)((u >> 16) | 0x40u);
+        u += 0x7fffu + ((u >> 16) & 1u);
+        return (S)(u >> 16);
+    }
+    __device__ static A add(A a, A b) { return a + b; }
+    __device__ static void unpack(u32x4 v, A* a)
+    {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            a[2 * i] = __uint_as_float(w[i] << 16);
+            a[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ static u32x4 pack(const A* a)
+    {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) w[i] = (uint32_t)narrow(a[2 * i]) | ((uint32_t)narrow(a[2 * i + 1]) << 16);
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+};
+
+template <class T>
+__device__ __forceinline__ typename T::S load_s(const char* p)
+{
+    return *reinterpret_cast<const typename T::S*>(p);
+}
+
+template <class T>
+__device__ __forceinline__ void store_s(char* p, typename T::S v)
+{
+    *reinterpret_cast<typename T::S*>(p) = v;
+}
+
+// One ring-step element: round(widen(a) + widen(b)) in the storage type.
+template <class T>
+__device__ __forceinline__ typename T::S add_s(typename T::S a, typename T::S b)
+{
+    return T::narrow(T::add(T::widen(a), T::widen(b)));
+}
+
+// The same on a 16-byte vector.
+template <class T>
+__device__ __forceinline__ u32x4 add_v(u32x4 a, u32x4 b)
+{
+    typename T::A x[T::VEC], y[T::VEC];
+    T::unpack(a, x);
+    T::unpack(b, y);
+#pragma unroll
+    for (int i = 0; i < T::VEC; i++) x[i] = T::add(x[i], y[i]);
+    return T::pack(x);
+}
+
+}  // namespace vrc

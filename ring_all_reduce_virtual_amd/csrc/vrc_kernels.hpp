@@ -1,0 +1,255 @@
+// vrc_kernels.hpp -- HIP kernels (gfx950) for the virtual-rank collectives.
+//
+// All kernels are bandwidth-bound streaming loops: 256-lane workgroups (four
+// wave64s), a grid sized to the CU count, grid-stride iteration over 16-byte
+// vectors, and a scalar pass for the elements before the first 16-byte
+// boundary and after the last one.  No MFMA: the work is a sum, not a
+// contraction.
+//
+// Geometry.  An operand region is `rows` rows of `width` elements with a row
+// stride in elements.  The host splits each row into `head` scalar elements
+// (up to the first 16-byte boundary), `nvb` 16-byte vectors and `tail`
+// scalar elements; when the operands of one region do not share the same
+// address offset modulo 16 (or a row stride is not a multiple of 16 bytes)
+// it sets head = width, nvb = tail = 0 and the region runs scalar.
+#pragma once
+
+#include "vrc_elem.hpp"
+
+namespace vrc {
+
+constexpr int kBlock = 256;
+constexpr int kMaxRanks = 16;
+constexpr int kMaxStepOps = 2 * kMaxRanks;
+
+struct RowSplit {
+    uint64_t head, nvb, tail;
+};
+
+// Map a scalar slot k (0 <= k < rows*(head+tail)) to (row, column).
+__device__ __forceinline__ void scalar_slot(uint64_t k, const RowSplit& g, uint64_t vec, uint64_t& row,
+                                            uint64_t& col)
+{
+    const uint64_t per_row = g.head + g.tail;
+    row = k / per_row;
+    const uint64_t j = k - row * per_row;
+    col = (j < g.head) ? j : g.head + g.nvb * vec + (j - g.head);
+}
+
+// ---------------------------------------------------------------------------
+// Ring step: one launch runs one reduce-scatter step (d = a + b) or one
+// all-gather step (d = a) for every rank at once; blockIdx.y is the rank's
+// operation.
+// ---------------------------------------------------------------------------
+struct StepOp {
+    const char* a;  // element (0,0) of the first operand region
+    const char* b;  // second operand (add only)
+    char* d;        // destination
+    uint64_t rows, width;
+    uint64_t sa, sb, sd;  // row strides, elements
+    RowSplit g;
+};
+
+struct StepArgs {
+    StepOp op[kMaxStepOps];
+};
+
+template <class T, bool ADD, bool NT>
+__global__ __launch_bounds__(kBlock) void k_ring_step(StepArgs args)
+{
+    const StepOp& op = args.op[blockIdx.y];
+    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    constexpr uint64_t E = T::ESZ;
+
+    const uint64_t nv = op.rows * op.g.nvb;
+    const uint64_t body = op.g.head * E;
+    if (op.rows == 1) {
+        for (uint64_t v = tid; v < nv; v += nthreads) {
+            const uint64_t off = body + v * 16;
+            u32x4 x = ld16<NT>(op.a + off);
+            if constexpr (ADD) x = add_v<T>(x, ld16<NT>(op.b + off));
+            st16<NT>(op.d + off, x);
+        }
+    } else {
+        for (uint64_t v = tid; v < nv; v += nthreads) {
+            const uint64_t row = v / op.g.nvb;
+            const uint64_t col = (v - row * op.g.nvb) * 16 + body;
+            u32x4 x = ld16<NT>(op.a + row * op.sa * E + col);
+            if constexpr (ADD) x = add_v<T>(x, ld16<NT>(op.b + row * op.sb * E + col));
+            st16<NT>(op.d + row * op.sd * E + col, x);
+        }
+    }
+
+    const uint64_t ns = op.rows * (op.g.head + op.g.tail);
+    for (uint64_t k = tid; k < ns; k += nthreads) {
+        uint64_t row, col;
+        scalar_slot(k, op.g, T::VEC, row, col);
+        typename T::S x = load_s<T>(op.a + (row * op.sa + col) * E);
+        if constexpr (ADD) x = add_s<T>(x, load_s<T>(op.b + (row * op.sb + col) * E));
+        store_s<T>(op.d + (row * op.sd + col) * E, x);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused all-reduce: every lane reads element block i of all N inputs, folds
+// them in rank order in the accumulator, rounds once and writes the result
+// to all N outputs.  Reads precede writes within a lane, so in-place calls
+// are safe.  U independent vectors per lane per iteration keep U*N 16-byte
+// loads in flight.
+// ---------------------------------------------------------------------------
+struct FusedArArgs {
+    const char* src[kMaxRanks];
+    char* dst[kMaxRanks];
+    uint64_t count;  // elements per rank
+    RowSplit g;      // one row of `count` elements
+};
+
+template <class T, int N>
+__device__ __forceinline__ u32x4 fold_v(const u32x4* in)
+{
+    typename T::A acc[T::VEC], x[T::VEC];
+    T::unpack(in[0], acc);
+#pragma unroll
+    for (int r = 1; r < N; r++) {
+        T::unpack(in[r], x);
+#pragma unroll
+        for (int i = 0; i < T::VEC; i++) acc[i] = T::add(acc[i], x[i]);
+    }
+    return T::pack(acc);
+}
+
+template <class T, int N, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void k_fused_allreduce(FusedArArgs a)
+{
+    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    constexpr uint64_t E = T::ESZ;
+    const uint64_t body = a.g.head * E;
+    const uint64_t nv = a.g.nvb;
+
+    uint64_t v = tid;
+    if constexpr (U > 1) {
+        for (; v + (U - 1) * nthreads < nv; v += U * nthreads) {
+            u32x4 in[U][N];
+#pragma unroll
+            for (int u = 0; u < U; u++)
+#pragma unroll
+                for (int r = 0; r < N; r++) in[u][r] = ld16<NT>(a.src[r] + body + (v + u * nthreads) * 16);
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const u32x4 s = fold_v<T, N>(in[u]);
+#pragma unroll
+                for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + (v + u * nthreads) * 16, s);
+            }
+        }
+    }
+    for (; v < nv; v += nthreads) {
+        u32x4 in[N];
+#pragma unroll
+        for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
+        const u32x4 s = fold_v<T, N>(in);
+#pragma unroll
+        for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, s);
+    }
+
+    const uint64_t ns = a.g.head + a.g.tail;
+    for (uint64_t k = tid; k < ns; k += nthreads) {
+        const uint64_t i = (k < a.g.head) ? k : a.g.head + a.g.nvb * T::VEC + (k - a.g.head);
+        typename T::A acc = T::widen(load_s<T>(a.src[0] + i * E));
+#pragma unroll
+        for (int r = 1; r < N; r++) acc = T::add(acc, T::widen(load_s<T>(a.src[r] + i * E)));
+        const typename T::S s = T::narrow(acc);
+#pragma unroll
+        for (int r = 0; r < N; r++) store_s<T>(a.dst[r] + i * E, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused reduce-scatter: blockIdx.y = chunk c.  Output c is the rank-order
+// fold of chunk c over all N inputs, rounded once.
+// ---------------------------------------------------------------------------
+struct RsChunk {
+    uint64_t src_off;  // element offset of chunk c's (0,0) in every input
+    char* d;           // output c
+    uint64_t rows, width;
+    uint64_t s_src, s_dst;  // row strides, elements
+    RowSplit g;
+};
+
+struct FusedRsArgs {
+    const char* src[kMaxRanks];
+    RsChunk ch[kMaxRanks];
+};
+
+template <class T, int N, bool NT>
+__global__ __launch_bounds__(kBlock) void k_fused_reduce_scatter(FusedRsArgs a)
+{
+    const RsChunk& c = a.ch[blockIdx.y];
+    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    constexpr uint64_t E = T::ESZ;
+    const uint64_t nv = c.rows * c.g.nvb;
+    for (uint64_t v = tid; v < nv; v += nthreads) {
+        const uint64_t row = (c.rows == 1) ? 0 : v / c.g.nvb;
+        const uint64_t col = (v - row * c.g.nvb) * 16 + c.g.head * E;
+        const uint64_t so = (c.src_off + row * c.s_src) * E + col;
+        u32x4 in[N];
+#pragma unroll
+        for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + so);
+        st16<NT>(c.d + row * c.s_dst * E + col, fold_v<T, N>(in));
+    }
+    const uint64_t ns = c.rows * (c.g.head + c.g.tail);
+    for (uint64_t k = tid; k < ns; k += nthreads) {
+        uint64_t row, col;
+        scalar_slot(k, c.g, T::VEC, row, col);
+        const uint64_t so = (c.src_off + row * c.s_src + col) * E;
+        typename T::A acc = T::widen(load_s<T>(a.src[0] + so));
+#pragma unroll
+        for (int r = 1; r < N; r++) acc = T::add(acc, T::widen(load_s<T>(a.src[r] + so)));
+        store_s<T>(c.d + (row * c.s_dst + col) * E, T::narrow(acc));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused all-gather: blockIdx.y = source rank q.  Input q ([rows, width]) is
+// read once and written into column slab q of every output ([rows,
+// n*width]).
+// ---------------------------------------------------------------------------
+struct FusedAgArgs {
+    const char* src[kMaxRanks];
+    char* dst[kMaxRanks];
+    uint64_t rows, width;  // input geometry; output row stride is n * width
+    int n;
+    RowSplit g[kMaxRanks];  // per source rank (its slab offset sets the alignment)
+};
+
+template <class T, bool NT>
+__global__ __launch_bounds__(kBlock) void k_fused_all_gather(FusedAgArgs a)
+{
+    const int q = blockIdx.y;
+    const RowSplit& g = a.g[q];
+    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    constexpr uint64_t E = T::ESZ;
+    const uint64_t s_dst = (uint64_t)a.n * a.width;
+    const uint64_t slab = (uint64_t)q * a.width;
+    const uint64_t nv = a.rows * g.nvb;
+    for (uint64_t v = tid; v < nv; v += nthreads) {
+        const uint64_t row = (a.rows == 1) ? 0 : v / g.nvb;
+        const uint64_t col = (v - row * g.nvb) * 16 + g.head * E;
+        const u32x4 x = ld16<NT>(a.src[q] + row * a.width * E + col);
+        const uint64_t dof = (row * s_dst + slab) * E + col;
+        for (int r = 0; r < a.n; r++) st16<NT>(a.dst[r] + dof, x);
+    }
+    const uint64_t ns = a.rows * (g.head + g.tail);
+    for (uint64_t k = tid; k < ns; k += nthreads) {
+        uint64_t row, col;
+        scalar_slot(k, g, T::VEC, row, col);
+        const typename T::S x = load_s<T>(a.src[q] + (row * a.width + col) * E);
+        const uint64_t dof = (row * s_dst + slab + col) * E;
+        for (int r = 0; r < a.n; r++) store_s<T>(a.dst[r] + dof, x);
+    }
+}
+
+}  // namespace vrc

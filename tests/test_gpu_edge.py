@@ -1,0 +1,238 @@
+"""Edge cases of the HIP path through the C ABI: in place, misaligned views,
+degenerate rank counts and sizes, determinism, composition, streams and the
+error paths with real device buffers."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity_util import assert_bitwise, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+DTYPES = ("int32", "fp32", "fp16", "bf16")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def vrc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_all_reduce_virtual_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def oracle_ar(orc, hx, dtype, mode):
+    return orc.ring_allreduce(hx, dtype) if mode == "ring" else orc.fused_allreduce(hx, dtype)
+
+
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_in_place_equals_out_of_place(vrc, orc, mode, dtype):
+    say(f"in place {mode} {dtype}")
+    n, count = 8, 50001
+    xs = workloads.random_ranks(n, count, dtype, seed=400, device=DEV)
+    want = oracle_ar(orc, host(xs), dtype, mode)
+    ys = vrc.vrc_allreduce(xs, recv=xs, mode=mode)  # recv is send
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bitwise(workloads.to_numpy(ys[r]), want[r], f"in place {mode} {dtype} rank {r}")
+
+
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+def test_some_ranks_in_place(vrc, orc, mode):
+    say(f"mixed in place {mode}")
+    n, count = 5, 40000
+    xs = workloads.random_ranks(n, count, "fp32", seed=401, device=DEV)
+    want = oracle_ar(orc, host(xs), "fp32", mode)
+    recv = [xs[r] if r % 2 == 0 else torch.empty_like(xs[r]) for r in range(n)]
+    vrc.vrc_allreduce(xs, recv=recv, mode=mode)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bitwise(workloads.to_numpy(recv[r]), want[r], f"mixed {mode} rank {r}")
+
+
+def _views(xs, offsets, count):
+    """Contiguous views of `count` elements starting `offsets[r]` elements
+    into a fresh buffer (so data pointers are misaligned by design)."""
+    out = []
+    for x, off in zip(xs, offsets):
+        buf = torch.empty(count + 16, dtype=x.dtype, device=x.device)
+        v = buf[off:off + count]
+        v.copy_(x)
+        out.append(v)
+    return out
+
+
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("offsets", ["same", "mixed"])
+def test_misaligned_views(vrc, orc, mode, dtype, offsets):
+    say(f"misaligned {offsets} {mode} {dtype}")
+    n, count = 4, 30011
+    xs = workloads.random_ranks(n, count, dtype, seed=402, device=DEV)
+    offs_in = [1] * n if offsets == "same" else [0, 1, 3, 5]
+    offs_out = [1] * n if offsets == "same" else [2, 0, 1, 7]
+    vx = _views(xs, offs_in, count)
+    vy = _views([torch.zeros_like(x) for x in xs], offs_out, count)
+    vrc.vrc_allreduce(vx, recv=vy, mode=mode)
+    want = oracle_ar(orc, host(xs), dtype, mode)
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bitwise(workloads.to_numpy(vy[r]), want[r], f"misaligned {mode} {dtype} rank {r}")
+    # reduce-scatter and all-gather through misaligned views too
+    rs = vrc.vrc_reduce_scatter(vx, mode=mode)
+    want_rs = (orc.ring_reduce_scatter if mode == "ring" else orc.fused_reduce_scatter)(host(xs), dtype)
+    ag = vrc.vrc_all_gather(vx, mode=mode)
+    want_ag = orc.ring_all_gather(host(xs), dtype)
+    torch.cuda.synchronize()
+    for c in range(n):
+        assert_bitwise(workloads.to_numpy(rs[c]), want_rs[c], f"misaligned rs {mode} {dtype} chunk {c}")
+        assert_bitwise(workloads.to_numpy(ag[c]), want_ag[c], f"misaligned ag {mode} {dtype} rank {c}")
+
+
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_single_rank_is_identity(vrc, mode, dtype):
+    say(f"n=1 {mode} {dtype}")
+    (x,) = workloads.random_ranks(1, 1234, dtype, seed=403, device=DEV)
+    (y,) = vrc.vrc_allreduce([x], mode=mode)
+    (z,) = vrc.vrc_reduce_scatter([x], mode=mode)
+    (g,) = vrc.vrc_all_gather([x], mode=mode)
+    (p,) = vrc.vrc_allreduce([x], recv=[x], mode=mode)
+    torch.cuda.synchronize()
+    hx = workloads.to_numpy(x)
+    for t, what in ((y, "ar"), (z, "rs"), (g, "ag"), (p, "ar in place")):
+        assert_bitwise(workloads.to_numpy(t), hx, f"n=1 {what} {mode} {dtype}")
+
+
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("n,count", [(8, 3), (16, 15), (4, 1), (3, 0)])
+def test_fewer_elements_than_ranks(vrc, orc, mode, n, count):
+    say(f"count<n {mode} n={n} count={count}")
+    xs = workloads.random_ranks(n, count, "fp32", seed=404, device=DEV)
+    ys = vrc.vrc_allreduce(xs, mode=mode)
+    rs = vrc.vrc_reduce_scatter(xs, mode=mode)
+    torch.cuda.synchronize()
+    hx = host(xs)
+    want = oracle_ar(orc, hx, "fp32", mode)
+    want_rs = (orc.ring_reduce_scatter if mode == "ring" else orc.fused_reduce_scatter)(hx, "fp32")
+    for r in range(n):
+        assert_bitwise(workloads.to_numpy(ys[r]), want[r], f"count<n {mode} rank {r}")
+        assert_bitwise(workloads.to_numpy(rs[r]), want_rs[r], f"count<n rs {mode} chunk {r}")
+
+
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+def test_repeat_runs_are_bitwise_identical(vrc, mode):
+    say(f"determinism {mode}")
+    xs = workloads.make_inputs(workloads.WORKLOADS["allreduce_fp32_n8_16mib"], DEV)
+    outs = []
+    for _ in range(3):
+        ys = vrc.vrc_allreduce(xs, mode=mode)
+        torch.cuda.synchronize()
+        outs.append(torch.stack(ys).view(torch.int32))
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_all_gather_of_reduce_scatter_is_allreduce(vrc, dtype):
+    say(f"composition {dtype}")
+    n, count = 8, 8 * 12345  # equal chunks
+    xs = workloads.random_ranks(n, count, dtype, seed=405, device=DEV)
+    ar = vrc.vrc_allreduce(xs, mode="ring")
+    rs = vrc.vrc_reduce_scatter(xs, mode="ring")
+    ag = vrc.vrc_all_gather(rs, mode="ring")
+    torch.cuda.synchronize()
+    for r in range(n):
+        assert_bitwise(workloads.to_numpy(ag[r]), workloads.to_numpy(ar[r]), f"AG(RS) vs AR {dtype} rank {r}")
+
+
+def test_exact_small_integers_ring_equals_fused(vrc):
+    say("exact small integers")
+    n, count = 8, 77777
+    g = torch.Generator(device=DEV).manual_seed(406)
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        xs = [torch.randint(-15, 16, (count,), generator=g, device=DEV).to(dt) for _ in range(n)]
+        a = vrc.vrc_allreduce(xs, mode="ring")
+        b = vrc.vrc_allreduce(xs, mode="fused")
+        s = torch.stack([x.double() for x in xs]).sum(0)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert torch.equal(a[r].double(), s) and torch.equal(b[r].double(), s)
+
+
+def test_int32_wraps(vrc):
+    say("int32 wrap")
+    xs = [torch.full((1000,), 2**31 - 1, dtype=torch.int32, device=DEV) for _ in range(3)]
+    for mode in ("ring", "fused"):
+        ys = vrc.vrc_allreduce(xs, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.all(ys[0] == 2**31 - 3)
+
+
+def test_fp16_overflow_goes_to_inf(vrc, orc):
+    say("fp16 overflow")
+    xs = [torch.full((100,), 60000.0, dtype=torch.float16, device=DEV) for _ in range(2)]
+    for mode in ("ring", "fused"):
+        ys = vrc.vrc_allreduce(xs, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.all(torch.isinf(ys[1])) and torch.all(ys[1] > 0)
+
+
+def test_subnormals_are_kept(vrc, orc):
+    say("subnormals")
+    n = 4
+    tiny32 = torch.tensor([1e-45, -3e-44, 1.2e-38, 5.9e-39] * 64, dtype=torch.float32, device=DEV)
+    tiny16 = torch.tensor([6e-8, -1.2e-7, 3e-5, 6.1e-5] * 64, dtype=torch.float16, device=DEV)
+    for x0, dtype in ((tiny32, "fp32"), (tiny16, "fp16"), (tiny32.to(torch.bfloat16), "bf16")):
+        xs = [x0 * (r + 1) for r in range(n)]
+        for mode in ("ring", "fused"):
+            ys = vrc.vrc_allreduce(xs, mode=mode)
+            torch.cuda.synchronize()
+            want = oracle_ar(orc, host(xs), dtype, mode)
+            assert_bitwise(workloads.to_numpy(ys[0]), want[0], f"subnormal {mode} {dtype}")
+            assert torch.any(ys[0] != 0)
+
+
+def test_side_stream(vrc, orc):
+    say("side stream")
+    xs = workloads.random_ranks(8, 300000, "bf16", seed=407, device=DEV)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ys = vrc.vrc_allreduce(xs, mode="ring")
+        zs = vrc.vrc_allreduce(xs, mode="fused")
+    s.synchronize()
+    hx = host(xs)
+    assert_bitwise(workloads.to_numpy(ys[3]), orc.ring_allreduce(hx, "bf16")[3], "side stream ring")
+    assert_bitwise(workloads.to_numpy(zs[3]), orc.fused_allreduce(hx, "bf16")[3], "side stream fused")
+
+
+def test_errors_through_the_binding(vrc):
+    say("errors")
+    xs = workloads.random_ranks(4, 1000, "fp32", seed=408, device=DEV)
+    with pytest.raises(vrc.VrcError) as e:
+        vrc.vrc_allreduce(xs, recv=[xs[1], xs[0], xs[2], xs[3]])  # outputs are other ranks' inputs
+    assert e.value.status == vrc.VRC_ERR_ALIAS
+    with pytest.raises(vrc.VrcError) as e:
+        vrc.vrc_reduce_scatter(xs, recv=[x[:250] for x in xs])
+    assert e.value.status == vrc.VRC_ERR_ALIAS
+    with pytest.raises(ValueError):
+        vrc.vrc_reduce_scatter([x.view(8, 125) for x in xs], dim=1)  # 125 not divisible by 4
+    with pytest.raises(TypeError):
+        vrc.vrc_allreduce([x.double() for x in xs])
+    empty = [torch.empty(0, device=DEV) for _ in range(4)]
+    for mode in ("ring", "fused"):
+        vrc.vrc_allreduce(empty, mode=mode)
+        vrc.vrc_all_gather(empty, mode=mode)
+    torch.cuda.synchronize()
+    assert vrc.lib().vrc_last_hip_error() == 0

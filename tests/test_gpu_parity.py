@@ -1,0 +1,223 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases span several 4 KiB lane tiles and a ragged tail and are compared
+element by element with the oracle's full simulation.  The named workloads
+run at full size in the launch configuration the benchmark times; where the
+oracle is too slow for every element (128 MiB and 512 MiB per rank) they are
+compared on sampled elements through the oracle's per-element forms, and on
+every element through properties (all ranks identical, the fp64 tolerance
+gate).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity_util import (assert_bitwise, host, ranks_identical, sample_indices,
+                               tolerance_gate_torch)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("int32", "fp32", "fp16", "bf16")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def vrc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_all_reduce_virtual_amd as m  # fails loudly if libvrc.so is missing
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+DEV = "cuda:0"
+
+
+# ---------------------------------------------------------------------------
+# all-reduce, small and ragged, every dtype and mode, full oracle comparison
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n,count", [(2, 1), (2, 4099), (3, 5), (3, 100003), (4, 4099), (5, 3),
+                                     (8, 7), (8, 65536 * 3 + 13), (16, 1), (16, 100003)])
+def test_allreduce_small(vrc, orc, mode, dtype, n, count):
+    say(f"allreduce {mode} {dtype} n={n} count={count}")
+    xs = workloads.random_ranks(n, count, dtype, seed=100 + n * 7 + count % 97, device=DEV)
+    ys = vrc.vrc_allreduce(xs, mode=mode)
+    torch.cuda.synchronize()
+    hx = host(xs)
+    want = orc.ring_allreduce(hx, dtype) if mode == "ring" else orc.fused_allreduce(hx, dtype)
+    for r, y in enumerate(host(ys)):
+        assert_bitwise(y, want[r], f"{mode} {dtype} n={n} count={count} rank {r}")
+
+
+# ---------------------------------------------------------------------------
+# reduce-scatter and all-gather, flat and along a dimension
+# ---------------------------------------------------------------------------
+RS_CASES = [  # (n, shape, dim)
+    (2, (9,), 0), (4, (4099,), 0), (8, (7,), 0), (3, (100003,), 0), (16, (65536 * 2 + 5,), 0),
+    (8, (8, 4096), -1), (4, (3, 40), 1), (2, (5, 6, 14), 2), (8, (2, 3, 16, 8), 2), (16, (4, 16 * 33), -1),
+    (4, (7, 12), -1),
+]
+
+
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n,shape,dim", RS_CASES)
+def test_reduce_scatter_small(vrc, orc, mode, dtype, n, shape, dim):
+    say(f"reduce_scatter {mode} {dtype} n={n} shape={shape} dim={dim}")
+    xs = workloads.random_ranks(n, shape, dtype, seed=200 + n + len(shape), device=DEV)
+    ys = vrc.vrc_reduce_scatter(xs, dim=dim, mode=mode)
+    torch.cuda.synchronize()
+    outer = int(np.prod(shape[:dim % len(shape)])) if len(shape) > 1 else 1
+    hx = host(xs)
+    want = (orc.ring_reduce_scatter(hx, dtype, outer=outer) if mode == "ring"
+            else orc.fused_reduce_scatter(hx, dtype, outer=outer))
+    for c, y in enumerate(host(ys)):
+        assert_bitwise(y, want[c], f"rs {mode} {dtype} n={n} shape={shape} chunk {c}")
+
+
+AG_CASES = [  # (n, shape, dim)
+    (2, (9,), 0), (4, (4099,), 0), (8, (1,), 0), (3, (100003,), 0), (16, (4096 + 3,), 0),
+    (8, (1, 5, 64, 128), 1), (4, (3, 7), 1), (2, (5, 6, 14), 2), (8, (2, 3, 16, 8), 2), (3, (4, 33), -1),
+]
+
+
+@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("n,shape,dim", AG_CASES)
+def test_all_gather_small(vrc, orc, mode, dtype, n, shape, dim):
+    say(f"all_gather {mode} {dtype} n={n} shape={shape} dim={dim}")
+    xs = workloads.random_ranks(n, shape, dtype, seed=300 + n + len(shape), device=DEV)
+    ys = vrc.vrc_all_gather(xs, dim=dim, mode=mode)
+    torch.cuda.synchronize()
+    outer = int(np.prod(shape[:dim % len(shape)])) if len(shape) > 1 else 1
+    want = orc.ring_all_gather(host(xs), dtype, outer=outer)
+    ref = torch.cat(xs, dim=dim)
+    for r, y in enumerate(ys):
+        assert tuple(y.shape) == tuple(ref.shape)
+        assert_bitwise(workloads.to_numpy(y), want[r], f"ag {mode} {dtype} n={n} shape={shape} rank {r}")
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size
+# ---------------------------------------------------------------------------
+def test_workload_allreduce_int32_n4_4099(vrc, orc):
+    w = workloads.WORKLOADS["allreduce_int32_n4_4099"]
+    xs = workloads.make_inputs(w, DEV)
+    hx = host(xs)
+    naive = np.sum([x.astype(np.int64) for x in hx], axis=0).astype(np.int32)
+    for mode in ("ring", "fused"):
+        say(f"{w.name} {mode}")
+        ys = vrc.vrc_allreduce(xs, mode=mode)
+        torch.cuda.synchronize()
+        want = orc.ring_allreduce(hx, "int32") if mode == "ring" else orc.fused_allreduce(hx, "int32")
+        for r, y in enumerate(host(ys)):
+            assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
+            assert_bitwise(y, naive, f"{w.name} {mode} rank {r} vs naive sum")
+
+
+def test_workload_allreduce_fp32_n8_16mib(vrc, orc):
+    w = workloads.WORKLOADS["allreduce_fp32_n8_16mib"]
+    xs = workloads.make_inputs(w, DEV)
+    hx = host(xs)
+    for mode in ("ring", "fused"):
+        say(f"{w.name} {mode}")
+        ys = vrc.vrc_allreduce(xs, mode=mode)
+        torch.cuda.synchronize()
+        ranks_identical(ys, f"{w.name} {mode}")
+        if mode == "ring":
+            want = orc.ring_allreduce(hx, "fp32")
+        else:
+            want = orc.fused_allreduce(hx, "fp32")
+            tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} fused")
+        for r, y in enumerate(host(ys)):
+            assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
+
+
+@pytest.mark.parametrize("count", [524288, 8388608])
+def test_workload_allreduce_fp16_sweep(vrc, orc, count):
+    w = workloads.WORKLOADS["allreduce_fp16_n8_128mib"].with_count(count)
+    xs = workloads.make_inputs(w, DEV)
+    hx = host(xs)
+    for mode in ("ring", "fused"):
+        say(f"{w.name} {mode}")
+        ys = vrc.vrc_allreduce(xs, mode=mode)
+        torch.cuda.synchronize()
+        tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} {mode}")
+        want = orc.ring_allreduce(hx, "fp16") if mode == "ring" else orc.fused_allreduce(hx, "fp16")
+        for r, y in enumerate(host(ys)):
+            assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
+
+
+def _sampled_allreduce(vrc, orc, w, modes, m):
+    xs = workloads.make_inputs(w, DEV)
+    hx = host(xs)
+    idx = sample_indices(w.count, w.n, m, seed=w.seed)
+    tidx = torch.from_numpy(idx.astype(np.int64)).to(DEV)
+    for mode in modes:
+        say(f"{w.name} {mode} ({idx.size} sampled elements)")
+        ys = vrc.vrc_allreduce(xs, mode=mode)
+        torch.cuda.synchronize()
+        ranks_identical(ys, f"{w.name} {mode}")
+        tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} {mode}")
+        at = orc.ring_allreduce_at if mode == "ring" else orc.fused_allreduce_at
+        want = at(hx, w.dtype, idx)
+        for r in (0, w.n - 1):
+            got = workloads.to_numpy(ys[r].reshape(-1)[tidx])
+            assert_bitwise(got, want, f"{w.name} {mode} rank {r} sampled")
+        del ys
+        torch.cuda.empty_cache()
+
+
+def test_workload_allreduce_fp16_n8_128mib(vrc, orc):
+    w = workloads.WORKLOADS["allreduce_fp16_n8_128mib"]
+    _sampled_allreduce(vrc, orc, w, ("ring", "fused"), m=1 << 20)
+
+
+def test_workload_allreduce_bf16_n8_512mib(vrc, orc):
+    w = workloads.WORKLOADS["allreduce_bf16_n8_512mib"]
+    # fused is the headline mode; the ring runs too (not gated by the workload)
+    _sampled_allreduce(vrc, orc, w, ("fused", "ring"), m=1 << 20)
+
+
+def test_workload_all_gather_fp16_n8_heads(vrc, orc):
+    w = workloads.WORKLOADS["all_gather_fp16_n8_heads"]
+    xs = workloads.make_inputs(w, DEV)
+    want = orc.ring_all_gather(host(xs), "fp16", outer=1)
+    for mode in ("ring", "fused"):
+        say(f"{w.name} {mode}")
+        ys = vrc.vrc_all_gather(xs, dim=w.dim, mode=mode)
+        torch.cuda.synchronize()
+        assert tuple(ys[0].shape) == (1, 40, 4096, 128)
+        ranks_identical(ys, f"{w.name} {mode}")
+        for r, y in enumerate(ys):
+            assert_bitwise(workloads.to_numpy(y), want[r], f"{w.name} {mode} rank {r}")
+
+
+def test_workload_reduce_scatter_fp16_n8_act(vrc, orc):
+    w = workloads.WORKLOADS["reduce_scatter_fp16_n8_act"]
+    xs = workloads.make_inputs(w, DEV)
+    hx = host(xs)
+    for mode in ("ring", "fused"):
+        say(f"{w.name} {mode}")
+        ys = vrc.vrc_reduce_scatter(xs, dim=w.dim, mode=mode)
+        torch.cuda.synchronize()
+        assert tuple(ys[0].shape) == (8, 512)
+        want = (orc.ring_reduce_scatter(hx, "fp16", outer=8) if mode == "ring"
+                else orc.fused_reduce_scatter(hx, "fp16", outer=8))
+        for c, y in enumerate(host(ys)):
+            assert_bitwise(y, want[c], f"{w.name} {mode} chunk {c}")
+        # tolerance gate against the fp64 sum of each column block
+        for c in range(w.n):
+            blocks = [x[:, c * 512:(c + 1) * 512].contiguous() for x in xs]
+            tolerance_gate_torch([ys[c]], blocks, w.rtol, f"{w.name} {mode} chunk {c}")
