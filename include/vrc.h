@@ -66,6 +66,10 @@
  *   Errors      Argument errors return before anything is enqueued.
  *   Threads     Calls are re-entrant and thread-safe; calls that overlap on
  *               the same buffers race like any two kernels would.
+ *   Runtime     The library calls the HIP runtime (libamdhip64.so.7) that is
+ *               already loaded in the process.  A process that also uses
+ *               PyTorch-ROCm, which bundles its own copy, must load PyTorch
+ *               before this library so that both use one runtime.
  */
 #ifndef VRC_H
 #define VRC_H

@@ -39,6 +39,15 @@ class VrcError(RuntimeError):
 
 
 def _load():
+    # PyTorch-ROCm ships its own HIP runtime.  Import it first so that
+    # libvrc.so binds to that same runtime (the dynamic linker reuses an
+    # already-loaded libamdhip64 with a matching soname); loading libvrc.so
+    # first would bring up a second HIP runtime that cannot see the device
+    # memory torch allocates.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "

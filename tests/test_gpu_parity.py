@@ -159,6 +159,24 @@ def test_workload_allreduce_fp16_sweep(vrc, orc, count):
             assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
 
 
+def ring_bound(n: int, dtype: str) -> float:
+    """Error bound of the ring's recursive sum with every partial rounded to
+    the storage type: gamma_{n-1} = (n-1)u / (1 - (n-1)u), u the storage unit
+    roundoff (2^-24 fp32, 2^-11 fp16, 2^-8 bf16)."""
+    u = {"fp32": 2.0**-24, "fp16": 2.0**-11, "bf16": 2.0**-8}[dtype]
+    k = n - 1
+    return k * u / (1 - k * u)
+
+
+def gate_rtol(w, mode: str) -> float:
+    """The workload's tolerance for its gated modes.  A bf16 ring is not a
+    gated mode of any workload: 7 roundings to an 8-bit significand can
+    exceed 1e-2, so it is held to its own derived bound instead."""
+    if mode == "ring" and w.dtype == "bf16":
+        return ring_bound(w.n, "bf16")
+    return w.rtol
+
+
 def _sampled_allreduce(vrc, orc, w, modes, m):
     xs = workloads.make_inputs(w, DEV)
     hx = host(xs)
@@ -169,7 +187,7 @@ def _sampled_allreduce(vrc, orc, w, modes, m):
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
         ranks_identical(ys, f"{w.name} {mode}")
-        tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} {mode}")
+        tolerance_gate_torch(ys, xs, gate_rtol(w, mode), f"{w.name} {mode}")
         at = orc.ring_allreduce_at if mode == "ring" else orc.fused_allreduce_at
         want = at(hx, w.dtype, idx)
         for r in (0, w.n - 1):
