@@ -125,6 +125,9 @@ def main() -> int:
     ap.add_argument("--mode", default="fused", choices=["fused", "ring"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra ring-mode timing")
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="only run torch's device copy of 1 GiB (known HBM traffic: 1 GiB read, 1 GiB "
+                         "written per launch), for calibrating rocprofv3 byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -141,6 +144,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr, flush=True)
         return 1
+    if args.probe_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe": "copy", "bytes_read_per_launch": 1 << 30, "bytes_written_per_launch": 1 << 30,
+                          "launches": args.steps}), flush=True)
+        return 0
     w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
     if w.collective != "allreduce":
         print("bench.py: only all-reduce workloads are benchmarked", file=sys.stderr, flush=True)

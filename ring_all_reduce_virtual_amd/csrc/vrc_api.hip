@@ -44,17 +44,48 @@ int env_int(const char* name, int dflt, int lo, int hi)
     return (int)v;
 }
 
+// Launch shape, from measurements on MI355X (HIP events, 8 ranks):
+//  - fused kernels: one 256-lane workgroup per CU is fastest once the whole
+//    operation moves >= 4 GiB (5.4 TB/s for 8 x 512 MiB bf16, the speed of a
+//    plain 8-in/8-out copy on the same buffers); 2 per CU from 1 GiB (128 MiB
+//    per rank: 5.6 TB/s); 8 per CU below that, where the Infinity Cache
+//    holds much of the data and latency hiding matters more than open DRAM
+//    rows;
+//  - ring steps: 4 workgroups per CU (summed over the N per-rank operations)
+//    once a step moves >= 1 GiB, 8 below.
+// Each lane keeps two 16-byte vectors per rank in flight (unroll 2), and
+// loads and stores carry the non-temporal hint (both measured faster for
+// this never-reused stream).  The environment variables override the
+// policy, for measurement.
 struct Tuning {
-    int blocks_per_cu;  // resident workgroups per CU the grid is sized for
-    int unroll;         // independent vectors per lane per fused iteration
-    int nontemporal;    // 1: streaming loads/stores carry the non-temporal hint
+    int fused_blocks_per_cu;  // 0: size policy
+    int step_blocks_per_cu;   // 0: size policy
+    int unroll;               // independent vectors per lane per fused iteration
+    int nontemporal;          // 1: streaming loads/stores carry the non-temporal hint
 };
 
 const Tuning& tuning()
 {
-    static const Tuning t = {env_int("VRC_BLOCKS_PER_CU", 8, 1, 64), env_int("VRC_UNROLL", 1, 1, 4),
+    static const Tuning t = {env_int("VRC_FUSED_BLOCKS_PER_CU", 0, 1, 64),
+                             env_int("VRC_STEP_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 2, 1, 4),
                              env_int("VRC_NT", 1, 0, 1)};
     return t;
+}
+
+constexpr uint64_t kGiB = 1ull << 30;
+
+int fused_blocks_per_cu(uint64_t bytes_moved)
+{
+    if (tuning().fused_blocks_per_cu) return tuning().fused_blocks_per_cu;
+    if (bytes_moved >= 4 * kGiB) return 1;
+    if (bytes_moved >= kGiB) return 2;
+    return 8;
+}
+
+int step_blocks_per_cu(uint64_t bytes_moved)
+{
+    if (tuning().step_blocks_per_cu) return tuning().step_blocks_per_cu;
+    return bytes_moved >= kGiB ? 4 : 8;
 }
 
 hipError_t cu_count(int* out)
@@ -78,11 +109,12 @@ hipError_t cu_count(int* out)
     return hipSuccess;
 }
 
-// Grid x for `ops` operations of at most `work` lane-items each.
-unsigned grid_x(int cus, uint64_t work, int ops)
+// Grid x for `ops` operations of at most `work` lane-items each, capped at
+// blocks_per_cu workgroups per CU over the whole grid.
+unsigned grid_x(int cus, uint64_t work, int ops, int blocks_per_cu)
 {
     const uint64_t want = (work + kBlock - 1) / kBlock;
-    uint64_t cap = (uint64_t)cus * (uint64_t)tuning().blocks_per_cu / (uint64_t)(ops > 0 ? ops : 1);
+    uint64_t cap = (uint64_t)cus * (uint64_t)blocks_per_cu / (uint64_t)(ops > 0 ? ops : 1);
     if (cap < 1) cap = 1;
     uint64_t g = want < cap ? want : cap;
     if (g < 1) g = 1;
@@ -197,10 +229,21 @@ template <class T>
 struct Launch {
     static constexpr int E = T::ESZ;
 
+    // Bytes one step moves: per operation, width*rows elements read from each
+    // operand and written once.
+    template <bool ADD>
+    static uint64_t step_bytes(const vrc::StepArgs& args, int nops)
+    {
+        uint64_t b = 0;
+        for (int i = 0; i < nops; i++) b += args.op[i].rows * args.op[i].width * (uint64_t)E * (ADD ? 3 : 2);
+        return b;
+    }
+
     template <bool ADD>
     static vrc_status_t step(const vrc::StepArgs& args, int nops, uint64_t work, int cus, hipStream_t st)
     {
-        const dim3 grid(grid_x(cus, work, nops), (unsigned)nops);
+        const int bpc = step_blocks_per_cu(step_bytes<ADD>(args, nops));
+        const dim3 grid(grid_x(cus, work, nops, bpc), (unsigned)nops);
         if (tuning().nontemporal)
             hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true>), grid, dim3(kBlock), 0, st, args);
         else
@@ -393,7 +436,7 @@ struct Launch {
         a.count = count;
         a.g = split_rows(addr, 2 * n, 1, nullptr, 0, count, E);
         const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
-        const dim3 grid(grid_x(cus, work, 1));
+        const dim3 grid(grid_x(cus, work, 1, fused_blocks_per_cu(2 * (uint64_t)n * count * E)));
         switch (n) {
 #define VRC_CASE(K) \
     case K: launch_fused_ar_n<K>(a, grid, st); break;
@@ -438,7 +481,7 @@ struct Launch {
             const uint64_t w = k.rows * (ch.g.nvb + ch.g.head + ch.g.tail);
             if (w > work) work = w;
         }
-        const dim3 grid(grid_x(cus, work, n), (unsigned)n);
+        const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * count * E)), (unsigned)n);
         switch (n) {
 #define VRC_CASE(K) \
     case K: launch_fused_rs_n<K>(a, grid, st); break;
@@ -472,7 +515,7 @@ struct Launch {
             const uint64_t w = outer * (a.g[q].nvb + a.g[q].head + a.g[q].tail);
             if (w > work) work = w;
         }
-        const dim3 grid(grid_x(cus, work, n), (unsigned)n);
+        const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * n * count * E)), (unsigned)n);
         if (tuning().nontemporal)
             hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
         else
