@@ -60,9 +60,10 @@ def alg_bytes(mode: str, n: int, size_bytes: int) -> int:
 
 
 def recorded_traffic(workload: str, mode: str):
-    """Measured HBM bytes per launch from profiles/<kernel>_<workload>_counters.md,
+    """Measured HBM bytes per launch from profiles/<kernel>.<workload>.counters.md,
     if those counters were taken on the current kernel sources."""
-    path = os.path.join(PROFILES, f"{mode}_allreduce_{workload}_counters.md")
+    kernel = {"fused": "k_fused_allreduce", "ring": "k_ring_step"}[mode]
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
