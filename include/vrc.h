@@ -88,7 +88,22 @@ typedef struct ihipStream_t* vrc_stream_t; /* the same type as hipStream_t */
 
 typedef enum { VRC_INT32 = 0, VRC_FP32 = 1, VRC_FP16 = 2, VRC_BF16 = 3 } vrc_dtype_t;
 typedef enum { VRC_SUM = 0 } vrc_op_t;
-typedef enum { VRC_RING = 0, VRC_FUSED = 1 } vrc_mode_t;
+/* Kernel family.  VRC_RING, VRC_RING_CHAINED and VRC_RING_ORDER return the same
+ * bits (the ring's summation order, every partial rounded to the storage
+ * type); VRC_FUSED folds in rank order in fp32 and rounds once.
+ *   VRC_RING          one launch per ring step: 2(N-1) launches for the
+ *                     all-reduce, N-1 for either half.
+ *   VRC_FUSED         one launch; every input read once, every output
+ *                     written once.
+ *   VRC_RING_CHAINED  one launch running the same per-step reads and writes
+ *                     as VRC_RING: each element of chunk c walks its chunk's
+ *                     ring steps through the rank buffers (every element's
+ *                     steps depend only on that element, so no grid-wide
+ *                     barrier is needed).
+ *   VRC_RING_ORDER    one launch with the fused traffic (read N, write N):
+ *                     the ring's partials stay in registers.  For the
+ *                     all-gather it equals VRC_FUSED. */
+typedef enum { VRC_RING = 0, VRC_FUSED = 1, VRC_RING_CHAINED = 2, VRC_RING_ORDER = 3 } vrc_mode_t;
 
 typedef enum {
     VRC_OK = 0,

@@ -53,22 +53,22 @@ int env_int(const char* name, int dflt, int lo, int hi)
 //    rows;
 //  - ring steps: 4 workgroups per CU (summed over the N per-rank operations)
 //    once a step moves >= 1 GiB, 8 below.
-// Each lane keeps two 16-byte vectors per rank in flight (unroll 2), and
-// loads and stores carry the non-temporal hint (both measured faster for
-// this never-reused stream).  The environment variables override the
-// policy, for measurement.
+// Each lane keeps two 16-byte vectors per rank in flight (unroll 2).  Loads
+// and stores carry the non-temporal hint (measured faster for this
+// never-reused stream).  The environment variables override the policy,
+// for measurement.
 struct Tuning {
     int fused_blocks_per_cu;  // 0: size policy
     int step_blocks_per_cu;   // 0: size policy
-    int unroll;               // independent vectors per lane per fused iteration
-    int nontemporal;          // 1: streaming loads/stores carry the non-temporal hint
+    int chain_blocks_per_cu;  // 0: size policy
+    int unroll;               // independent vectors per lane per fused iteration (1 or 2)
 };
 
 const Tuning& tuning()
 {
     static const Tuning t = {env_int("VRC_FUSED_BLOCKS_PER_CU", 0, 1, 64),
-                             env_int("VRC_STEP_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 2, 1, 4),
-                             env_int("VRC_NT", 1, 0, 1)};
+                             env_int("VRC_STEP_BLOCKS_PER_CU", 0, 1, 64),
+                             env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 2, 1, 2)};
     return t;
 }
 
@@ -87,6 +87,16 @@ int step_blocks_per_cu(uint64_t bytes_moved)
     if (tuning().step_blocks_per_cu) return tuning().step_blocks_per_cu;
     return bytes_moved >= kGiB ? 4 : 8;
 }
+
+// Memory-faithful chains wait on their own stores between steps, so they
+// need more resident waves than the fused loop to hide latency.
+int chain_blocks_per_cu(uint64_t bytes_moved)
+{
+    if (tuning().chain_blocks_per_cu) return tuning().chain_blocks_per_cu;
+    return bytes_moved >= 4 * kGiB ? 4 : 8;
+}
+
+#define VRC_FOR_N(X) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 
 hipError_t cu_count(int* out)
 {
@@ -244,10 +254,7 @@ struct Launch {
     {
         const int bpc = step_blocks_per_cu(step_bytes<ADD>(args, nops));
         const dim3 grid(grid_x(cus, work, nops, bpc), (unsigned)nops);
-        if (tuning().nontemporal)
-            hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true>), grid, dim3(kBlock), 0, st, args);
-        else
-            hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, false>), grid, dim3(kBlock), 0, st, args);
+        hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true>), grid, dim3(kBlock), 0, st, args);
         return check_launch();
     }
 
@@ -398,23 +405,13 @@ struct Launch {
     }
 
     // ---- fused family ----------------------------------------------------
-    template <int N, int U>
-    static void launch_fused_ar_nu(const vrc::FusedArArgs& a, dim3 grid, hipStream_t st)
-    {
-        if (tuning().nontemporal)
-            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, U, true>), grid, dim3(kBlock), 0, st, a);
-        else
-            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, U, false>), grid, dim3(kBlock), 0, st, a);
-    }
-
     template <int N>
     static void launch_fused_ar_n(const vrc::FusedArArgs& a, dim3 grid, hipStream_t st)
     {
-        switch (tuning().unroll) {
-        case 4: launch_fused_ar_nu<N, 4>(a, grid, st); break;
-        case 2: launch_fused_ar_nu<N, 2>(a, grid, st); break;
-        default: launch_fused_ar_nu<N, 1>(a, grid, st); break;
-        }
+        if (tuning().unroll == 2)
+            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 2, true>), grid, dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 1, true>), grid, dim3(kBlock), 0, st, a);
     }
 
     static vrc_status_t fused_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
@@ -440,8 +437,7 @@ struct Launch {
         switch (n) {
 #define VRC_CASE(K) \
     case K: launch_fused_ar_n<K>(a, grid, st); break;
-            VRC_CASE(2) VRC_CASE(3) VRC_CASE(4) VRC_CASE(5) VRC_CASE(6) VRC_CASE(7) VRC_CASE(8) VRC_CASE(9)
-            VRC_CASE(10) VRC_CASE(11) VRC_CASE(12) VRC_CASE(13) VRC_CASE(14) VRC_CASE(15) VRC_CASE(16)
+            VRC_FOR_N(VRC_CASE)
 #undef VRC_CASE
         default: return VRC_ERR_INVALID_ARG;
         }
@@ -451,10 +447,7 @@ struct Launch {
     template <int N>
     static void launch_fused_rs_n(const vrc::FusedRsArgs& a, dim3 grid, hipStream_t st)
     {
-        if (tuning().nontemporal)
-            hipLaunchKernelGGL((vrc::k_fused_reduce_scatter<T, N, true>), grid, dim3(kBlock), 0, st, a);
-        else
-            hipLaunchKernelGGL((vrc::k_fused_reduce_scatter<T, N, false>), grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((vrc::k_fused_reduce_scatter<T, N, true>), grid, dim3(kBlock), 0, st, a);
     }
 
     static vrc_status_t fused_reduce_scatter(const char* const* x, char* const* y, int n, uint64_t count,
@@ -485,8 +478,7 @@ struct Launch {
         switch (n) {
 #define VRC_CASE(K) \
     case K: launch_fused_rs_n<K>(a, grid, st); break;
-            VRC_CASE(2) VRC_CASE(3) VRC_CASE(4) VRC_CASE(5) VRC_CASE(6) VRC_CASE(7) VRC_CASE(8) VRC_CASE(9)
-            VRC_CASE(10) VRC_CASE(11) VRC_CASE(12) VRC_CASE(13) VRC_CASE(14) VRC_CASE(15) VRC_CASE(16)
+            VRC_FOR_N(VRC_CASE)
 #undef VRC_CASE
         default: return VRC_ERR_INVALID_ARG;
         }
@@ -516,33 +508,155 @@ struct Launch {
             if (w > work) work = w;
         }
         const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * n * count * E)), (unsigned)n);
-        if (tuning().nontemporal)
-            hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
-        else
-            hipLaunchKernelGGL((vrc::k_fused_all_gather<T, false>), grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
+        return check_launch();
+    }
+
+    // ---- single-launch ring (chained per element) ------------------------
+    template <bool MEM>
+    static vrc_status_t chain_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
+                                        hipStream_t st)
+    {
+        if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc::ChainArgs a;
+        uint64_t work = 0;
+        for (int r = 0; r < kMaxRanks; r++) {
+            a.src[r] = r < n ? x[r] : nullptr;
+            a.dst[r] = r < n ? y[r] : nullptr;
+        }
+        for (int c = 0; c < n; c++) {
+            uint64_t off, len;
+            chunk_range(count, n, c, &off, &len);
+            uintptr_t addr[2 * kMaxRanks];
+            for (int r = 0; r < n; r++) {
+                addr[2 * r] = (uintptr_t)(x[r] + off * E);
+                addr[2 * r + 1] = (uintptr_t)(y[r] + off * E);
+            }
+            a.ch[c] = {off, 1, len, 0, split_rows(addr, 2 * n, 1, nullptr, 0, len, E)};
+            const uint64_t w = a.ch[c].g.nvb + a.ch[c].g.head + a.ch[c].g.tail;
+            if (w > work) work = w;
+        }
+        const uint64_t bytes = MEM ? 5 * (uint64_t)(n - 1) * count * E : 2 * (uint64_t)n * count * E;
+        const int bpc = MEM ? chain_blocks_per_cu(bytes) : fused_blocks_per_cu(bytes);
+        const dim3 grid(grid_x(cus, work, n, bpc), (unsigned)n);
+        switch (n) {
+#define VRC_CASE(K) \
+    case K: hipLaunchKernelGGL((vrc::k_ring_chain_allreduce<T, K, MEM, true>), grid, dim3(kBlock), 0, st, a); break;
+            VRC_FOR_N(VRC_CASE)
+#undef VRC_CASE
+        default: return VRC_ERR_INVALID_ARG;
+        }
+        return check_launch();
+    }
+
+    template <bool MEM>
+    static vrc_status_t chain_reduce_scatter(const char* const* x, char* const* y, int n, uint64_t count,
+                                             uint64_t outer, int cus, hipStream_t st)
+    {
+        if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc::ChainArgs a;
+        uint64_t work = 0;
+        for (int r = 0; r < kMaxRanks; r++) {
+            a.src[r] = r < n ? x[r] : nullptr;
+            a.dst[r] = r < n ? y[r] : nullptr;
+        }
+        for (int c = 0; c < n; c++) {
+            const Chunk k = rs_chunk(count, outer, n, c);
+            uintptr_t addr[kMaxRanks + 1];
+            for (int r = 0; r < n; r++) addr[r] = (uintptr_t)(x[r] + k.off * E);
+            addr[n] = (uintptr_t)y[c];
+            const uint64_t strides[2] = {k.stride * E, k.width * E};
+            a.ch[c] = {k.off, k.rows, k.width, k.stride, split_rows(addr, n + 1, k.rows, strides, 2, k.width, E)};
+            const uint64_t w = k.rows * (a.ch[c].g.nvb + a.ch[c].g.head + a.ch[c].g.tail);
+            if (w > work) work = w;
+        }
+        const uint64_t bytes = MEM ? 3 * (uint64_t)(n - 1) * count * E : (uint64_t)(n + 1) * count * E;
+        const int bpc = MEM ? chain_blocks_per_cu(bytes) : fused_blocks_per_cu(bytes);
+        const dim3 grid(grid_x(cus, work, n, bpc), (unsigned)n);
+        switch (n) {
+#define VRC_CASE(K) \
+    case K:         \
+        hipLaunchKernelGGL((vrc::k_ring_chain_reduce_scatter<T, K, MEM, true>), grid, dim3(kBlock), 0, st, a); break;
+            VRC_FOR_N(VRC_CASE)
+#undef VRC_CASE
+        default: return VRC_ERR_INVALID_ARG;
+        }
+        return check_launch();
+    }
+
+    static vrc_status_t chain_all_gather(const char* const* x, char* const* y, int n, uint64_t count,
+                                         uint64_t outer, int cus, hipStream_t st)
+    {
+        if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc::FusedAgArgs a;
+        const uint64_t row = count / outer;
+        a.rows = outer;
+        a.width = row;
+        a.n = n;
+        uint64_t work = 0;
+        for (int r = 0; r < kMaxRanks; r++) {
+            a.src[r] = r < n ? x[r] : nullptr;
+            a.dst[r] = r < n ? y[r] : nullptr;
+        }
+        for (int q = 0; q < n; q++) {
+            uintptr_t addr[kMaxRanks + 1];
+            addr[0] = (uintptr_t)x[q];
+            for (int r = 0; r < n; r++) addr[r + 1] = (uintptr_t)(y[r] + (uint64_t)q * row * E);
+            const uint64_t strides[2] = {row * E, (uint64_t)n * row * E};
+            a.g[q] = split_rows(addr, n + 1, outer, strides, 2, row, E);
+            const uint64_t w = outer * (a.g[q].nvb + a.g[q].head + a.g[q].tail);
+            if (w > work) work = w;
+        }
+        const dim3 grid(grid_x(cus, work, n, chain_blocks_per_cu(2 * (uint64_t)n * n * count * E)), (unsigned)n);
+        switch (n) {
+#define VRC_CASE(K) \
+    case K: hipLaunchKernelGGL((vrc::k_ring_chain_all_gather<T, K, true>), grid, dim3(kBlock), 0, st, a); break;
+            VRC_FOR_N(VRC_CASE)
+#undef VRC_CASE
+        default: return VRC_ERR_INVALID_ARG;
+        }
         return check_launch();
     }
 };
 
-enum class Op { AR_RING, AR_FUSED, RS_RING, RS_FUSED, AG_RING, AG_FUSED };
+enum class Coll { AR, RS, AG };
 
 template <class T>
-vrc_status_t run_typed(Op op, const char* const* x, char* const* y, int n, uint64_t count, uint64_t outer,
-                       int cus, hipStream_t st)
+vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* const* y, int n, uint64_t count,
+                       uint64_t outer, int cus, hipStream_t st)
 {
-    switch (op) {
-    case Op::AR_RING: return Launch<T>::ring_allreduce(x, y, n, count, cus, st);
-    case Op::AR_FUSED: return Launch<T>::fused_allreduce(x, y, n, count, cus, st);
-    case Op::RS_RING: return Launch<T>::ring_reduce_scatter(x, y, n, count, outer, cus, st);
-    case Op::RS_FUSED: return Launch<T>::fused_reduce_scatter(x, y, n, count, outer, cus, st);
-    case Op::AG_RING: return Launch<T>::ring_all_gather(x, y, n, count, outer, cus, st);
-    case Op::AG_FUSED: return Launch<T>::fused_all_gather(x, y, n, count, outer, cus, st);
+    using L = Launch<T>;
+    switch (coll) {
+    case Coll::AR:
+        switch (mode) {
+        case VRC_RING: return L::ring_allreduce(x, y, n, count, cus, st);
+        case VRC_FUSED: return L::fused_allreduce(x, y, n, count, cus, st);
+        case VRC_RING_CHAINED: return L::template chain_allreduce<true>(x, y, n, count, cus, st);
+        case VRC_RING_ORDER: return L::template chain_allreduce<false>(x, y, n, count, cus, st);
+        }
+        break;
+    case Coll::RS:
+        switch (mode) {
+        case VRC_RING: return L::ring_reduce_scatter(x, y, n, count, outer, cus, st);
+        case VRC_FUSED: return L::fused_reduce_scatter(x, y, n, count, outer, cus, st);
+        case VRC_RING_CHAINED: return L::template chain_reduce_scatter<true>(x, y, n, count, outer, cus, st);
+        case VRC_RING_ORDER: return L::template chain_reduce_scatter<false>(x, y, n, count, outer, cus, st);
+        }
+        break;
+    case Coll::AG:
+        switch (mode) {
+        case VRC_RING: return L::ring_all_gather(x, y, n, count, outer, cus, st);
+        case VRC_FUSED:
+        case VRC_RING_ORDER: return L::fused_all_gather(x, y, n, count, outer, cus, st);
+        case VRC_RING_CHAINED: return L::chain_all_gather(x, y, n, count, outer, cus, st);
+        }
+        break;
     }
     return VRC_ERR_UNSUPPORTED;
 }
 
-vrc_status_t run(Op op, vrc_dtype_t dt, const void* const* send, void* const* recv, int n, uint64_t count,
-                 uint64_t outer, hipStream_t st)
+vrc_status_t run(Coll coll, vrc_mode_t mode, vrc_dtype_t dt, const void* const* send, void* const* recv, int n,
+                 uint64_t count, uint64_t outer, hipStream_t st)
 {
     int cus = 0;
     hipError_t e = cu_count(&cus);
@@ -555,12 +669,17 @@ vrc_status_t run(Op op, vrc_dtype_t dt, const void* const* send, void* const* re
         y[r] = static_cast<char*>(recv[r]);
     }
     switch (dt) {
-    case VRC_INT32: return run_typed<vrc::I32>(op, x, y, n, count, outer, cus, st);
-    case VRC_FP32: return run_typed<vrc::F32>(op, x, y, n, count, outer, cus, st);
-    case VRC_FP16: return run_typed<vrc::F16>(op, x, y, n, count, outer, cus, st);
-    case VRC_BF16: return run_typed<vrc::BF16>(op, x, y, n, count, outer, cus, st);
+    case VRC_INT32: return run_typed<vrc::I32>(coll, mode, x, y, n, count, outer, cus, st);
+    case VRC_FP32: return run_typed<vrc::F32>(coll, mode, x, y, n, count, outer, cus, st);
+    case VRC_FP16: return run_typed<vrc::F16>(coll, mode, x, y, n, count, outer, cus, st);
+    case VRC_BF16: return run_typed<vrc::BF16>(coll, mode, x, y, n, count, outer, cus, st);
     }
     return VRC_ERR_UNSUPPORTED;
+}
+
+bool mode_ok(vrc_mode_t m)
+{
+    return m == VRC_RING || m == VRC_FUSED || m == VRC_RING_CHAINED || m == VRC_RING_ORDER;
 }
 
 }  // namespace
@@ -575,15 +694,14 @@ vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nrank
 {
     vrc_status_t rc = check_common(send, recv, nranks, dtype);
     if (rc) return rc;
-    if (op != VRC_SUM || (mode != VRC_RING && mode != VRC_FUSED)) return VRC_ERR_UNSUPPORTED;
+    if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
     const uint64_t bytes = (uint64_t)count * (uint64_t)esize(dtype);
     uint64_t rb[kMaxRanks];
     for (int r = 0; r < nranks; r++) rb[r] = bytes;
     rc = check_buffers(send, recv, nranks, bytes, rb, true);
     if (rc) return rc;
     if (count == 0) return VRC_OK;
-    return run(mode == VRC_RING ? Op::AR_RING : Op::AR_FUSED, dtype, send, recv, nranks, count, 1,
-               (hipStream_t)stream);
+    return run(Coll::AR, mode, dtype, send, recv, nranks, count, 1, (hipStream_t)stream);
 }
 
 vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int nranks, size_t count,
@@ -592,7 +710,7 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
 {
     vrc_status_t rc = check_common(send, recv, nranks, dtype);
     if (rc) return rc;
-    if (op != VRC_SUM || (mode != VRC_RING && mode != VRC_FUSED)) return VRC_ERR_UNSUPPORTED;
+    if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     if (outer > 1 && (count / outer) % (uint64_t)nranks != 0) return VRC_ERR_INVALID_ARG;
     const int E = esize(dtype);
@@ -609,8 +727,7 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
     rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, false);
     if (rc) return rc;
     if (count == 0) return VRC_OK;
-    return run(mode == VRC_RING ? Op::RS_RING : Op::RS_FUSED, dtype, send, recv, nranks, count, outer,
-               (hipStream_t)stream);
+    return run(Coll::RS, mode, dtype, send, recv, nranks, count, outer, (hipStream_t)stream);
 }
 
 vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nranks, size_t count,
@@ -618,7 +735,7 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
 {
     vrc_status_t rc = check_common(send, recv, nranks, dtype);
     if (rc) return rc;
-    if (mode != VRC_RING && mode != VRC_FUSED) return VRC_ERR_UNSUPPORTED;
+    if (!mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     const int E = esize(dtype);
     uint64_t rb[kMaxRanks];
@@ -626,8 +743,7 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
     rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, false);
     if (rc) return rc;
     if (count == 0) return VRC_OK;
-    return run(mode == VRC_RING ? Op::AG_RING : Op::AG_FUSED, dtype, send, recv, nranks, count, outer,
-               (hipStream_t)stream);
+    return run(Coll::AG, mode, dtype, send, recv, nranks, count, outer, (hipStream_t)stream);
 }
 
 vrc_status_t vrc_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* length)

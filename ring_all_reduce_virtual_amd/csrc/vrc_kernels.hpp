@@ -252,4 +252,195 @@ __global__ __launch_bounds__(kBlock) void k_fused_all_gather(FusedAgArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Single-launch ring.  In the ring schedule element i of chunk c depends only
+// on element i of chunk c at the previous step: the reduce-scatter carries
+// the partial of chunk c from rank c+1 to c+2 ... to c+N-1 (= c-1), and the
+// all-gather relays the finished chunk from rank c-1 to c, c+1, ..., c+N-2.
+// Each element is therefore an independent chain of 2(N-1) operations, and
+// one launch can run every chain to the end with no grid-wide barrier.
+// blockIdx.y = chunk c, so the rank rotation is uniform per workgroup.
+//
+// MEM = true ("chained"): every step writes its partial into the next
+// rank's buffer and the following step reads it back from there, so the
+// reads and writes per step are those of the per-step ring launches.
+// MEM = false ("ring order"): the partial stays in registers; every input is
+// read once and every output written once (the fused kernel's traffic), with
+// the ring's summation order and per-step rounding.  Both give the per-step
+// ring's bits.
+// ---------------------------------------------------------------------------
+struct ChainChunk {
+    uint64_t off;          // element offset of chunk (0,0) in every rank buffer
+    uint64_t rows, width;  // chunk geometry
+    uint64_t stride;       // row stride of the rank buffers, elements
+    RowSplit g;
+};
+
+struct ChainArgs {
+    const char* src[kMaxRanks];
+    char* dst[kMaxRanks];
+    ChainChunk ch[kMaxRanks];
+};
+
+// All-reduce chain over flat chunks (rows == 1).
+template <class T, int N, bool MEM, bool NT>
+__global__ __launch_bounds__(kBlock) void k_ring_chain_allreduce(ChainArgs a)
+{
+    const int c = blockIdx.y;
+    const ChainChunk& k = a.ch[c];
+    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    constexpr uint64_t E = T::ESZ;
+    const int owner = (c + N - 1) % N;  // holds chunk c complete after the reduce-scatter
+    const uint64_t body = (k.off + k.g.head) * E;
+    for (uint64_t v = tid; v < k.g.nvb; v += nthreads) {
+        const uint64_t o = body + v * 16;
+        u32x4 p;
+        if constexpr (MEM) {
+            p = ld16<NT>(a.src[c] + o);
+#pragma unroll
+            for (int t = 1; t < N; t++) {
+                const int r = (c + t) % N;
+                const u32x4 own = ld16<NT>(a.src[r] + o);
+                if (t > 1) p = ld16<NT>(a.dst[(c + t - 1) % N] + o);
+                p = add_v<T>(p, own);
+                st16<NT>(a.dst[r] + o, p);
+            }
+#pragma unroll
+            for (int s = 0; s < N - 1; s++) {
+                const int r = (c + s) % N;
+                st16<NT>(a.dst[r] + o, ld16<NT>(a.dst[(c + s + N - 1) % N] + o));
+            }
+        } else {
+            u32x4 in[N];
+#pragma unroll
+            for (int t = 0; t < N; t++) in[t] = ld16<NT>(a.src[(c + t) % N] + o);
+            p = in[0];
+#pragma unroll
+            for (int t = 1; t < N; t++) p = add_v<T>(p, in[t]);
+#pragma unroll
+            for (int t = 0; t < N; t++) st16<NT>(a.dst[(owner + 1 + t) % N] + o, p);
+        }
+    }
+    const uint64_t ns = k.g.head + k.g.tail;
+    for (uint64_t j = tid; j < ns; j += nthreads) {
+        const uint64_t col = (j < k.g.head) ? j : k.g.head + k.g.nvb * T::VEC + (j - k.g.head);
+        const uint64_t o = (k.off + col) * E;
+        typename T::S p = load_s<T>(a.src[c] + o);
+        if constexpr (MEM) {
+#pragma unroll
+            for (int t = 1; t < N; t++) {
+                const int r = (c + t) % N;
+                const typename T::S own = load_s<T>(a.src[r] + o);
+                if (t > 1) p = load_s<T>(a.dst[(c + t - 1) % N] + o);
+                p = add_s<T>(p, own);
+                store_s<T>(a.dst[r] + o, p);
+            }
+#pragma unroll
+            for (int s = 0; s < N - 1; s++)
+                store_s<T>(a.dst[(c + s) % N] + o, load_s<T>(a.dst[(c + s + N - 1) % N] + o));
+        } else {
+            typename T::S in[N];
+#pragma unroll
+            for (int t = 0; t < N; t++) in[t] = load_s<T>(a.src[(c + t) % N] + o);
+#pragma unroll
+            for (int t = 1; t < N; t++) p = add_s<T>(p, in[t]);
+#pragma unroll
+            for (int t = 0; t < N; t++) store_s<T>(a.dst[(owner + 1 + t) % N] + o, p);
+        }
+    }
+}
+
+// Reduce-scatter chain: chunk c of every rank ([rows, width] with row stride
+// `stride`) is summed in ring order into output c ([rows, width], dense).
+template <class T, int N, bool MEM, bool NT>
+__global__ __launch_bounds__(kBlock) void k_ring_chain_reduce_scatter(ChainArgs a)
+{
+    const int c = blockIdx.y;
+    const ChainChunk& k = a.ch[c];
+    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    constexpr uint64_t E = T::ESZ;
+    char* out = a.dst[c];
+    const uint64_t nv = k.rows * k.g.nvb;
+    for (uint64_t v = tid; v < nv; v += nthreads) {
+        const uint64_t row = (k.rows == 1) ? 0 : v / k.g.nvb;
+        const uint64_t col = (v - row * k.g.nvb) * 16 + k.g.head * E;
+        const uint64_t so = (k.off + row * k.stride) * E + col;
+        const uint64_t dof = row * k.width * E + col;
+        u32x4 p;
+        if constexpr (MEM) {
+            p = ld16<NT>(a.src[c] + so);
+#pragma unroll
+            for (int t = 1; t < N; t++) {
+                const u32x4 own = ld16<NT>(a.src[(c + t) % N] + so);
+                if (t > 1) p = ld16<NT>(out + dof);
+                p = add_v<T>(p, own);
+                st16<NT>(out + dof, p);
+            }
+        } else {
+            u32x4 in[N];
+#pragma unroll
+            for (int t = 0; t < N; t++) in[t] = ld16<NT>(a.src[(c + t) % N] + so);
+            p = in[0];
+#pragma unroll
+            for (int t = 1; t < N; t++) p = add_v<T>(p, in[t]);
+            st16<NT>(out + dof, p);
+        }
+    }
+    const uint64_t ns = k.rows * (k.g.head + k.g.tail);
+    for (uint64_t j = tid; j < ns; j += nthreads) {
+        uint64_t row, col;
+        scalar_slot(j, k.g, T::VEC, row, col);
+        const uint64_t so = (k.off + row * k.stride + col) * E;
+        const uint64_t dof = (row * k.width + col) * E;
+        typename T::S p = load_s<T>(a.src[c] + so);
+#pragma unroll
+        for (int t = 1; t < N; t++) {
+            const typename T::S own = load_s<T>(a.src[(c + t) % N] + so);
+            if (MEM && t > 1) p = load_s<T>(out + dof);
+            p = add_s<T>(p, own);
+            if (MEM || t == N - 1) store_s<T>(out + dof, p);
+        }
+    }
+}
+
+// All-gather chain (memory-faithful relay): slab q (blockIdx.y) is copied
+// from input q into output q and output q+1, then relayed output q+t-1 ->
+// output q+t for t = 2..N-1.  Inputs are [rows, width]; outputs are
+// [rows, N*width] with slab q at column q*width.
+template <class T, int N, bool NT>
+__global__ __launch_bounds__(kBlock) void k_ring_chain_all_gather(FusedAgArgs a)
+{
+    const int q = blockIdx.y;
+    const RowSplit& g = a.g[q];
+    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    constexpr uint64_t E = T::ESZ;
+    const uint64_t s_dst = (uint64_t)N * a.width;
+    const uint64_t slab = (uint64_t)q * a.width;
+    const uint64_t nv = a.rows * g.nvb;
+    for (uint64_t v = tid; v < nv; v += nthreads) {
+        const uint64_t row = (a.rows == 1) ? 0 : v / g.nvb;
+        const uint64_t col = (v - row * g.nvb) * 16 + g.head * E;
+        const uint64_t dof = (row * s_dst + slab) * E + col;
+        const u32x4 x = ld16<NT>(a.src[q] + row * a.width * E + col);
+        st16<NT>(a.dst[q] + dof, x);
+        if (N > 1) st16<NT>(a.dst[(q + 1) % N] + dof, x);
+#pragma unroll
+        for (int t = 2; t < N; t++) st16<NT>(a.dst[(q + t) % N] + dof, ld16<NT>(a.dst[(q + t - 1) % N] + dof));
+    }
+    const uint64_t ns = a.rows * (g.head + g.tail);
+    for (uint64_t j = tid; j < ns; j += nthreads) {
+        uint64_t row, col;
+        scalar_slot(j, g, T::VEC, row, col);
+        const uint64_t dof = (row * s_dst + slab + col) * E;
+        const typename T::S x = load_s<T>(a.src[q] + (row * a.width + col) * E);
+        store_s<T>(a.dst[q] + dof, x);
+        if (N > 1) store_s<T>(a.dst[(q + 1) % N] + dof, x);
+#pragma unroll
+        for (int t = 2; t < N; t++) store_s<T>(a.dst[(q + t) % N] + dof, load_s<T>(a.dst[(q + t - 1) % N] + dof));
+    }
+}
+
 }  // namespace vrc

@@ -12,6 +12,8 @@ from tests.parity_util import assert_bitwise, host
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 DTYPES = ("int32", "fp32", "fp16", "bf16")
+MODES = ("ring", "fused", "ring_chained", "ring_order")
+RING_FAMILY = ("ring", "ring_chained", "ring_order")
 
 
 def say(msg):
@@ -32,10 +34,16 @@ def orc():
 
 
 def oracle_ar(orc, hx, dtype, mode):
-    return orc.ring_allreduce(hx, dtype) if mode == "ring" else orc.fused_allreduce(hx, dtype)
+    return orc.ring_allreduce(hx, dtype) if mode in RING_FAMILY else orc.fused_allreduce(hx, dtype)
 
 
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+def oracle_rs(orc, hx, dtype, mode, outer=1):
+    if mode in RING_FAMILY:
+        return orc.ring_reduce_scatter(hx, dtype, outer=outer)
+    return orc.fused_reduce_scatter(hx, dtype, outer=outer)
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_in_place_equals_out_of_place(vrc, orc, mode, dtype):
     say(f"in place {mode} {dtype}")
@@ -48,7 +56,7 @@ def test_in_place_equals_out_of_place(vrc, orc, mode, dtype):
         assert_bitwise(workloads.to_numpy(ys[r]), want[r], f"in place {mode} {dtype} rank {r}")
 
 
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("mode", MODES)
 def test_some_ranks_in_place(vrc, orc, mode):
     say(f"mixed in place {mode}")
     n, count = 5, 40000
@@ -73,7 +81,7 @@ def _views(xs, offsets, count):
     return out
 
 
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("offsets", ["same", "mixed"])
 def test_misaligned_views(vrc, orc, mode, dtype, offsets):
@@ -91,7 +99,7 @@ def test_misaligned_views(vrc, orc, mode, dtype, offsets):
         assert_bitwise(workloads.to_numpy(vy[r]), want[r], f"misaligned {mode} {dtype} rank {r}")
     # reduce-scatter and all-gather through misaligned views too
     rs = vrc.vrc_reduce_scatter(vx, mode=mode)
-    want_rs = (orc.ring_reduce_scatter if mode == "ring" else orc.fused_reduce_scatter)(host(xs), dtype)
+    want_rs = oracle_rs(orc, host(xs), dtype, mode)
     ag = vrc.vrc_all_gather(vx, mode=mode)
     want_ag = orc.ring_all_gather(host(xs), dtype)
     torch.cuda.synchronize()
@@ -100,7 +108,7 @@ def test_misaligned_views(vrc, orc, mode, dtype, offsets):
         assert_bitwise(workloads.to_numpy(ag[c]), want_ag[c], f"misaligned ag {mode} {dtype} rank {c}")
 
 
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_single_rank_is_identity(vrc, mode, dtype):
     say(f"n=1 {mode} {dtype}")
@@ -115,7 +123,7 @@ def test_single_rank_is_identity(vrc, mode, dtype):
         assert_bitwise(workloads.to_numpy(t), hx, f"n=1 {what} {mode} {dtype}")
 
 
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("n,count", [(8, 3), (16, 15), (4, 1), (3, 0)])
 def test_fewer_elements_than_ranks(vrc, orc, mode, n, count):
     say(f"count<n {mode} n={n} count={count}")
@@ -125,13 +133,13 @@ def test_fewer_elements_than_ranks(vrc, orc, mode, n, count):
     torch.cuda.synchronize()
     hx = host(xs)
     want = oracle_ar(orc, hx, "fp32", mode)
-    want_rs = (orc.ring_reduce_scatter if mode == "ring" else orc.fused_reduce_scatter)(hx, "fp32")
+    want_rs = oracle_rs(orc, hx, "fp32", mode)
     for r in range(n):
         assert_bitwise(workloads.to_numpy(ys[r]), want[r], f"count<n {mode} rank {r}")
         assert_bitwise(workloads.to_numpy(rs[r]), want_rs[r], f"count<n rs {mode} chunk {r}")
 
 
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("mode", MODES)
 def test_repeat_runs_are_bitwise_identical(vrc, mode):
     say(f"determinism {mode}")
     xs = workloads.make_inputs(workloads.WORKLOADS["allreduce_fp32_n8_16mib"], DEV)
@@ -143,14 +151,15 @@ def test_repeat_runs_are_bitwise_identical(vrc, mode):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("mode", RING_FAMILY)
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_all_gather_of_reduce_scatter_is_allreduce(vrc, dtype):
-    say(f"composition {dtype}")
+def test_all_gather_of_reduce_scatter_is_allreduce(vrc, dtype, mode):
+    say(f"composition {dtype} {mode}")
     n, count = 8, 8 * 12345  # equal chunks
     xs = workloads.random_ranks(n, count, dtype, seed=405, device=DEV)
-    ar = vrc.vrc_allreduce(xs, mode="ring")
-    rs = vrc.vrc_reduce_scatter(xs, mode="ring")
-    ag = vrc.vrc_all_gather(rs, mode="ring")
+    ar = vrc.vrc_allreduce(xs, mode=mode)
+    rs = vrc.vrc_reduce_scatter(xs, mode=mode)
+    ag = vrc.vrc_all_gather(rs, mode=mode)
     torch.cuda.synchronize()
     for r in range(n):
         assert_bitwise(workloads.to_numpy(ag[r]), workloads.to_numpy(ar[r]), f"AG(RS) vs AR {dtype} rank {r}")
@@ -173,7 +182,7 @@ def test_exact_small_integers_ring_equals_fused(vrc):
 def test_int32_wraps(vrc):
     say("int32 wrap")
     xs = [torch.full((1000,), 2**31 - 1, dtype=torch.int32, device=DEV) for _ in range(3)]
-    for mode in ("ring", "fused"):
+    for mode in MODES:
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
         assert torch.all(ys[0] == 2**31 - 3)
@@ -182,7 +191,7 @@ def test_int32_wraps(vrc):
 def test_fp16_overflow_goes_to_inf(vrc, orc):
     say("fp16 overflow")
     xs = [torch.full((100,), 60000.0, dtype=torch.float16, device=DEV) for _ in range(2)]
-    for mode in ("ring", "fused"):
+    for mode in MODES:
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
         assert torch.all(torch.isinf(ys[1])) and torch.all(ys[1] > 0)
@@ -195,7 +204,7 @@ def test_subnormals_are_kept(vrc, orc):
     tiny16 = torch.tensor([6e-8, -1.2e-7, 3e-5, 6.1e-5] * 64, dtype=torch.float16, device=DEV)
     for x0, dtype in ((tiny32, "fp32"), (tiny16, "fp16"), (tiny32.to(torch.bfloat16), "bf16")):
         xs = [x0 * (r + 1) for r in range(n)]
-        for mode in ("ring", "fused"):
+        for mode in MODES:
             ys = vrc.vrc_allreduce(xs, mode=mode)
             torch.cuda.synchronize()
             want = oracle_ar(orc, host(xs), dtype, mode)
@@ -209,12 +218,11 @@ def test_side_stream(vrc, orc):
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        ys = vrc.vrc_allreduce(xs, mode="ring")
-        zs = vrc.vrc_allreduce(xs, mode="fused")
+        outs = {m: vrc.vrc_allreduce(xs, mode=m) for m in MODES}
     s.synchronize()
     hx = host(xs)
-    assert_bitwise(workloads.to_numpy(ys[3]), orc.ring_allreduce(hx, "bf16")[3], "side stream ring")
-    assert_bitwise(workloads.to_numpy(zs[3]), orc.fused_allreduce(hx, "bf16")[3], "side stream fused")
+    for m, ys in outs.items():
+        assert_bitwise(workloads.to_numpy(ys[3]), oracle_ar(orc, hx, "bf16", m)[3], f"side stream {m}")
 
 
 def test_errors_through_the_binding(vrc):
@@ -231,7 +239,7 @@ def test_errors_through_the_binding(vrc):
     with pytest.raises(TypeError):
         vrc.vrc_allreduce([x.double() for x in xs])
     empty = [torch.empty(0, device=DEV) for _ in range(4)]
-    for mode in ("ring", "fused"):
+    for mode in MODES:
         vrc.vrc_allreduce(empty, mode=mode)
         vrc.vrc_all_gather(empty, mode=mode)
     torch.cuda.synchronize()

@@ -20,6 +20,8 @@ from tests.parity_util import (assert_bitwise, host, ranks_identical, sample_ind
 pytestmark = pytest.mark.gpu
 
 DTYPES = ("int32", "fp32", "fp16", "bf16")
+MODES = ("ring", "fused", "ring_chained", "ring_order")
+RING_FAMILY = ("ring", "ring_chained", "ring_order")  # all return the per-step ring's bits
 
 
 def say(msg):
@@ -45,7 +47,7 @@ DEV = "cuda:0"
 # ---------------------------------------------------------------------------
 # all-reduce, small and ragged, every dtype and mode, full oracle comparison
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("n,count", [(2, 1), (2, 4099), (3, 5), (3, 100003), (4, 4099), (5, 3),
                                      (8, 7), (8, 65536 * 3 + 13), (16, 1), (16, 100003)])
@@ -55,7 +57,7 @@ def test_allreduce_small(vrc, orc, mode, dtype, n, count):
     ys = vrc.vrc_allreduce(xs, mode=mode)
     torch.cuda.synchronize()
     hx = host(xs)
-    want = orc.ring_allreduce(hx, dtype) if mode == "ring" else orc.fused_allreduce(hx, dtype)
+    want = orc.ring_allreduce(hx, dtype) if mode in RING_FAMILY else orc.fused_allreduce(hx, dtype)
     for r, y in enumerate(host(ys)):
         assert_bitwise(y, want[r], f"{mode} {dtype} n={n} count={count} rank {r}")
 
@@ -70,7 +72,7 @@ RS_CASES = [  # (n, shape, dim)
 ]
 
 
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("n,shape,dim", RS_CASES)
 def test_reduce_scatter_small(vrc, orc, mode, dtype, n, shape, dim):
@@ -80,7 +82,7 @@ def test_reduce_scatter_small(vrc, orc, mode, dtype, n, shape, dim):
     torch.cuda.synchronize()
     outer = int(np.prod(shape[:dim % len(shape)])) if len(shape) > 1 else 1
     hx = host(xs)
-    want = (orc.ring_reduce_scatter(hx, dtype, outer=outer) if mode == "ring"
+    want = (orc.ring_reduce_scatter(hx, dtype, outer=outer) if mode in RING_FAMILY
             else orc.fused_reduce_scatter(hx, dtype, outer=outer))
     for c, y in enumerate(host(ys)):
         assert_bitwise(y, want[c], f"rs {mode} {dtype} n={n} shape={shape} chunk {c}")
@@ -92,7 +94,7 @@ AG_CASES = [  # (n, shape, dim)
 ]
 
 
-@pytest.mark.parametrize("mode", ["ring", "fused"])
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("n,shape,dim", AG_CASES)
 def test_all_gather_small(vrc, orc, mode, dtype, n, shape, dim):
@@ -116,11 +118,11 @@ def test_workload_allreduce_int32_n4_4099(vrc, orc):
     xs = workloads.make_inputs(w, DEV)
     hx = host(xs)
     naive = np.sum([x.astype(np.int64) for x in hx], axis=0).astype(np.int32)
-    for mode in ("ring", "fused"):
+    for mode in MODES:
         say(f"{w.name} {mode}")
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
-        want = orc.ring_allreduce(hx, "int32") if mode == "ring" else orc.fused_allreduce(hx, "int32")
+        want = orc.ring_allreduce(hx, "int32") if mode in RING_FAMILY else orc.fused_allreduce(hx, "int32")
         for r, y in enumerate(host(ys)):
             assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
             assert_bitwise(y, naive, f"{w.name} {mode} rank {r} vs naive sum")
@@ -130,13 +132,14 @@ def test_workload_allreduce_fp32_n8_16mib(vrc, orc):
     w = workloads.WORKLOADS["allreduce_fp32_n8_16mib"]
     xs = workloads.make_inputs(w, DEV)
     hx = host(xs)
-    for mode in ("ring", "fused"):
+    want_ring = orc.ring_allreduce(hx, "fp32")
+    for mode in MODES:
         say(f"{w.name} {mode}")
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
         ranks_identical(ys, f"{w.name} {mode}")
-        if mode == "ring":
-            want = orc.ring_allreduce(hx, "fp32")
+        if mode in RING_FAMILY:
+            want = want_ring
         else:
             want = orc.fused_allreduce(hx, "fp32")
             tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} fused")
@@ -149,12 +152,13 @@ def test_workload_allreduce_fp16_sweep(vrc, orc, count):
     w = workloads.WORKLOADS["allreduce_fp16_n8_128mib"].with_count(count)
     xs = workloads.make_inputs(w, DEV)
     hx = host(xs)
-    for mode in ("ring", "fused"):
+    want_ring = orc.ring_allreduce(hx, "fp16")
+    for mode in MODES:
         say(f"{w.name} {mode}")
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
         tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} {mode}")
-        want = orc.ring_allreduce(hx, "fp16") if mode == "ring" else orc.fused_allreduce(hx, "fp16")
+        want = want_ring if mode in RING_FAMILY else orc.fused_allreduce(hx, "fp16")
         for r, y in enumerate(host(ys)):
             assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
 
@@ -172,7 +176,7 @@ def gate_rtol(w, mode: str) -> float:
     """The workload's tolerance for its gated modes.  A bf16 ring is not a
     gated mode of any workload: 7 roundings to an 8-bit significand can
     exceed 1e-2, so it is held to its own derived bound instead."""
-    if mode == "ring" and w.dtype == "bf16":
+    if mode in RING_FAMILY and w.dtype == "bf16":
         return ring_bound(w.n, "bf16")
     return w.rtol
 
@@ -188,7 +192,7 @@ def _sampled_allreduce(vrc, orc, w, modes, m):
         torch.cuda.synchronize()
         ranks_identical(ys, f"{w.name} {mode}")
         tolerance_gate_torch(ys, xs, gate_rtol(w, mode), f"{w.name} {mode}")
-        at = orc.ring_allreduce_at if mode == "ring" else orc.fused_allreduce_at
+        at = orc.ring_allreduce_at if mode in RING_FAMILY else orc.fused_allreduce_at
         want = at(hx, w.dtype, idx)
         for r in (0, w.n - 1):
             got = workloads.to_numpy(ys[r].reshape(-1)[tidx])
@@ -199,20 +203,20 @@ def _sampled_allreduce(vrc, orc, w, modes, m):
 
 def test_workload_allreduce_fp16_n8_128mib(vrc, orc):
     w = workloads.WORKLOADS["allreduce_fp16_n8_128mib"]
-    _sampled_allreduce(vrc, orc, w, ("ring", "fused"), m=1 << 20)
+    _sampled_allreduce(vrc, orc, w, MODES, m=1 << 20)
 
 
 def test_workload_allreduce_bf16_n8_512mib(vrc, orc):
     w = workloads.WORKLOADS["allreduce_bf16_n8_512mib"]
-    # fused is the headline mode; the ring runs too (not gated by the workload)
-    _sampled_allreduce(vrc, orc, w, ("fused", "ring"), m=1 << 20)
+    # fused is the headline mode; the ring family runs too (not gated by the workload)
+    _sampled_allreduce(vrc, orc, w, MODES, m=1 << 20)
 
 
 def test_workload_all_gather_fp16_n8_heads(vrc, orc):
     w = workloads.WORKLOADS["all_gather_fp16_n8_heads"]
     xs = workloads.make_inputs(w, DEV)
     want = orc.ring_all_gather(host(xs), "fp16", outer=1)
-    for mode in ("ring", "fused"):
+    for mode in MODES:
         say(f"{w.name} {mode}")
         ys = vrc.vrc_all_gather(xs, dim=w.dim, mode=mode)
         torch.cuda.synchronize()
@@ -226,12 +230,12 @@ def test_workload_reduce_scatter_fp16_n8_act(vrc, orc):
     w = workloads.WORKLOADS["reduce_scatter_fp16_n8_act"]
     xs = workloads.make_inputs(w, DEV)
     hx = host(xs)
-    for mode in ("ring", "fused"):
+    for mode in MODES:
         say(f"{w.name} {mode}")
         ys = vrc.vrc_reduce_scatter(xs, dim=w.dim, mode=mode)
         torch.cuda.synchronize()
         assert tuple(ys[0].shape) == (8, 512)
-        want = (orc.ring_reduce_scatter(hx, "fp16", outer=8) if mode == "ring"
+        want = (orc.ring_reduce_scatter(hx, "fp16", outer=8) if mode in RING_FAMILY
                 else orc.fused_reduce_scatter(hx, "fp16", outer=8))
         for c, y in enumerate(host(ys)):
             assert_bitwise(y, want[c], f"{w.name} {mode} chunk {c}")
