@@ -50,11 +50,11 @@ def kernel_source_hash() -> str:
 
 
 def alg_bytes(mode: str, n: int, size_bytes: int) -> int:
-    """Bytes each mode must move per all-reduce.  Fused: read N inputs and
-    write N outputs.  Ring: N-1 reduce-scatter steps read two chunks and
-    write one per rank (3S per step), N-1 all-gather steps read and write one
-    chunk per rank (2S per step)."""
-    if mode == "fused":
+    """Bytes each mode must move per all-reduce.  Fused and ring-order: read
+    N inputs and write N outputs.  Ring and ring-chained: N-1 reduce-scatter
+    steps read two chunks and write one per rank (3S per step), N-1
+    all-gather steps read and write one chunk per rank (2S per step)."""
+    if mode in ("fused", "ring_order"):
         return 2 * n * size_bytes
     return 5 * (n - 1) * size_bytes
 
@@ -62,7 +62,8 @@ def alg_bytes(mode: str, n: int, size_bytes: int) -> int:
 def recorded_traffic(workload: str, mode: str):
     """Measured HBM bytes per launch from profiles/<kernel>.<workload>.counters.md,
     if those counters were taken on the current kernel sources."""
-    kernel = {"fused": "k_fused_allreduce", "ring": "k_ring_step"}[mode]
+    kernel = {"fused": "k_fused_allreduce", "ring": "k_ring_step", "ring_chained": "k_ring_chain_allreduce",
+              "ring_order": "k_ring_chain_allreduce"}[mode]
     path = os.path.join(PROFILES, f"{kernel}.{workload}.counters.md")
     if not os.path.exists(path):
         return None
@@ -117,15 +118,92 @@ def cpu_baseline(xs, w, mode: str):
     }
 
 
+def suite_bytes(w, mode: str) -> int:
+    """Algorithmic bytes per call for a workload's collective and mode."""
+    n, size = w.n, w.count * w.esize
+    fused_like = mode in ("fused", "ring_order")
+    if w.collective == "allreduce":
+        return 2 * n * size if fused_like else 5 * (n - 1) * size
+    if w.collective == "reduce_scatter":
+        return (n + 1) * size if fused_like else 3 * (n - 1) * size
+    return n * size + n * n * size if fused_like else 2 * n * n * size
+
+
+def run_suite(steps: int, torch, vrc, workloads) -> int:
+    """Every workload (and the fp16 sweep sizes) in every mode.  For
+    workloads whose buffers fit in 512 MiB, an untimed 1 GiB device write
+    before each timed call evicts the Infinity Cache (the result is labelled
+    "effective"); it also keeps the GPU busy while the host enqueues the
+    call, so the event interval holds GPU time only.  Larger workloads run
+    back to back.  One JSON line per case on stdout."""
+    dev = "cuda:0"
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cases = []
+    for w in workloads.WORKLOADS.values():
+        cases.append(w)
+        cases.extend(w.with_count(c) for c in w.sweep)
+    for w in cases:
+        xs = workloads.make_inputs(w, dev)
+        if w.collective == "allreduce":
+            outs = [torch.empty_like(x) for x in xs]
+        elif w.collective == "reduce_scatter":
+            outs = vrc.vrc_reduce_scatter(xs, dim=w.dim)
+        else:
+            outs = vrc.vrc_all_gather(xs, dim=w.dim)
+        torch.cuda.synchronize()
+        size = w.count * w.esize
+        footprint = {"allreduce": 2 * w.n * size, "reduce_scatter": (w.n + 1) * size,
+                     "all_gather": (w.n + w.n * w.n) * size}[w.collective]
+        cached = footprint <= (512 << 20)
+        for mode in vrc.MODES:
+            def call():
+                if w.collective == "allreduce":
+                    vrc.vrc_allreduce(xs, recv=outs, mode=mode)
+                elif w.collective == "reduce_scatter":
+                    vrc.vrc_reduce_scatter(xs, recv=outs, dim=w.dim, mode=mode)
+                else:
+                    vrc.vrc_all_gather(xs, recv=outs, dim=w.dim, mode=mode)
+            for _ in range(5):
+                call()
+            k = min(steps, 20) if w.count * w.esize >= (256 << 20) else steps
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+            for s0, s1 in evs:
+                if cached:
+                    flush.zero_()
+                s0.record()
+                call()
+                s1.record()
+            torch.cuda.synchronize()
+            ms = [s0.elapsed_time(s1) for s0, s1 in evs]
+            ms.sort()
+            med, p90 = ms[len(ms) // 2], ms[min(len(ms) - 1, int(0.9 * len(ms)))]
+            nb = suite_bytes(w, mode)
+            rec = {"workload": w.name, "collective": w.collective, "mode": mode, "dtype": w.dtype, "n_ranks": w.n,
+                   "elements_per_rank": w.count, "alg_bytes": nb, "calls": k, "us_median": round(med * 1e3, 2),
+                   "us_min": round(ms[0] * 1e3, 2), "us_p90": round(p90 * 1e3, 2),
+                   "GB_per_s": round(nb / (med * 1e-3) / 1e9, 1),
+                   "pct_of_peak": round(100 * nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                   "footprint_bytes": footprint,
+                   "label": "effective (footprint <= 512 MiB, cache flushed before each call)" if cached
+                   else "hbm"}
+            print(json.dumps(rec), flush=True)
+            log(f"{w.name:34s} {mode:13s} {rec['us_median']:10.1f} us  {rec['GB_per_s']:8.1f} GB/s")
+        del xs, outs
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the 8 x 512 MiB bf16 all-reduce)")
-    ap.add_argument("--mode", default="fused", choices=["fused", "ring"])
+    ap.add_argument("--mode", default="fused", choices=["fused", "ring", "ring_chained", "ring_order"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra ring-mode timing")
+    ap.add_argument("--suite", action="store_true",
+                    help="measure every workload in every mode (one JSON line each) instead of the headline")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB (known HBM traffic: 1 GiB read, 1 GiB "
                          "written per launch), for calibrating rocprofv3 byte counters")
@@ -145,6 +223,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr, flush=True)
         return 1
+    if args.suite:
+        return run_suite(args.steps, torch, vrc, workloads)
     if args.probe_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
         dst = torch.empty_like(src)
@@ -181,20 +261,22 @@ def main() -> int:
     extra = {"kernel_ms_avg": round(kavg, 5), "kernel_ms_min": round(min(kms), 5),
              "alg_bytes_per_step": nbytes, "kernel_source_sha256_16": kernel_source_hash()}
     if not args.no_extra:
-        other = "ring" if args.mode == "fused" else "fused"
+        for other in vrc.MODES:
+            if other == args.mode:
+                continue
 
-        def step_other():
-            vrc.vrc_allreduce(xs, recv=ys, mode=other)
+            def step_other(other=other):
+                vrc.vrc_allreduce(xs, recv=ys, mode=other)
 
-        k2 = max(3, min(args.steps, 10))
-        wall2, kms2 = time_calls(step_other, k2, 2, torch)
-        nb2 = alg_bytes(other, w.n, size)
-        extra[f"{other}_mode"] = {
-            "steps": k2, "ms_per_step": round(wall2 * 1e3 / k2, 5),
-            "GB_per_s": round(nb2 / (wall2 / k2) / 1e9, 2), "alg_bytes_per_step": nb2,
-            "launches_per_step": 2 * (w.n - 1) if other == "ring" else 1,
-        }
-        log(f"{other} mode: {extra[f'{other}_mode']}")
+            k2 = max(3, min(args.steps, 10))
+            wall2, kms2 = time_calls(step_other, k2, 2, torch)
+            nb2 = alg_bytes(other, w.n, size)
+            extra[f"{other}_mode"] = {
+                "steps": k2, "ms_per_step": round(wall2 * 1e3 / k2, 5),
+                "GB_per_s": round(nb2 / (wall2 / k2) / 1e9, 2), "alg_bytes_per_step": nb2,
+                "launches_per_step": 2 * (w.n - 1) if other == "ring" else 1,
+            }
+            log(f"{other} mode: {extra[f'{other}_mode']}")
 
     cpu = None
     if not args.no_cpu_baseline:
