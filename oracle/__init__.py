@@ -28,7 +28,7 @@ DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
 NP_DTYPES = {"int32": np.int32, "fp32": np.float32, "fp16": np.float16, "bf16": np.uint16}
 
 OK, E_ARG, E_NOMEM, E_EMPTY, E_TAG, E_LEFTOVER = range(6)
-PHASE_RS, PHASE_AG = 0, 1
+PHASE_RS, PHASE_AG, PHASE_HD_RS, PHASE_HD_AG = 0, 1, 2, 3
 FAULT_NONE, FAULT_DROP, FAULT_DUP, FAULT_MISROUTE, FAULT_WRONG_CHUNK = range(5)
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra"]
@@ -51,7 +51,7 @@ class OracleError(RuntimeError):
 
 class _MsgRec(C.Structure):
     _fields_ = [("phase", C.c_int), ("step", C.c_int), ("src", C.c_int), ("dst", C.c_int),
-                ("chunk", C.c_int), ("elems", C.c_uint64)]
+                ("chunk", C.c_int), ("elems", C.c_uint64), ("chunk_hi", C.c_int)]
 
 
 class _Trace(C.Structure):
@@ -66,7 +66,7 @@ class _Fault(C.Structure):
 @dataclass
 class Trace:
     """What the simulated transport saw: one record per posted message."""
-    messages: list = field(default_factory=list)  # (phase, step, src, dst, chunk, elems)
+    messages: list = field(default_factory=list)  # (phase, step, src, dst, chunk, elems, chunk_hi)
     sent_elems: list = field(default_factory=list)
     recv_elems: list = field(default_factory=list)
 
@@ -102,6 +102,10 @@ class Oracle:
                                               C.POINTER(_Fault)]
         L.orc_ring_all_gather.argtypes = [i, i, u64, u64, vp, vp, C.POINTER(_Trace),
                                           C.POINTER(_Fault)]
+        L.orc_hd_allreduce_steps.argtypes = [i, i, u64, vp, vp, i, i, C.POINTER(_Trace), C.POINTER(_Fault)]
+        L.orc_hd_reduce_scatter.argtypes = [i, i, u64, u64, vp, vp, C.POINTER(_Trace), C.POINTER(_Fault)]
+        L.orc_hd_all_gather.argtypes = [i, i, u64, u64, vp, vp, C.POINTER(_Trace), C.POINTER(_Fault)]
+        L.orc_hd_allreduce_at.argtypes = [i, i, u64, vp, vp, u64, vp]
         L.orc_fused_allreduce.argtypes = [i, i, u64, vp, vp]
         L.orc_fused_reduce_scatter.argtypes = [i, i, u64, u64, vp, vp]
         L.orc_ring_allreduce_at.argtypes = [i, i, u64, vp, vp, u64, vp]
@@ -143,7 +147,7 @@ class Oracle:
         t = Trace()
         for k in range(min(tr.log_len, tr.log_cap)):
             r = log[k]
-            t.messages.append((r.phase, r.step, r.src, r.dst, r.chunk, int(r.elems)))
+            t.messages.append((r.phase, r.step, r.src, r.dst, r.chunk, int(r.elems), r.chunk_hi))
         t.sent_elems = [int(sent[r]) for r in range(n)]
         t.recv_elems = [int(recv[r]) for r in range(n)]
         return t
@@ -194,6 +198,56 @@ class Oracle:
         if rc:
             raise OracleError("ring_all_gather", rc)
         return (ys, self._read_trace(tr, keep, n)) if trace else ys
+
+    # -- halving-doubling ------------------------------------------------------
+    def hd_allreduce(self, xs, dtype, rs_steps=-1, ag_steps=-1, trace=False, fault=None):
+        xs = self._check_inputs(xs, dtype)
+        n, count = len(xs), xs[0].size
+        ys = [np.empty_like(x) for x in xs]
+        tr = keep = None
+        if trace:
+            tr, keep = self._make_trace(n, 2 * n * 8 + 8)
+        rc = self._L.orc_hd_allreduce_steps(DTYPES[dtype], n, count, _ptrs(xs), _ptrs(ys), rs_steps, ag_steps,
+                                            C.byref(tr) if trace else None, self._fault(fault))
+        if rc:
+            raise OracleError("hd_allreduce", rc)
+        return (ys, self._read_trace(tr, keep, n)) if trace else ys
+
+    def hd_reduce_scatter(self, xs, dtype, outer=1, trace=False, fault=None):
+        xs = self._check_inputs(xs, dtype)
+        n, count = len(xs), xs[0].size
+        ys = [np.empty(self.rs_len(count, n, outer, c), dtype=xs[0].dtype) for c in range(n)]
+        tr = keep = None
+        if trace:
+            tr, keep = self._make_trace(n, n * 8 + 8)
+        rc = self._L.orc_hd_reduce_scatter(DTYPES[dtype], n, count, outer, _ptrs(xs), _ptrs(ys),
+                                           C.byref(tr) if trace else None, self._fault(fault))
+        if rc:
+            raise OracleError("hd_reduce_scatter", rc)
+        return (ys, self._read_trace(tr, keep, n)) if trace else ys
+
+    def hd_all_gather(self, xs, dtype, outer=1, trace=False, fault=None):
+        xs = self._check_inputs(xs, dtype)
+        n, count = len(xs), xs[0].size
+        ys = [np.empty(n * count, dtype=xs[0].dtype) for _ in range(n)]
+        tr = keep = None
+        if trace:
+            tr, keep = self._make_trace(n, n * 8 + 8)
+        rc = self._L.orc_hd_all_gather(DTYPES[dtype], n, count, outer, _ptrs(xs), _ptrs(ys),
+                                       C.byref(tr) if trace else None, self._fault(fault))
+        if rc:
+            raise OracleError("hd_all_gather", rc)
+        return (ys, self._read_trace(tr, keep, n)) if trace else ys
+
+    def hd_allreduce_at(self, xs, dtype, idx):
+        xs = self._check_inputs(xs, dtype)
+        idx = np.ascontiguousarray(idx, dtype=np.uint64)
+        out = np.empty(idx.size, dtype=xs[0].dtype)
+        rc = self._L.orc_hd_allreduce_at(DTYPES[dtype], len(xs), xs[0].size, _ptrs(xs), idx.ctypes.data,
+                                         idx.size, out.ctypes.data)
+        if rc:
+            raise OracleError("hd_allreduce_at", rc)
+        return out
 
     # -- fused (naive) reductions ---------------------------------------------
     def fused_allreduce(self, xs, dtype):

@@ -28,6 +28,17 @@
  *  [NAIVE] hwcomputing.csdn.net/6a0dc11a10ee7a33f273f7fd.html, section "为什么
  *         大模型训练离不开通信": the naive all-reduce, where one collector adds
  *         every contribution and hands the sum back to all ranks.
+ *  [HD]   ai6s.net/6a0dd5b5662f9a54cb75ef90.html, section "TP 通信": on fully
+ *         connected NPUs the all-reduce uses halving-doubling, finishing in a
+ *         logarithmic number of steps.  The pages give no further detail; the
+ *         oracle follows the textbook algorithm (recursive halving
+ *         reduce-scatter, then recursive doubling all-gather, for N a power of
+ *         two; Thakur, Rabenseifner and Gropp, "Optimization of Collective
+ *         Communication Operations in MPICH", IJHPCA 19(1), 2005): at the step
+ *         with distance d (N/2, N/4, ..., 1) rank r exchanges with r XOR d,
+ *         keeps the half of its current block range that holds block r and
+ *         adds the partner's copy of that half; the all-gather then doubles
+ *         the owned range with distances 1, 2, ..., N/2.
  *
  * Readings taken where the pages are silent or garbled:
  *  - The listing adds into the chunk it sends; the walkthrough says a card
@@ -63,7 +74,7 @@ enum {
     ORC_E_LEFTOVER = 5  /* messages left undelivered at the end */
 };
 
-enum { ORC_PHASE_RS = 0, ORC_PHASE_AG = 1 };
+enum { ORC_PHASE_RS = 0, ORC_PHASE_AG = 1, ORC_PHASE_HD_RS = 2, ORC_PHASE_HD_AG = 3 };
 
 /* Test hook: plant one fault into the simulated transport. */
 enum {
@@ -81,10 +92,12 @@ typedef struct {
     int rank; /* sending rank */
 } orc_fault;
 
-/* One record per posted message, for schedule checks. */
+/* One record per posted message, for schedule checks.  A message carries
+ * the blocks [chunk, chunk_hi). */
 typedef struct {
     int phase, step, src, dst, chunk;
     uint64_t elems;
+    int chunk_hi;
 } orc_msg_rec;
 
 typedef struct {
@@ -309,7 +322,7 @@ static int mod(int a, int n) { return ((a % n) + n) % n; }
 /* ------------------------------------------------------------------ */
 
 typedef struct msg {
-    int src, phase, step, chunk;
+    int src, phase, step, chunk, chunk_hi;
     uint64_t elems;
     unsigned char* payload;
     struct msg* next;
@@ -371,6 +384,7 @@ static msg* msg_make(const net* nt, int src, int phase, int step, int chunk,
     m->phase = phase;
     m->step = step;
     m->chunk = chunk;
+    m->chunk_hi = chunk + 1;
     m->elems = elems;
     for (uint64_t k = 0; k < elems; k++) {
         uint64_t at;
@@ -385,11 +399,10 @@ static msg* msg_make(const net* nt, int src, int phase, int step, int chunk,
     return m;
 }
 
-/* Post a message from `src` to its ring successor, applying a planted
- * fault if one matches. */
-static int post(net* nt, msg* m)
+/* Post a message to rank `dst`, applying a planted fault if one matches
+ * (a misrouted message goes to dst+1). */
+static int post_to(net* nt, msg* m, int dst)
 {
-    int dst = mod(m->src + 1, nt->n);
     const orc_fault* f = nt->fault;
     int hit = f && f->kind != ORC_FAULT_NONE && f->phase == m->phase &&
               f->step == m->step && f->rank == m->src;
@@ -397,7 +410,7 @@ static int post(net* nt, msg* m)
         msg_free(m);
         return ORC_OK;
     }
-    if (hit && f->kind == ORC_FAULT_MISROUTE) dst = mod(m->src + 2, nt->n);
+    if (hit && f->kind == ORC_FAULT_MISROUTE) dst = mod(dst + 1, nt->n);
 
     if (nt->trace) {
         orc_trace* t = nt->trace;
@@ -408,6 +421,7 @@ static int post(net* nt, msg* m)
             r->src = m->src;
             r->dst = dst;
             r->chunk = m->chunk;
+            r->chunk_hi = m->chunk_hi;
             r->elems = m->elems;
         }
         t->log_len++;
@@ -430,6 +444,9 @@ static int post(net* nt, msg* m)
     }
     return ORC_OK;
 }
+
+/* Post a message from `src` to its ring successor. */
+static int post(net* nt, msg* m) { return post_to(nt, m, mod(m->src + 1, nt->n)); }
 
 /* Receive the next message of rank r and check its tag. */
 static int receive(net* nt, int r, int phase, int step, int want_chunk, msg** out)
@@ -820,6 +837,315 @@ int orc_fused_allreduce_at(int dt, int n, uint64_t count, const void* const* x, 
         acc_set(dt, &acc, (const unsigned char*)x[0] + i * esz);
         for (int r = 1; r < n; r++) acc_add(dt, &acc, (const unsigned char*)x[r] + i * esz);
         acc_store(dt, &acc, (unsigned char*)out + k * esz);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Halving-doubling [HD]                                               */
+/* ------------------------------------------------------------------ */
+
+static int is_pow2(int n) { return n >= 1 && (n & (n - 1)) == 0; }
+
+/* Elements in the block range [lo, hi). */
+static uint64_t range_len(const geom* g, int lo, int hi)
+{
+    uint64_t total = 0;
+    for (int b = lo; b < hi; b++) total += chunk_len(g, b);
+    return total;
+}
+
+/* Flat index of the k-th element of the block range [lo, hi), taking the
+ * blocks in order and each block's elements in order. */
+static uint64_t range_elem(const geom* g, int lo, int hi, uint64_t k)
+{
+    for (int b = lo; b < hi; b++) {
+        uint64_t len = chunk_len(g, b);
+        if (k < len) return chunk_elem(g, b, k);
+        k -= len;
+    }
+    return 0; /* not reached for k < range_len */
+}
+
+/* Flat index, in an [outer, n*row] all-gather output, of the k-th element
+ * of the slab range [lo, hi) (row by row, slab by slab). */
+static uint64_t slab_range_elem(const geom* g, int lo, int hi, uint64_t k)
+{
+    uint64_t width = (uint64_t)(hi - lo) * g->row;
+    uint64_t o = k / width, rem = k % width;
+    uint64_t q = (uint64_t)lo + rem / g->row, j = rem % g->row;
+    return o * g->row * (uint64_t)g->n + q * g->row + j;
+}
+
+static msg* range_msg(const net* nt, int src, int phase, int step, int lo, int hi, const unsigned char* buf,
+                      const geom* g, int slabs)
+{
+    uint64_t elems = slabs ? (uint64_t)(hi - lo) * g->count : range_len(g, lo, hi);
+    msg* m = (msg*)calloc(1, sizeof(msg));
+    if (!m) return NULL;
+    m->payload = (unsigned char*)malloc(elems ? elems * nt->esz : 1);
+    if (!m->payload) {
+        free(m);
+        return NULL;
+    }
+    m->src = src;
+    m->phase = phase;
+    m->step = step;
+    m->chunk = lo;
+    m->chunk_hi = hi;
+    m->elems = elems;
+    for (uint64_t k = 0; k < elems; k++) {
+        uint64_t at = slabs ? slab_range_elem(g, lo, hi, k) : range_elem(g, lo, hi, k);
+        memcpy(m->payload + k * nt->esz, buf + at * nt->esz, nt->esz);
+    }
+    return m;
+}
+
+/* Receive rank r's next message and check it came from `src` with the
+ * expected phase, step and block range. */
+static int receive_range(net* nt, int r, int src, int phase, int step, int lo, int hi, msg** out)
+{
+    msg* m = inbox_pop(&nt->boxes[r]);
+    *out = NULL;
+    if (!m) return ORC_E_EMPTY;
+    if (m->src != src || m->phase != phase || m->step != step || m->chunk != lo || m->chunk_hi != hi) {
+        msg_free(m);
+        return ORC_E_TAG;
+    }
+    *out = m;
+    return ORC_OK;
+}
+
+/* Recursive halving.  lo[r], hi[r]: rank r's current block range (start
+ * [0, N)).  At the step with distance d the range is split in two; the rank
+ * whose bit d is clear keeps the lower half, its partner r XOR d the upper
+ * half; each sends the other half to the partner and adds the half it
+ * receives into its own copy.  After log2 N steps rank r holds block r. */
+static int phase_halving(net* nt, unsigned char** buf, const geom* g, int* lo, int* hi, int steps)
+{
+    int n = nt->n, step = 0;
+    for (int d = n / 2; d >= 1 && step < steps; d /= 2, step++) {
+        for (int r = 0; r < n; r++) {
+            int mid = (lo[r] + hi[r]) / 2;
+            int upper = (r & d) != 0;
+            int give_lo = upper ? lo[r] : mid, give_hi = upper ? mid : hi[r];
+            const orc_fault* f = nt->fault;
+            if (f && f->kind == ORC_FAULT_WRONG_CHUNK && f->phase == ORC_PHASE_HD_RS && f->step == step &&
+                f->rank == r) {
+                give_lo = upper ? mid : lo[r];
+                give_hi = upper ? hi[r] : mid;
+            }
+            msg* m = range_msg(nt, r, ORC_PHASE_HD_RS, step, give_lo, give_hi, buf[r], g, 0);
+            if (!m) return ORC_E_NOMEM;
+            int rc = post_to(nt, m, r ^ d);
+            if (rc) return rc;
+        }
+        for (int r = 0; r < n; r++) {
+            int mid = (lo[r] + hi[r]) / 2;
+            int upper = (r & d) != 0;
+            int keep_lo = upper ? mid : lo[r], keep_hi = upper ? hi[r] : mid;
+            msg* m;
+            int rc = receive_range(nt, r, r ^ d, ORC_PHASE_HD_RS, step, keep_lo, keep_hi, &m);
+            if (rc) return rc;
+            for (uint64_t k = 0; k < m->elems; k++) {
+                unsigned char* mine = buf[r] + range_elem(g, keep_lo, keep_hi, k) * nt->esz;
+                elem_add(nt->dt, mine, m->payload + k * nt->esz, mine);
+            }
+            msg_free(m);
+            lo[r] = keep_lo;
+            hi[r] = keep_hi;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Recursive doubling.  At the step with distance d (1, 2, ..., N/2) rank r
+ * sends its whole current range to r XOR d and copies the partner's range
+ * into its own buffer; the two ranges are adjacent and merge.  `slabs`
+ * selects all-gather slabs of an [outer, N*row] buffer instead of blocks. */
+static int phase_doubling(net* nt, unsigned char** buf, const geom* g, int* lo, int* hi, int steps, int slabs)
+{
+    int n = nt->n, step = 0;
+    int plo[64], phi[64];
+    for (int d = 1; d < n && step < steps; d *= 2, step++) {
+        for (int r = 0; r < n; r++) {
+            int give_lo = lo[r], give_hi = hi[r];
+            const orc_fault* f = nt->fault;
+            if (f && f->kind == ORC_FAULT_WRONG_CHUNK && f->phase == ORC_PHASE_HD_AG && f->step == step &&
+                f->rank == r) {
+                give_lo = lo[r ^ d];
+                give_hi = hi[r ^ d];
+            }
+            msg* m = range_msg(nt, r, ORC_PHASE_HD_AG, step, give_lo, give_hi, buf[r], g, slabs);
+            if (!m) return ORC_E_NOMEM;
+            int rc = post_to(nt, m, r ^ d);
+            if (rc) return rc;
+        }
+        for (int r = 0; r < n; r++) {
+            plo[r] = lo[r];
+            phi[r] = hi[r];
+        }
+        for (int r = 0; r < n; r++) {
+            int p = r ^ d;
+            msg* m;
+            int rc = receive_range(nt, r, p, ORC_PHASE_HD_AG, step, plo[p], phi[p], &m);
+            if (rc) return rc;
+            for (uint64_t k = 0; k < m->elems; k++) {
+                uint64_t at = slabs ? slab_range_elem(g, plo[p], phi[p], k) : range_elem(g, plo[p], phi[p], k);
+                memcpy(buf[r] + at * nt->esz, m->payload + k * nt->esz, nt->esz);
+            }
+            msg_free(m);
+            lo[r] = plo[r] < plo[p] ? plo[r] : plo[p];
+            hi[r] = phi[r] > phi[p] ? phi[r] : phi[p];
+        }
+    }
+    return ORC_OK;
+}
+
+static int log2i(int n)
+{
+    int k = 0;
+    while ((1 << k) < n) k++;
+    return k;
+}
+
+/* Halving-doubling all-reduce (N a power of two, at most 64).  rs_steps /
+ * ag_steps < 0 mean log2 N; smaller values stop early so tests can inspect
+ * the intermediate rank buffers. */
+int orc_hd_allreduce_steps(int dt, int n, uint64_t count, const void* const* x, void* const* y, int rs_steps,
+                           int ag_steps, orc_trace* trace, const orc_fault* fault)
+{
+    int rc = check_dtype_n(dt, n);
+    if (rc) return rc;
+    if (!is_pow2(n) || n > 64) return ORC_E_ARG;
+    int k = log2i(n);
+    if (rs_steps < 0) rs_steps = k;
+    if (ag_steps < 0) ag_steps = k;
+    if (rs_steps > k || ag_steps > k) return ORC_E_ARG;
+    geom g = {count, 1, count, n};
+    size_t esz = elem_size(dt);
+    unsigned char** buf = rank_state_new(n, count, esz);
+    if (!buf) return ORC_E_NOMEM;
+    for (int r = 0; r < n; r++) memcpy(buf[r], x[r], count * esz);
+    net* nt = net_new(dt, n, trace, fault);
+    if (!nt) {
+        rank_state_free(buf, n);
+        return ORC_E_NOMEM;
+    }
+    int lo[64], hi[64];
+    for (int r = 0; r < n; r++) {
+        lo[r] = 0;
+        hi[r] = n;
+    }
+    rc = phase_halving(nt, buf, &g, lo, hi, rs_steps);
+    if (!rc && rs_steps == k) rc = phase_doubling(nt, buf, &g, lo, hi, ag_steps, 0);
+    if (!rc) rc = drain_check(nt);
+    if (!rc)
+        for (int r = 0; r < n; r++) memcpy(y[r], buf[r], count * esz);
+    net_free(nt);
+    rank_state_free(buf, n);
+    return rc;
+}
+
+/* Halving-doubling reduce-scatter: recursive halving, after which rank c
+ * holds block c, delivered unchanged as output c. */
+int orc_hd_reduce_scatter(int dt, int n, uint64_t count, uint64_t outer, const void* const* x, void* const* y,
+                          orc_trace* trace, const orc_fault* fault)
+{
+    int rc = check_dtype_n(dt, n);
+    if (rc) return rc;
+    if (!is_pow2(n) || n > 64) return ORC_E_ARG;
+    if (outer == 0 || count % outer != 0) return ORC_E_ARG;
+    geom g = {count, outer, count / outer, n};
+    if (outer > 1 && g.row % (uint64_t)n != 0) return ORC_E_ARG;
+    size_t esz = elem_size(dt);
+    unsigned char** buf = rank_state_new(n, count, esz);
+    if (!buf) return ORC_E_NOMEM;
+    for (int r = 0; r < n; r++) memcpy(buf[r], x[r], count * esz);
+    net* nt = net_new(dt, n, trace, fault);
+    if (!nt) {
+        rank_state_free(buf, n);
+        return ORC_E_NOMEM;
+    }
+    int lo[64], hi[64];
+    for (int r = 0; r < n; r++) {
+        lo[r] = 0;
+        hi[r] = n;
+    }
+    rc = phase_halving(nt, buf, &g, lo, hi, log2i(n));
+    if (!rc) rc = drain_check(nt);
+    if (!rc) {
+        for (int c = 0; c < n; c++) {
+            if (lo[c] != c || hi[c] != c + 1) {
+                rc = ORC_E_TAG;
+                break;
+            }
+            unsigned char* out = (unsigned char*)y[c];
+            for (uint64_t k = 0; k < chunk_len(&g, c); k++)
+                memcpy(out + k * esz, buf[c] + chunk_elem(&g, c, k) * esz, esz);
+        }
+    }
+    net_free(nt);
+    rank_state_free(buf, n);
+    return rc;
+}
+
+/* Halving-doubling all-gather: recursive doubling over the slabs of the
+ * [outer, N*row] outputs, starting from each rank's own slab. */
+int orc_hd_all_gather(int dt, int n, uint64_t count, uint64_t outer, const void* const* x, void* const* y,
+                      orc_trace* trace, const orc_fault* fault)
+{
+    int rc = check_dtype_n(dt, n);
+    if (rc) return rc;
+    if (!is_pow2(n) || n > 64) return ORC_E_ARG;
+    if (outer == 0 || count % outer != 0) return ORC_E_ARG;
+    geom g = {count, outer, count / outer, n};
+    size_t esz = elem_size(dt);
+    uint64_t out_elems = count * (uint64_t)n;
+    unsigned char** buf = rank_state_new(n, out_elems, esz);
+    if (!buf) return ORC_E_NOMEM;
+    int lo[64], hi[64];
+    for (int r = 0; r < n; r++) {
+        memset(buf[r], 0, out_elems * esz);
+        for (uint64_t k = 0; k < count; k++)
+            memcpy(buf[r] + slab_range_elem(&g, r, r + 1, k) * esz, (const unsigned char*)x[r] + k * esz, esz);
+        lo[r] = r;
+        hi[r] = r + 1;
+    }
+    net* nt = net_new(dt, n, trace, fault);
+    if (!nt) {
+        rank_state_free(buf, n);
+        return ORC_E_NOMEM;
+    }
+    rc = phase_doubling(nt, buf, &g, lo, hi, log2i(n), 1);
+    if (!rc) rc = drain_check(nt);
+    if (!rc)
+        for (int r = 0; r < n; r++) memcpy(y[r], buf[r], out_elems * esz);
+    net_free(nt);
+    rank_state_free(buf, n);
+    return rc;
+}
+
+/* Halving-doubling result at flat index idx[k].  Every rank and every block
+ * gets the same butterfly: pairs at distance N/2 first, then pairs of pairs
+ * at distance N/4, and so on, each partial rounded to the storage type:
+ * v[r] = x_r[i]; for d = N/2 .. 1: v[r] = v[r] (+) v[r + d] for r < d;
+ * the result is v[0]. */
+int orc_hd_allreduce_at(int dt, int n, uint64_t count, const void* const* x, const uint64_t* idx, uint64_t m,
+                        void* out)
+{
+    int rc = check_dtype_n(dt, n);
+    if (rc) return rc;
+    if (!is_pow2(n) || n > 64) return ORC_E_ARG;
+    size_t esz = elem_size(dt);
+    unsigned char v[64 * 8];
+    for (uint64_t k = 0; k < m; k++) {
+        uint64_t i = idx[k];
+        if (i >= count) return ORC_E_ARG;
+        for (int r = 0; r < n; r++) memcpy(v + r * esz, (const unsigned char*)x[r] + i * esz, esz);
+        for (int d = n / 2; d >= 1; d /= 2)
+            for (int r = 0; r < d; r++) elem_add(dt, v + r * esz, v + r * esz, v + (r + d) * esz);
+        memcpy((unsigned char*)out + k * esz, v, esz);
     }
     return ORC_OK;
 }

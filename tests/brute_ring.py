@@ -168,3 +168,64 @@ def fused_reduce_scatter(xs: list[np.ndarray], dtype: str, outer: int = 1) -> li
     blks = blocks(count, n) if outer == 1 else column_blocks(count, n, outer)
     full = fused_fold(xs, dtype)
     return [full[_block_index(blks[c])].copy() for c in range(n)]
+
+
+# ---------------------------------------------------------------------------
+# Halving-doubling, written recursively (divide and conquer over rank
+# groups) rather than with the oracle's XOR partners: a group of 2m ranks
+# sharing a block range splits it in two; the lower m ranks keep the lower
+# half, the upper m ranks the upper half; lower rank k pairs with upper
+# rank k and each adds the partner's copy of the half it keeps; then each
+# half-group recurses on its half.  The all-gather undoes the recursion:
+# each half-group first completes its half, then partners swap halves.
+# ---------------------------------------------------------------------------
+def _hd_rs(state, dtype, ranks, lo, hi, blks):
+    if len(ranks) == 1:
+        return
+    m = len(ranks) // 2
+    mid = (lo + hi) // 2
+    lower, upper = ranks[:m], ranks[m:]
+    lo_ix = np.concatenate([_block_index(blks[b]) for b in range(lo, mid)]) if mid > lo else np.zeros(0, np.int64)
+    hi_ix = np.concatenate([_block_index(blks[b]) for b in range(mid, hi)]) if hi > mid else np.zeros(0, np.int64)
+    sent = {}
+    for a, b in zip(lower, upper):
+        sent[(b, a)] = state[b][lo_ix].copy()  # upper sends the lower half to lower
+        sent[(a, b)] = state[a][hi_ix].copy()  # lower sends the upper half to upper
+    for a, b in zip(lower, upper):
+        state[a][lo_ix] = storage_add(state[a][lo_ix], sent[(b, a)], dtype)
+        state[b][hi_ix] = storage_add(state[b][hi_ix], sent[(a, b)], dtype)
+    _hd_rs(state, dtype, lower, lo, mid, blks)
+    _hd_rs(state, dtype, upper, mid, hi, blks)
+
+
+def _hd_ag(state, ranks, lo, hi, blks):
+    if len(ranks) == 1:
+        return
+    m = len(ranks) // 2
+    mid = (lo + hi) // 2
+    lower, upper = ranks[:m], ranks[m:]
+    _hd_ag(state, lower, lo, mid, blks)
+    _hd_ag(state, upper, mid, hi, blks)
+    lo_ix = np.concatenate([_block_index(blks[b]) for b in range(lo, mid)]) if mid > lo else np.zeros(0, np.int64)
+    hi_ix = np.concatenate([_block_index(blks[b]) for b in range(mid, hi)]) if hi > mid else np.zeros(0, np.int64)
+    for a, b in zip(lower, upper):
+        state[b][lo_ix] = state[a][lo_ix]
+        state[a][hi_ix] = state[b][hi_ix]
+
+
+def hd_allreduce(xs, dtype):
+    n = len(xs)
+    blks = blocks(xs[0].size, n)
+    state = [x.copy() for x in xs]
+    _hd_rs(state, dtype, list(range(n)), 0, n, blks)
+    _hd_ag(state, list(range(n)), 0, n, blks)
+    return state
+
+
+def hd_reduce_scatter(xs, dtype, outer=1):
+    n = len(xs)
+    count = xs[0].size
+    blks = blocks(count, n) if outer == 1 else column_blocks(count, n, outer)
+    state = [x.copy() for x in xs]
+    _hd_rs(state, dtype, list(range(n)), 0, n, blks)
+    return [state[c][_block_index(blks[c])].copy() for c in range(n)]

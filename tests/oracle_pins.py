@@ -482,4 +482,166 @@ def pin_fault_detection(orc):
                 raise AssertionError(f"fault {kind} not detected")
 
 
+
+
+# ---------------------------------------------------------------------------
+# halving-doubling (recursive halving reduce-scatter + recursive doubling
+# all-gather), pinned the same way: hand-derived N = 4 fixtures, integer
+# sums, the traffic formula, an independent recursive brute force, the
+# pairwise-summation error bound and fault detection
+# ---------------------------------------------------------------------------
+def pin_hd_schedule_golden_n4(orc):
+    want = []
+    for row in _read_rows("hd_n4_schedule.txt"):
+        ph, s, src, dst, lo, hi = row.split()
+        want.append((orc_mod.PHASE_HD_RS if ph == "rs" else orc_mod.PHASE_HD_AG, int(s), int(src), int(dst),
+                     int(lo), int(hi)))
+    xs = [np.arange(12, dtype=np.int32) for _ in range(4)]
+    _, tr = orc.hd_allreduce(xs, "int32", trace=True)
+    got = [(m[0], m[1], m[2], m[3], m[4], m[6]) for m in tr.messages]
+    assert sorted(got) == sorted(want), f"hd schedule differs:\n{got}\nvs\n{want}"
+
+
+def pin_hd_contributors_golden_n4(orc):
+    table = {}
+    for row in _read_rows("hd_n4_contributors.txt"):
+        s, r, *masks = (int(v) for v in row.split())
+        table[(s, r)] = masks
+    xs = [np.full(8, 1 << r, dtype=np.int32) for r in range(4)]
+    for s in range(-1, 2):
+        ys = orc.hd_allreduce(xs, "int32", rs_steps=s + 1, ag_steps=0)
+        for r in range(4):
+            got = [int(ys[r][2 * c]) for c in range(4)]
+            assert got == table[(s, r)] and [int(ys[r][2 * c + 1]) for c in range(4)] == got, (s, r, got)
+
+
+def pin_hd_order_golden_n4(orc):
+    for row in _read_rows("hd_n4_order.txt"):
+        head, out_s = (p.strip() for p in row.split("|"))
+        dtype, *vs = head.split()
+        v = [float(t) for t in vs]
+        want = np.array([float(t) for t in out_s.split()], dtype=np.float64)
+        xs = [brute.narrow(np.full(want.size, v[r], dtype=np.float32), dtype) for r in range(4)]
+        for ys in (orc.hd_allreduce(xs, dtype),):
+            for r in range(4):
+                assert np.array_equal(_to_f64(ys[r], dtype), want), (dtype, r)
+
+
+def pin_hd_integer_equals_naive_sum(orc):
+    rng = np.random.default_rng(31)
+    for n in (1, 2, 4, 8, 16):
+        for count in (0, 1, n - 1, n, 3 * n + 5, 4099):
+            xs = _ranks(rng, "int32", n, count)
+            want = brute.narrow(np.sum([x.astype(np.int64) for x in xs], axis=0), "int32") if count else \
+                np.zeros(0, np.int32)
+            for r, y in enumerate(orc.hd_allreduce(xs, "int32")):
+                _same_bits(y, want, f"hd int32 n={n} count={count} rank {r}")
+
+
+def pin_hd_all_ranks_identical_and_traffic(orc):
+    rng = np.random.default_rng(32)
+    for dtype in DTYPES:
+        for n in (2, 4, 8, 16):
+            for count in (n, 8 * n, 8 * n + 3):
+                xs = _ranks(rng, dtype, n, count)
+                ys, tr = orc.hd_allreduce(xs, dtype, trace=True)
+                for r in range(1, n):
+                    _same_bits(ys[r], ys[0], f"hd {dtype} n={n} rank {r}")
+                assert sum(tr.sent_elems) == 2 * (n - 1) * count, (n, count)
+                if count % n == 0:
+                    assert all(s == 2 * (n - 1) * count // n for s in tr.sent_elems), (n, count)
+                k = n.bit_length() - 1
+                assert len(tr.messages) == 2 * k * n
+
+
+def pin_hd_brute_force(orc):
+    rng = np.random.default_rng(33)
+    for dtype in DTYPES:
+        for n in (1, 2, 4, 8):
+            for count in range(0, 3 * n + 3, max(1, n // 2)):
+                xs = _ranks(rng, dtype, n, count)
+                want = brute.hd_allreduce(xs, dtype)
+                got = orc.hd_allreduce(xs, dtype)
+                for r in range(n):
+                    _same_bits(got[r], want[r], f"hd {dtype} n={n} count={count} rank {r}")
+                rs = orc.hd_reduce_scatter(xs, dtype)
+                want_rs = brute.hd_reduce_scatter(xs, dtype)
+                for c in range(n):
+                    _same_bits(rs[c], want_rs[c], f"hd rs {dtype} n={n} count={count} chunk {c}")
+        for n, outer, w in ((2, 3, 2), (4, 2, 3), (8, 2, 2)):
+            xs = _ranks(rng, dtype, n, outer * n * w)
+            rs = orc.hd_reduce_scatter(xs, dtype, outer=outer)
+            want = brute.hd_reduce_scatter(xs, dtype, outer=outer)
+            for c in range(n):
+                _same_bits(rs[c], want[c], f"hd rs {dtype} n={n} outer={outer} chunk {c}")
+
+
+def pin_hd_all_gather_and_composition(orc):
+    rng = np.random.default_rng(34)
+    for dtype in DTYPES:
+        for n, outer, row in ((1, 1, 5), (2, 1, 7), (4, 3, 5), (8, 2, 16), (16, 1, 3)):
+            xs = _ranks(rng, dtype, n, outer * row)
+            want = np.concatenate([x.reshape(outer, row) for x in xs], axis=1).reshape(-1)
+            for r, y in enumerate(orc.hd_all_gather(xs, dtype, outer=outer)):
+                _same_bits(y, want, f"hd ag {dtype} n={n} rank {r}")
+        for n in (2, 4, 8):
+            xs = _ranks(rng, dtype, n, 8 * n)
+            ar = orc.hd_allreduce(xs, dtype)
+            ag = orc.hd_all_gather(orc.hd_reduce_scatter(xs, dtype), dtype)
+            for r in range(n):
+                _same_bits(ag[r], ar[r], f"hd AG(RS) {dtype} n={n} rank {r}")
+
+
+def pin_hd_closed_form_matches_simulation(orc):
+    rng = np.random.default_rng(35)
+    for dtype in DTYPES:
+        for n, count in ((1, 5), (2, 9), (4, 4099), (8, 1000), (16, 77)):
+            xs = _ranks(rng, dtype, n, count)
+            idx = np.arange(count, dtype=np.uint64)
+            _same_bits(orc.hd_allreduce_at(xs, dtype, idx), orc.hd_allreduce(xs, dtype)[0],
+                       f"hd_at {dtype} n={n} count={count}")
+
+
+def pin_hd_error_bound(orc):
+    """Pairwise summation (Higham eq. 4.6) with each partial rounded to the
+    storage type: |y - s| <= gamma_{log2 N}(u_s) * sum|x|, on same-sign data
+    in [1, 2) where rounding errors pile up fastest, and on N(0, 0.01^2)."""
+    rng = np.random.default_rng(36)
+    for dtype, u in (("fp16", 2.0**-11), ("bf16", 2.0**-8)):
+        n, count = 16, 100000
+        for xs in ([brute.narrow((1 + rng.random(count)).astype(np.float32), dtype) for _ in range(n)],
+                   _ranks(rng, dtype, n, count, 1e-2)):
+            x64 = [_to_f64(x, dtype) for x in xs]
+            s = np.sum(x64, axis=0)
+            sabs = np.sum(np.abs(x64), axis=0)
+            k = 4
+            bound = k * u / (1 - k * u) * sabs + 2.0**-24
+            y = _to_f64(orc.hd_allreduce(xs, dtype)[0], dtype)
+            assert np.all(np.abs(y - s) <= bound), dtype
+
+
+def pin_hd_rejects_non_power_of_two_and_detects_faults(orc):
+    rng = np.random.default_rng(37)
+    for n in (3, 5, 6, 12):
+        xs = _ranks(rng, "fp32", n, 10)
+        try:
+            orc.hd_allreduce(xs, "fp32")
+        except orc_mod.OracleError as e:
+            assert e.code == orc_mod.E_ARG
+        else:
+            raise AssertionError(f"n={n} accepted")
+    n = 8
+    xs = _ranks(rng, "fp32", n, 4 * n + 1)
+    for kind in (orc_mod.FAULT_DROP, orc_mod.FAULT_DUP, orc_mod.FAULT_MISROUTE, orc_mod.FAULT_WRONG_CHUNK):
+        for phase in (orc_mod.PHASE_HD_RS, orc_mod.PHASE_HD_AG):
+            for step in (0, 2):
+                f = orc_mod.Fault(kind, phase, step, rank=5)
+                try:
+                    orc.hd_allreduce(xs, "fp32", fault=f)
+                except orc_mod.OracleError as e:
+                    assert e.code in (orc_mod.E_EMPTY, orc_mod.E_TAG, orc_mod.E_LEFTOVER), e
+                else:
+                    raise AssertionError(f"hd fault {kind} phase {phase} step {step} not detected")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -54,6 +54,20 @@ MUTANTS = [
      "memcpy(mine, m->payload + k * nt->esz, nt->esz);"),
     ("decode_bias_off_by_one", "int bias = (1 << (ebits - 1)) - 1;\n    uint32_t sign = (bits",
      "int bias = (1 << (ebits - 1));\n    uint32_t sign = (bits"),
+    # halving-doubling
+    ("hd_keeps_other_half",
+     "int upper = (r & d) != 0;\n            int give_lo",
+     "int upper = (r & d) == 0;\n            int give_lo"),
+    ("hd_distances_ascending", "for (int d = n / 2; d >= 1 && step < steps; d /= 2, step++) {",
+     "for (int d = 1; d < n && step < steps; d *= 2, step++) {"),
+    ("hd_doubling_does_not_merge", "lo[r] = plo[r] < plo[p] ? plo[r] : plo[p];", "lo[r] = plo[r];"),
+    ("hd_closed_form_sequential",
+     "for (int d = n / 2; d >= 1; d /= 2)\n            for (int r = 0; r < d; r++) elem_add(dt, v + r * esz, v + r * esz, v + (r + d) * esz);",
+     "for (int r = 1; r < n; r++) elem_add(dt, v, v, v + r * esz);"),
+    ("hd_received_half_overwrites", "elem_add(nt->dt, mine, m->payload + k * nt->esz, mine);",
+     "memcpy(mine, m->payload + k * nt->esz, nt->esz);"),
+    ("hd_range_drops_remainder", "for (int b = lo; b < hi; b++) total += chunk_len(g, b);",
+     "for (int b = lo; b < hi; b++) total += g->count / (uint64_t)g->n;"),
 ]
 
 
