@@ -102,8 +102,30 @@ typedef enum { VRC_SUM = 0 } vrc_op_t;
  *                     barrier is needed).
  *   VRC_RING_ORDER    one launch with the fused traffic (read N, write N):
  *                     the ring's partials stay in registers.  For the
- *                     all-gather it equals VRC_FUSED. */
-typedef enum { VRC_RING = 0, VRC_FUSED = 1, VRC_RING_CHAINED = 2, VRC_RING_ORDER = 3 } vrc_mode_t;
+ *                     all-gather it equals VRC_FUSED.
+ * Halving-doubling [TP] (nranks must be a power of two, else
+ * VRC_ERR_INVALID_ARG): recursive halving reduce-scatter with distances N/2,
+ * N/4, ..., 1 (rank r pairs with r XOR d, keeps the half of its block range
+ * that holds block r and adds the partner's copy of it), then recursive
+ * doubling all-gather with distances 1, 2, ..., N/2.  Every element is
+ * summed as a butterfly: pairs at distance N/2 first, then N/4, ..., each
+ * partial rounded to the storage type.  VRC_HD and VRC_HD_ORDER return the
+ * same bits.
+ *   VRC_HD            one launch per step: 2 log2 N launches for the
+ *                     all-reduce, log2 N for the all-gather.  The stand-alone
+ *                     reduce-scatter has no room for the N/2 blocks of
+ *                     partials each rank holds after its first step (the
+ *                     library allocates nothing), so it runs as VRC_HD_ORDER.
+ *   VRC_HD_ORDER      one launch with the fused traffic, partials in
+ *                     registers.  For the all-gather it equals VRC_FUSED. */
+typedef enum {
+    VRC_RING = 0,
+    VRC_FUSED = 1,
+    VRC_RING_CHAINED = 2,
+    VRC_RING_ORDER = 3,
+    VRC_HD = 4,
+    VRC_HD_ORDER = 5
+} vrc_mode_t;
 
 typedef enum {
     VRC_OK = 0,

@@ -13,7 +13,9 @@ Modes: ``"ring"`` is the step-faithful ring (one launch per reduce-scatter
 and per all-gather step), ``"fused"`` the single-launch N-way kernel,
 ``"ring_chained"`` the ring's per-step reads and writes in one launch, and
 ``"ring_order"`` one launch with fused traffic but the ring's summation order
-(the three ring modes return the same bits).
+(the three ring modes return the same bits), ``"hd"`` halving-doubling with
+one launch per step and ``"hd_order"`` halving-doubling in one launch (both
+need a power-of-two rank count and return the same bits).
 """
 from __future__ import annotations
 
@@ -25,12 +27,14 @@ LIB_PATH = os.path.join(PKG, "libvrc.so")
 
 VRC_INT32, VRC_FP32, VRC_FP16, VRC_BF16 = 0, 1, 2, 3
 VRC_SUM = 0
-VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER = 0, 1, 2, 3
+VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER = 0, 1, 2, 3, 4, 5
 VRC_OK, VRC_ERR_INVALID_ARG, VRC_ERR_UNSUPPORTED, VRC_ERR_ALIAS, VRC_ERR_HIP = range(5)
 MAX_RANKS = 16
 
-MODES = {"ring": VRC_RING, "fused": VRC_FUSED, "ring_chained": VRC_RING_CHAINED, "ring_order": VRC_RING_ORDER}
+MODES = {"ring": VRC_RING, "fused": VRC_FUSED, "ring_chained": VRC_RING_CHAINED, "ring_order": VRC_RING_ORDER,
+         "hd": VRC_HD, "hd_order": VRC_HD_ORDER}
 RING_MODES = ("ring", "ring_chained", "ring_order")  # same bits as the per-step ring
+HD_MODES = ("hd", "hd_order")  # halving-doubling; nranks must be a power of two
 
 
 class VrcError(RuntimeError):
@@ -271,6 +275,6 @@ __all__ = [
     "vrc_allreduce", "vrc_reduce_scatter", "vrc_all_gather", "reduce_scatter_shape", "chunk_range",
     "version", "raw_allreduce", "raw_reduce_scatter", "raw_all_gather", "lib", "VrcError",
     "VRC_INT32", "VRC_FP32", "VRC_FP16", "VRC_BF16", "VRC_SUM", "VRC_RING", "VRC_FUSED", "VRC_RING_CHAINED",
-    "VRC_RING_ORDER", "MODES", "RING_MODES", "VRC_OK",
+    "VRC_RING_ORDER", "VRC_HD", "VRC_HD_ORDER", "MODES", "RING_MODES", "HD_MODES", "VRC_OK",
     "VRC_ERR_INVALID_ARG", "VRC_ERR_UNSUPPORTED", "VRC_ERR_ALIAS", "VRC_ERR_HIP", "MAX_RANKS",
 ]

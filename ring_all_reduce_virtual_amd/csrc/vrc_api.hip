@@ -16,6 +16,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 
 #include "vrc.h"
 #include "vrc_kernels.hpp"
@@ -405,15 +406,16 @@ struct Launch {
     }
 
     // ---- fused family ----------------------------------------------------
-    template <int N>
+    template <int N, class Fold>
     static void launch_fused_ar_n(const vrc::FusedArArgs& a, dim3 grid, hipStream_t st)
     {
         if (tuning().unroll == 2)
-            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 2, true>), grid, dim3(kBlock), 0, st, a);
+            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 2, true, Fold>), grid, dim3(kBlock), 0, st, a);
         else
-            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 1, true>), grid, dim3(kBlock), 0, st, a);
+            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 1, true, Fold>), grid, dim3(kBlock), 0, st, a);
     }
 
+    template <class Fold = vrc::RankFold>
     static vrc_status_t fused_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
                                         hipStream_t st)
     {
@@ -434,22 +436,33 @@ struct Launch {
         a.g = split_rows(addr, 2 * n, 1, nullptr, 0, count, E);
         const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
         const dim3 grid(grid_x(cus, work, 1, fused_blocks_per_cu(2 * (uint64_t)n * count * E)));
-        switch (n) {
+        if constexpr (std::is_same<Fold, vrc::Butterfly>::value) {
+            switch (n) {
+            case 2: launch_fused_ar_n<2, Fold>(a, grid, st); break;
+            case 4: launch_fused_ar_n<4, Fold>(a, grid, st); break;
+            case 8: launch_fused_ar_n<8, Fold>(a, grid, st); break;
+            case 16: launch_fused_ar_n<16, Fold>(a, grid, st); break;
+            default: return VRC_ERR_INVALID_ARG;
+            }
+        } else {
+            switch (n) {
 #define VRC_CASE(K) \
-    case K: launch_fused_ar_n<K>(a, grid, st); break;
-            VRC_FOR_N(VRC_CASE)
+    case K: launch_fused_ar_n<K, Fold>(a, grid, st); break;
+                VRC_FOR_N(VRC_CASE)
 #undef VRC_CASE
-        default: return VRC_ERR_INVALID_ARG;
+            default: return VRC_ERR_INVALID_ARG;
+            }
         }
         return check_launch();
     }
 
-    template <int N>
+    template <int N, class Fold>
     static void launch_fused_rs_n(const vrc::FusedRsArgs& a, dim3 grid, hipStream_t st)
     {
-        hipLaunchKernelGGL((vrc::k_fused_reduce_scatter<T, N, true>), grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((vrc::k_fused_reduce_scatter<T, N, true, Fold>), grid, dim3(kBlock), 0, st, a);
     }
 
+    template <class Fold = vrc::RankFold>
     static vrc_status_t fused_reduce_scatter(const char* const* x, char* const* y, int n, uint64_t count,
                                              uint64_t outer, int cus, hipStream_t st)
     {
@@ -475,12 +488,22 @@ struct Launch {
             if (w > work) work = w;
         }
         const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * count * E)), (unsigned)n);
-        switch (n) {
+        if constexpr (std::is_same<Fold, vrc::Butterfly>::value) {
+            switch (n) {
+            case 2: launch_fused_rs_n<2, Fold>(a, grid, st); break;
+            case 4: launch_fused_rs_n<4, Fold>(a, grid, st); break;
+            case 8: launch_fused_rs_n<8, Fold>(a, grid, st); break;
+            case 16: launch_fused_rs_n<16, Fold>(a, grid, st); break;
+            default: return VRC_ERR_INVALID_ARG;
+            }
+        } else {
+            switch (n) {
 #define VRC_CASE(K) \
-    case K: launch_fused_rs_n<K>(a, grid, st); break;
-            VRC_FOR_N(VRC_CASE)
+    case K: launch_fused_rs_n<K, Fold>(a, grid, st); break;
+                VRC_FOR_N(VRC_CASE)
 #undef VRC_CASE
-        default: return VRC_ERR_INVALID_ARG;
+            default: return VRC_ERR_INVALID_ARG;
+            }
         }
         return check_launch();
     }
@@ -510,6 +533,126 @@ struct Launch {
         const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * n * count * E)), (unsigned)n);
         hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
         return check_launch();
+    }
+
+    // ---- halving-doubling, one launch per step ---------------------------
+    // Block range [lo, hi) of a flat buffer as an element range.
+    static void block_span(uint64_t count, int n, int lo, int hi, uint64_t* off, uint64_t* len)
+    {
+        const uint64_t base = count / (uint64_t)n;
+        const uint64_t end = (hi == n) ? count : (uint64_t)hi * base;
+        *off = (uint64_t)lo * base;
+        *len = end - *off;
+    }
+
+    // Recursive halving (distances N/2 .. 1): rank r keeps the half of its
+    // block range that holds block r and adds the partner's (r XOR d) copy
+    // of that half.  Then recursive doubling (distances 1 .. N/2): rank r
+    // copies the partner's range.  2 log2 N launches.
+    static vrc_status_t hd_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
+                                     hipStream_t st)
+    {
+        if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        int lo[kMaxRanks], hi[kMaxRanks], nlo[kMaxRanks], nhi[kMaxRanks];
+        for (int r = 0; r < n; r++) {
+            lo[r] = 0;
+            hi[r] = n;
+        }
+        vrc::StepArgs args;
+        bool first = true;
+        for (int d = n / 2; d >= 1; d /= 2) {
+            uint64_t work = 0;
+            for (int r = 0; r < n; r++) {
+                const int p = r ^ d, mid = (lo[r] + hi[r]) / 2;
+                const bool upper = (r & d) != 0;
+                nlo[r] = upper ? mid : lo[r];
+                nhi[r] = upper ? hi[r] : mid;
+                uint64_t off, len;
+                block_span(count, n, nlo[r], nhi[r], &off, &len);
+                const char* own = (first ? x[r] : y[r]) + off * E;
+                const char* other = (first ? x[p] : y[p]) + off * E;
+                args.op[r] = make_op(own, other, y[r] + off * E, 1, len, 0, 0, 0);
+                const uint64_t w = op_work(args.op[r]);
+                if (w > work) work = w;
+            }
+            vrc_status_t rc = step<true>(args, n, work, cus, st);
+            if (rc) return rc;
+            for (int r = 0; r < n; r++) {
+                lo[r] = nlo[r];
+                hi[r] = nhi[r];
+            }
+            first = false;
+        }
+        for (int d = 1; d < n; d *= 2) {
+            uint64_t work = 0;
+            for (int r = 0; r < n; r++) {
+                const int p = r ^ d;
+                uint64_t off, len;
+                block_span(count, n, lo[p], hi[p], &off, &len);
+                args.op[r] = make_op(y[p] + off * E, nullptr, y[r] + off * E, 1, len, 0, 0, 0);
+                const uint64_t w = op_work(args.op[r]);
+                if (w > work) work = w;
+            }
+            vrc_status_t rc = step<false>(args, n, work, cus, st);
+            if (rc) return rc;
+            for (int r = 0; r < n; r++) {
+                nlo[r] = lo[r] < lo[r ^ d] ? lo[r] : lo[r ^ d];
+                nhi[r] = hi[r] > hi[r ^ d] ? hi[r] : hi[r ^ d];
+            }
+            for (int r = 0; r < n; r++) {
+                lo[r] = nlo[r];
+                hi[r] = nhi[r];
+            }
+        }
+        return VRC_OK;
+    }
+
+    // Recursive-doubling all-gather over the slabs of [outer, N*row]
+    // outputs.  Step 0 copies each rank's own slab and its distance-1
+    // partner's slab from the inputs; step d copies the partner's slab range
+    // from the partner's output.  log2 N launches.
+    static vrc_status_t hd_all_gather(const char* const* x, char* const* y, int n, uint64_t count, uint64_t outer,
+                                      int cus, hipStream_t st)
+    {
+        const uint64_t row = count / outer, sy = (uint64_t)n * row;
+        if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        int lo[kMaxRanks], hi[kMaxRanks], nlo[kMaxRanks], nhi[kMaxRanks];
+        vrc::StepArgs args;
+        uint64_t work = 0;
+        for (int r = 0; r < n; r++) {
+            const int p = r ^ 1;
+            args.op[2 * r] = make_op(x[r], nullptr, y[r] + (uint64_t)r * row * E, outer, row, row, 0, sy);
+            args.op[2 * r + 1] = make_op(x[p], nullptr, y[r] + (uint64_t)p * row * E, outer, row, row, 0, sy);
+            const uint64_t w0 = op_work(args.op[2 * r]), w1 = op_work(args.op[2 * r + 1]);
+            if (w0 > work) work = w0;
+            if (w1 > work) work = w1;
+            lo[r] = r < p ? r : p;
+            hi[r] = (r < p ? p : r) + 1;
+        }
+        vrc_status_t rc = step<false>(args, 2 * n, work, cus, st);
+        if (rc) return rc;
+        for (int d = 2; d < n; d *= 2) {
+            work = 0;
+            for (int r = 0; r < n; r++) {
+                const int p = r ^ d;
+                const uint64_t off = (uint64_t)lo[p] * row * E;
+                const uint64_t width = (uint64_t)(hi[p] - lo[p]) * row;
+                args.op[r] = make_op(y[p] + off, nullptr, y[r] + off, outer, width, sy, 0, sy);
+                const uint64_t w = op_work(args.op[r]);
+                if (w > work) work = w;
+            }
+            rc = step<false>(args, n, work, cus, st);
+            if (rc) return rc;
+            for (int r = 0; r < n; r++) {
+                nlo[r] = lo[r] < lo[r ^ d] ? lo[r] : lo[r ^ d];
+                nhi[r] = hi[r] > hi[r ^ d] ? hi[r] : hi[r ^ d];
+            }
+            for (int r = 0; r < n; r++) {
+                lo[r] = nlo[r];
+                hi[r] = nhi[r];
+            }
+        }
+        return VRC_OK;
     }
 
     // ---- single-launch ring (chained per element) ------------------------
@@ -633,6 +776,8 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
         case VRC_FUSED: return L::fused_allreduce(x, y, n, count, cus, st);
         case VRC_RING_CHAINED: return L::template chain_allreduce<true>(x, y, n, count, cus, st);
         case VRC_RING_ORDER: return L::template chain_allreduce<false>(x, y, n, count, cus, st);
+        case VRC_HD: return L::hd_allreduce(x, y, n, count, cus, st);
+        case VRC_HD_ORDER: return L::template fused_allreduce<vrc::Butterfly>(x, y, n, count, cus, st);
         }
         break;
     case Coll::RS:
@@ -641,14 +786,18 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
         case VRC_FUSED: return L::fused_reduce_scatter(x, y, n, count, outer, cus, st);
         case VRC_RING_CHAINED: return L::template chain_reduce_scatter<true>(x, y, n, count, outer, cus, st);
         case VRC_RING_ORDER: return L::template chain_reduce_scatter<false>(x, y, n, count, outer, cus, st);
+        case VRC_HD:
+        case VRC_HD_ORDER: return L::template fused_reduce_scatter<vrc::Butterfly>(x, y, n, count, outer, cus, st);
         }
         break;
     case Coll::AG:
         switch (mode) {
         case VRC_RING: return L::ring_all_gather(x, y, n, count, outer, cus, st);
         case VRC_FUSED:
-        case VRC_RING_ORDER: return L::fused_all_gather(x, y, n, count, outer, cus, st);
+        case VRC_RING_ORDER:
+        case VRC_HD_ORDER: return L::fused_all_gather(x, y, n, count, outer, cus, st);
         case VRC_RING_CHAINED: return L::chain_all_gather(x, y, n, count, outer, cus, st);
+        case VRC_HD: return L::hd_all_gather(x, y, n, count, outer, cus, st);
         }
         break;
     }
@@ -679,7 +828,15 @@ vrc_status_t run(Coll coll, vrc_mode_t mode, vrc_dtype_t dt, const void* const* 
 
 bool mode_ok(vrc_mode_t m)
 {
-    return m == VRC_RING || m == VRC_FUSED || m == VRC_RING_CHAINED || m == VRC_RING_ORDER;
+    return m == VRC_RING || m == VRC_FUSED || m == VRC_RING_CHAINED || m == VRC_RING_ORDER || m == VRC_HD ||
+           m == VRC_HD_ORDER;
+}
+
+// Halving-doubling pairs rank r with r XOR d, so it needs a power of two.
+bool ranks_ok_for(vrc_mode_t m, int n)
+{
+    if (m != VRC_HD && m != VRC_HD_ORDER) return true;
+    return (n & (n - 1)) == 0;
 }
 
 }  // namespace
@@ -695,6 +852,7 @@ vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nrank
     vrc_status_t rc = check_common(send, recv, nranks, dtype);
     if (rc) return rc;
     if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
+    if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     const uint64_t bytes = (uint64_t)count * (uint64_t)esize(dtype);
     uint64_t rb[kMaxRanks];
     for (int r = 0; r < nranks; r++) rb[r] = bytes;
@@ -711,6 +869,7 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
     vrc_status_t rc = check_common(send, recv, nranks, dtype);
     if (rc) return rc;
     if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
+    if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     if (outer > 1 && (count / outer) % (uint64_t)nranks != 0) return VRC_ERR_INVALID_ARG;
     const int E = esize(dtype);
@@ -736,6 +895,7 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
     vrc_status_t rc = check_common(send, recv, nranks, dtype);
     if (rc) return rc;
     if (!mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
+    if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     const int E = esize(dtype);
     uint64_t rb[kMaxRanks];

@@ -119,7 +119,48 @@ __device__ __forceinline__ u32x4 fold_v(const u32x4* in)
     return T::pack(acc);
 }
 
-template <class T, int N, int U, bool NT>
+// How the fused kernels combine the N values of one element.
+//  RankFold:  x_0 + x_1 + ... + x_{N-1} folded left in the accumulator type,
+//             rounded once (the collector all-reduce).
+//  Butterfly: halving-doubling order, N a power of two: pairs at distance
+//             N/2 first, then N/4, ..., each partial rounded to the storage
+//             type: v[r] = v[r] (+) v[r + d] for r < d, d = N/2 .. 1.
+struct RankFold {
+    template <class T, int N>
+    __device__ static u32x4 vec(u32x4* in) { return fold_v<T, N>(in); }
+    template <class T, int N>
+    __device__ static typename T::S scalar(typename T::S* in)
+    {
+        typename T::A acc = T::widen(in[0]);
+#pragma unroll
+        for (int r = 1; r < N; r++) acc = T::add(acc, T::widen(in[r]));
+        return T::narrow(acc);
+    }
+};
+
+struct Butterfly {
+    template <class T, int N>
+    __device__ static u32x4 vec(u32x4* in)
+    {
+        static_assert((N & (N - 1)) == 0, "butterfly needs a power of two");
+#pragma unroll
+        for (int d = N / 2; d >= 1; d /= 2)
+#pragma unroll
+            for (int r = 0; r < d; r++) in[r] = add_v<T>(in[r], in[r + d]);
+        return in[0];
+    }
+    template <class T, int N>
+    __device__ static typename T::S scalar(typename T::S* in)
+    {
+#pragma unroll
+        for (int d = N / 2; d >= 1; d /= 2)
+#pragma unroll
+            for (int r = 0; r < d; r++) in[r] = add_s<T>(in[r], in[r + d]);
+        return in[0];
+    }
+};
+
+template <class T, int N, int U, bool NT, class Fold = RankFold>
 __global__ __launch_bounds__(kBlock) void k_fused_allreduce(FusedArArgs a)
 {
     const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -138,7 +179,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_allreduce(FusedArArgs a)
                 for (int r = 0; r < N; r++) in[u][r] = ld16<NT>(a.src[r] + body + (v + u * nthreads) * 16);
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const u32x4 s = fold_v<T, N>(in[u]);
+                const u32x4 s = Fold::template vec<T, N>(in[u]);
 #pragma unroll
                 for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + (v + u * nthreads) * 16, s);
             }
@@ -148,7 +189,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_allreduce(FusedArArgs a)
         u32x4 in[N];
 #pragma unroll
         for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
-        const u32x4 s = fold_v<T, N>(in);
+        const u32x4 s = Fold::template vec<T, N>(in);
 #pragma unroll
         for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, s);
     }
@@ -156,10 +197,10 @@ __global__ __launch_bounds__(kBlock) void k_fused_allreduce(FusedArArgs a)
     const uint64_t ns = a.g.head + a.g.tail;
     for (uint64_t k = tid; k < ns; k += nthreads) {
         const uint64_t i = (k < a.g.head) ? k : a.g.head + a.g.nvb * T::VEC + (k - a.g.head);
-        typename T::A acc = T::widen(load_s<T>(a.src[0] + i * E));
+        typename T::S in[N];
 #pragma unroll
-        for (int r = 1; r < N; r++) acc = T::add(acc, T::widen(load_s<T>(a.src[r] + i * E)));
-        const typename T::S s = T::narrow(acc);
+        for (int r = 0; r < N; r++) in[r] = load_s<T>(a.src[r] + i * E);
+        const typename T::S s = Fold::template scalar<T, N>(in);
 #pragma unroll
         for (int r = 0; r < N; r++) store_s<T>(a.dst[r] + i * E, s);
     }
@@ -182,7 +223,7 @@ struct FusedRsArgs {
     RsChunk ch[kMaxRanks];
 };
 
-template <class T, int N, bool NT>
+template <class T, int N, bool NT, class Fold = RankFold>
 __global__ __launch_bounds__(kBlock) void k_fused_reduce_scatter(FusedRsArgs a)
 {
     const RsChunk& c = a.ch[blockIdx.y];
@@ -197,17 +238,17 @@ __global__ __launch_bounds__(kBlock) void k_fused_reduce_scatter(FusedRsArgs a)
         u32x4 in[N];
 #pragma unroll
         for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + so);
-        st16<NT>(c.d + row * c.s_dst * E + col, fold_v<T, N>(in));
+        st16<NT>(c.d + row * c.s_dst * E + col, Fold::template vec<T, N>(in));
     }
     const uint64_t ns = c.rows * (c.g.head + c.g.tail);
     for (uint64_t k = tid; k < ns; k += nthreads) {
         uint64_t row, col;
         scalar_slot(k, c.g, T::VEC, row, col);
         const uint64_t so = (c.src_off + row * c.s_src + col) * E;
-        typename T::A acc = T::widen(load_s<T>(a.src[0] + so));
+        typename T::S in[N];
 #pragma unroll
-        for (int r = 1; r < N; r++) acc = T::add(acc, T::widen(load_s<T>(a.src[r] + so)));
-        store_s<T>(c.d + (row * c.s_dst + col) * E, T::narrow(acc));
+        for (int r = 0; r < N; r++) in[r] = load_s<T>(a.src[r] + so);
+        store_s<T>(c.d + (row * c.s_dst + col) * E, Fold::template scalar<T, N>(in));
     }
 }
 

@@ -75,7 +75,7 @@ def test_invalid_arguments_return_before_any_gpu_call():
                              vrc.VRC_FP32, vrc.VRC_RING) == vrc.VRC_ERR_INVALID_ARG
     # unknown dtype / op / mode
     assert vrc.raw_allreduce(x, y, count, 7, vrc.VRC_RING) == vrc.VRC_ERR_UNSUPPORTED
-    assert vrc.raw_allreduce(x, y, count, vrc.VRC_FP32, 5) == vrc.VRC_ERR_UNSUPPORTED
+    assert vrc.raw_allreduce(x, y, count, vrc.VRC_FP32, 9) == vrc.VRC_ERR_UNSUPPORTED
     assert vrc.raw_allreduce(x, y, count, vrc.VRC_FP32, vrc.VRC_RING, op=3) == vrc.VRC_ERR_UNSUPPORTED
     assert vrc.raw_all_gather(x, y, count, 1, vrc.VRC_FP32, 9) == vrc.VRC_ERR_UNSUPPORTED
     # null device pointer with count > 0
@@ -120,3 +120,13 @@ def test_alias_detection():
     # all-gather outputs are n times larger: adjacent 1 MiB strides overlap
     ag_y = addrs(FAKE + (64 << 20), n, count * E)  # each output needs n*count*E bytes
     assert vrc.raw_all_gather(x, ag_y, count, 1, vrc.VRC_FP32, vrc.VRC_RING) == A
+
+
+def test_halving_doubling_needs_a_power_of_two():
+    x = addrs(FAKE, 3, 1 << 20)
+    y = addrs(FAKE + (64 << 20), 3, 1 << 20)
+    for mode in (vrc.VRC_HD, vrc.VRC_HD_ORDER):
+        assert vrc.raw_allreduce(x, y, 1000, vrc.VRC_FP32, mode) == vrc.VRC_ERR_INVALID_ARG
+        assert vrc.raw_reduce_scatter(x, y, 1000, 1, vrc.VRC_FP32, mode) == vrc.VRC_ERR_INVALID_ARG
+        assert vrc.raw_all_gather(x, y, 1000, 1, vrc.VRC_FP32, mode) == vrc.VRC_ERR_INVALID_ARG
+    assert vrc.raw_allreduce(x, y, 1000, vrc.VRC_FP32, 6) == vrc.VRC_ERR_UNSUPPORTED

@@ -12,8 +12,14 @@ from tests.parity_util import assert_bitwise, host
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 DTYPES = ("int32", "fp32", "fp16", "bf16")
-MODES = ("ring", "fused", "ring_chained", "ring_order")
+MODES = ("ring", "fused", "ring_chained", "ring_order", "hd", "hd_order")
 RING_FAMILY = ("ring", "ring_chained", "ring_order")
+HD_FAMILY = ("hd", "hd_order")
+
+
+def runs(mode, n):
+    """Halving-doubling needs a power-of-two rank count."""
+    return mode not in HD_FAMILY or n & (n - 1) == 0
 
 
 def say(msg):
@@ -34,12 +40,18 @@ def orc():
 
 
 def oracle_ar(orc, hx, dtype, mode):
-    return orc.ring_allreduce(hx, dtype) if mode in RING_FAMILY else orc.fused_allreduce(hx, dtype)
+    if mode in RING_FAMILY:
+        return orc.ring_allreduce(hx, dtype)
+    if mode in HD_FAMILY:
+        return orc.hd_allreduce(hx, dtype)
+    return orc.fused_allreduce(hx, dtype)
 
 
 def oracle_rs(orc, hx, dtype, mode, outer=1):
     if mode in RING_FAMILY:
         return orc.ring_reduce_scatter(hx, dtype, outer=outer)
+    if mode in HD_FAMILY:
+        return orc.hd_reduce_scatter(hx, dtype, outer=outer)
     return orc.fused_reduce_scatter(hx, dtype, outer=outer)
 
 
@@ -59,7 +71,7 @@ def test_in_place_equals_out_of_place(vrc, orc, mode, dtype):
 @pytest.mark.parametrize("mode", MODES)
 def test_some_ranks_in_place(vrc, orc, mode):
     say(f"mixed in place {mode}")
-    n, count = 5, 40000
+    n, count = (5 if runs(mode, 5) else 4), 40000
     xs = workloads.random_ranks(n, count, "fp32", seed=401, device=DEV)
     want = oracle_ar(orc, host(xs), "fp32", mode)
     recv = [xs[r] if r % 2 == 0 else torch.empty_like(xs[r]) for r in range(n)]
@@ -128,6 +140,12 @@ def test_single_rank_is_identity(vrc, mode, dtype):
 def test_fewer_elements_than_ranks(vrc, orc, mode, n, count):
     say(f"count<n {mode} n={n} count={count}")
     xs = workloads.random_ranks(n, count, "fp32", seed=404, device=DEV)
+    if not runs(mode, n):  # halving-doubling needs a power-of-two rank count
+        for call in (lambda: vrc.vrc_allreduce(xs, mode=mode), lambda: vrc.vrc_reduce_scatter(xs, mode=mode)):
+            with pytest.raises(vrc.VrcError) as e:
+                call()
+            assert e.value.status == vrc.VRC_ERR_INVALID_ARG
+        return
     ys = vrc.vrc_allreduce(xs, mode=mode)
     rs = vrc.vrc_reduce_scatter(xs, mode=mode)
     torch.cuda.synchronize()
@@ -151,7 +169,7 @@ def test_repeat_runs_are_bitwise_identical(vrc, mode):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-@pytest.mark.parametrize("mode", RING_FAMILY)
+@pytest.mark.parametrize("mode", RING_FAMILY + HD_FAMILY)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_all_gather_of_reduce_scatter_is_allreduce(vrc, dtype, mode):
     say(f"composition {dtype} {mode}")
@@ -181,11 +199,11 @@ def test_exact_small_integers_ring_equals_fused(vrc):
 
 def test_int32_wraps(vrc):
     say("int32 wrap")
-    xs = [torch.full((1000,), 2**31 - 1, dtype=torch.int32, device=DEV) for _ in range(3)]
+    xs = [torch.full((1000,), 2**31 - 1, dtype=torch.int32, device=DEV) for _ in range(4)]
     for mode in MODES:
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
-        assert torch.all(ys[0] == 2**31 - 3)
+        assert torch.all(ys[0] == -4)  # 4 * (2^31 - 1) = 2^33 - 4, which wraps to -4
 
 
 def test_fp16_overflow_goes_to_inf(vrc, orc):
@@ -238,6 +256,9 @@ def test_errors_through_the_binding(vrc):
         vrc.vrc_reduce_scatter([x.view(8, 125) for x in xs], dim=1)  # 125 not divisible by 4
     with pytest.raises(TypeError):
         vrc.vrc_allreduce([x.double() for x in xs])
+    with pytest.raises(vrc.VrcError) as e:
+        vrc.vrc_allreduce(xs[:3], mode="hd")  # halving-doubling needs a power of two
+    assert e.value.status == vrc.VRC_ERR_INVALID_ARG
     empty = [torch.empty(0, device=DEV) for _ in range(4)]
     for mode in MODES:
         vrc.vrc_allreduce(empty, mode=mode)

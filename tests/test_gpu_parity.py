@@ -20,8 +20,39 @@ from tests.parity_util import (assert_bitwise, host, ranks_identical, sample_ind
 pytestmark = pytest.mark.gpu
 
 DTYPES = ("int32", "fp32", "fp16", "bf16")
-MODES = ("ring", "fused", "ring_chained", "ring_order")
+MODES = ("ring", "fused", "ring_chained", "ring_order", "hd", "hd_order")
 RING_FAMILY = ("ring", "ring_chained", "ring_order")  # all return the per-step ring's bits
+HD_FAMILY = ("hd", "hd_order")  # halving-doubling: power-of-two rank counts only
+
+
+def pow2(n):
+    return n & (n - 1) == 0
+
+
+def want_ar(orc, hx, dtype, mode):
+    if mode in RING_FAMILY:
+        return orc.ring_allreduce(hx, dtype)
+    if mode in HD_FAMILY:
+        return orc.hd_allreduce(hx, dtype)
+    return orc.fused_allreduce(hx, dtype)
+
+
+def want_rs(orc, hx, dtype, mode, outer=1):
+    if mode in RING_FAMILY:
+        return orc.ring_reduce_scatter(hx, dtype, outer=outer)
+    if mode in HD_FAMILY:
+        return orc.hd_reduce_scatter(hx, dtype, outer=outer)
+    return orc.fused_reduce_scatter(hx, dtype, outer=outer)
+
+
+def rejects_non_pow2(vrc, fn, mode, n):
+    """HD modes need a power-of-two rank count; anything else is an argument error."""
+    if mode in HD_FAMILY and not pow2(n):
+        with pytest.raises(vrc.VrcError) as e:
+            fn()
+        assert e.value.status == vrc.VRC_ERR_INVALID_ARG
+        return True
+    return False
 
 
 def say(msg):
@@ -54,10 +85,12 @@ DEV = "cuda:0"
 def test_allreduce_small(vrc, orc, mode, dtype, n, count):
     say(f"allreduce {mode} {dtype} n={n} count={count}")
     xs = workloads.random_ranks(n, count, dtype, seed=100 + n * 7 + count % 97, device=DEV)
+    if rejects_non_pow2(vrc, lambda: vrc.vrc_allreduce(xs, mode=mode), mode, n):
+        return
     ys = vrc.vrc_allreduce(xs, mode=mode)
     torch.cuda.synchronize()
     hx = host(xs)
-    want = orc.ring_allreduce(hx, dtype) if mode in RING_FAMILY else orc.fused_allreduce(hx, dtype)
+    want = want_ar(orc, hx, dtype, mode)
     for r, y in enumerate(host(ys)):
         assert_bitwise(y, want[r], f"{mode} {dtype} n={n} count={count} rank {r}")
 
@@ -78,12 +111,13 @@ RS_CASES = [  # (n, shape, dim)
 def test_reduce_scatter_small(vrc, orc, mode, dtype, n, shape, dim):
     say(f"reduce_scatter {mode} {dtype} n={n} shape={shape} dim={dim}")
     xs = workloads.random_ranks(n, shape, dtype, seed=200 + n + len(shape), device=DEV)
+    if rejects_non_pow2(vrc, lambda: vrc.vrc_reduce_scatter(xs, dim=dim, mode=mode), mode, n):
+        return
     ys = vrc.vrc_reduce_scatter(xs, dim=dim, mode=mode)
     torch.cuda.synchronize()
     outer = int(np.prod(shape[:dim % len(shape)])) if len(shape) > 1 else 1
     hx = host(xs)
-    want = (orc.ring_reduce_scatter(hx, dtype, outer=outer) if mode in RING_FAMILY
-            else orc.fused_reduce_scatter(hx, dtype, outer=outer))
+    want = want_rs(orc, hx, dtype, mode, outer)
     for c, y in enumerate(host(ys)):
         assert_bitwise(y, want[c], f"rs {mode} {dtype} n={n} shape={shape} chunk {c}")
 
@@ -100,10 +134,12 @@ AG_CASES = [  # (n, shape, dim)
 def test_all_gather_small(vrc, orc, mode, dtype, n, shape, dim):
     say(f"all_gather {mode} {dtype} n={n} shape={shape} dim={dim}")
     xs = workloads.random_ranks(n, shape, dtype, seed=300 + n + len(shape), device=DEV)
+    if rejects_non_pow2(vrc, lambda: vrc.vrc_all_gather(xs, dim=dim, mode=mode), mode, n):
+        return
     ys = vrc.vrc_all_gather(xs, dim=dim, mode=mode)
     torch.cuda.synchronize()
     outer = int(np.prod(shape[:dim % len(shape)])) if len(shape) > 1 else 1
-    want = orc.ring_all_gather(host(xs), dtype, outer=outer)
+    want = (orc.hd_all_gather if mode in HD_FAMILY else orc.ring_all_gather)(host(xs), dtype, outer=outer)
     ref = torch.cat(xs, dim=dim)
     for r, y in enumerate(ys):
         assert tuple(y.shape) == tuple(ref.shape)
@@ -122,7 +158,7 @@ def test_workload_allreduce_int32_n4_4099(vrc, orc):
         say(f"{w.name} {mode}")
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
-        want = orc.ring_allreduce(hx, "int32") if mode in RING_FAMILY else orc.fused_allreduce(hx, "int32")
+        want = want_ar(orc, hx, "int32", mode)
         for r, y in enumerate(host(ys)):
             assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
             assert_bitwise(y, naive, f"{w.name} {mode} rank {r} vs naive sum")
@@ -141,8 +177,8 @@ def test_workload_allreduce_fp32_n8_16mib(vrc, orc):
         if mode in RING_FAMILY:
             want = want_ring
         else:
-            want = orc.fused_allreduce(hx, "fp32")
-            tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} fused")
+            want = want_ar(orc, hx, "fp32", mode)
+            tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} {mode}")
         for r, y in enumerate(host(ys)):
             assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
 
@@ -158,26 +194,33 @@ def test_workload_allreduce_fp16_sweep(vrc, orc, count):
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
         tolerance_gate_torch(ys, xs, w.rtol, f"{w.name} {mode}")
-        want = want_ring if mode in RING_FAMILY else orc.fused_allreduce(hx, "fp16")
+        want = want_ring if mode in RING_FAMILY else want_ar(orc, hx, "fp16", mode)
         for r, y in enumerate(host(ys)):
             assert_bitwise(y, want[r], f"{w.name} {mode} rank {r}")
 
 
-def ring_bound(n: int, dtype: str) -> float:
-    """Error bound of the ring's recursive sum with every partial rounded to
-    the storage type: gamma_{n-1} = (n-1)u / (1 - (n-1)u), u the storage unit
-    roundoff (2^-24 fp32, 2^-11 fp16, 2^-8 bf16)."""
+def gamma(k: int, dtype: str) -> float:
+    """gamma_k = k u / (1 - k u), u the storage unit roundoff (2^-24 fp32,
+    2^-11 fp16, 2^-8 bf16): the bound of a sum whose every partial is
+    rounded to the storage type along a depth-k tree."""
     u = {"fp32": 2.0**-24, "fp16": 2.0**-11, "bf16": 2.0**-8}[dtype]
-    k = n - 1
     return k * u / (1 - k * u)
 
 
+def ring_bound(n: int, dtype: str) -> float:
+    """The ring's sequential sum: depth n-1."""
+    return gamma(n - 1, dtype)
+
+
 def gate_rtol(w, mode: str) -> float:
-    """The workload's tolerance for its gated modes.  A bf16 ring is not a
-    gated mode of any workload: 7 roundings to an 8-bit significand can
-    exceed 1e-2, so it is held to its own derived bound instead."""
-    if mode in RING_FAMILY and w.dtype == "bf16":
+    """The workload's tolerance for its gated modes.  bf16 in the ring or
+    halving-doubling family is not a gated mode of any workload: 7 (ring) or
+    3 (halving-doubling) roundings to an 8-bit significand can exceed 1e-2,
+    so it is held to its own derived bound instead."""
+    if w.dtype == "bf16" and mode in RING_FAMILY:
         return ring_bound(w.n, "bf16")
+    if w.dtype == "bf16" and mode in HD_FAMILY:
+        return gamma(w.n.bit_length() - 1, "bf16")
     return w.rtol
 
 
@@ -192,7 +235,8 @@ def _sampled_allreduce(vrc, orc, w, modes, m):
         torch.cuda.synchronize()
         ranks_identical(ys, f"{w.name} {mode}")
         tolerance_gate_torch(ys, xs, gate_rtol(w, mode), f"{w.name} {mode}")
-        at = orc.ring_allreduce_at if mode in RING_FAMILY else orc.fused_allreduce_at
+        at = (orc.ring_allreduce_at if mode in RING_FAMILY else
+              orc.hd_allreduce_at if mode in HD_FAMILY else orc.fused_allreduce_at)
         want = at(hx, w.dtype, idx)
         for r in (0, w.n - 1):
             got = workloads.to_numpy(ys[r].reshape(-1)[tidx])
@@ -216,6 +260,7 @@ def test_workload_all_gather_fp16_n8_heads(vrc, orc):
     w = workloads.WORKLOADS["all_gather_fp16_n8_heads"]
     xs = workloads.make_inputs(w, DEV)
     want = orc.ring_all_gather(host(xs), "fp16", outer=1)
+    assert all(np.array_equal(a, b) for a, b in zip(want, orc.hd_all_gather(host(xs), "fp16", outer=1)))
     for mode in MODES:
         say(f"{w.name} {mode}")
         ys = vrc.vrc_all_gather(xs, dim=w.dim, mode=mode)
@@ -235,8 +280,7 @@ def test_workload_reduce_scatter_fp16_n8_act(vrc, orc):
         ys = vrc.vrc_reduce_scatter(xs, dim=w.dim, mode=mode)
         torch.cuda.synchronize()
         assert tuple(ys[0].shape) == (8, 512)
-        want = (orc.ring_reduce_scatter(hx, "fp16", outer=8) if mode in RING_FAMILY
-                else orc.fused_reduce_scatter(hx, "fp16", outer=8))
+        want = want_rs(orc, hx, "fp16", mode, outer=8)
         for c, y in enumerate(host(ys)):
             assert_bitwise(y, want[c], f"{w.name} {mode} chunk {c}")
         # tolerance gate against the fp64 sum of each column block
