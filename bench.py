@@ -54,7 +54,7 @@ def alg_bytes(mode: str, n: int, size_bytes: int) -> int:
     N inputs and write N outputs.  Ring and ring-chained: N-1 reduce-scatter
     steps read two chunks and write one per rank (3S per step), N-1
     all-gather steps read and write one chunk per rank (2S per step)."""
-    if mode in ("fused", "ring_order"):
+    if mode in ("fused", "ring_order", "hd_order"):
         return 2 * n * size_bytes
     return 5 * (n - 1) * size_bytes
 
@@ -63,7 +63,7 @@ def recorded_traffic(workload: str, mode: str):
     """Measured HBM bytes per launch from profiles/<kernel>.<workload>.counters.md,
     if those counters were taken on the current kernel sources."""
     kernel = {"fused": "k_fused_allreduce", "ring": "k_ring_step", "ring_chained": "k_ring_chain_allreduce",
-              "ring_order": "k_ring_chain_allreduce"}[mode]
+              "ring_order": "k_ring_chain_allreduce", "hd": "k_ring_step", "hd_order": "k_fused_allreduce_butterfly"}[mode]
     path = os.path.join(PROFILES, f"{kernel}.{workload}.counters.md")
     if not os.path.exists(path):
         return None
@@ -121,7 +121,7 @@ def cpu_baseline(xs, w, mode: str):
 def suite_bytes(w, mode: str) -> int:
     """Algorithmic bytes per call for a workload's collective and mode."""
     n, size = w.n, w.count * w.esize
-    fused_like = mode in ("fused", "ring_order")
+    fused_like = mode in ("fused", "ring_order", "hd_order")
     if w.collective == "allreduce":
         return 2 * n * size if fused_like else 5 * (n - 1) * size
     if w.collective == "reduce_scatter":
@@ -193,15 +193,79 @@ def run_suite(steps: int, torch, vrc, workloads) -> int:
     return 0
 
 
+def run_overlap(steps: int, mode: str, torch, vrc, workloads) -> int:
+    """Overlap of the all-reduce with compute on two streams (the pages'
+    compute/communication overlap: the collective runs on its own stream,
+    started and joined through events).  A bf16 8192^3 matmul stream stands
+    in for backward compute; the all-reduce is the headline workload.  Times
+    each alone and both together, each the median of `steps` repetitions.
+    One JSON line."""
+    dev = "cuda:0"
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    xs = workloads.make_inputs(w, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(8192, 8192, generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, generator=g, device=dev).to(torch.bfloat16)
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+    s_comp, s_comm = torch.cuda.Stream(), torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+
+    def timed(launch):
+        ms = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            s_comp.wait_event(e0)
+            s_comm.wait_event(e0)
+            launch()
+            cur.wait_event(s_comp.record_event())
+            cur.wait_event(s_comm.record_event())
+            e1.record(cur)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        return ms[len(ms) // 2]
+
+    def gemms(k):
+        with torch.cuda.stream(s_comp):
+            for _ in range(k):
+                torch.matmul(a, b, out=c)
+
+    def allreduce():
+        vrc.vrc_allreduce(xs, recv=ys, mode=mode, stream=s_comm)
+
+    gemms(3)
+    allreduce()
+    torch.cuda.synchronize()
+    t_one = timed(lambda: gemms(1))
+    t_ar = timed(allreduce)
+    k = max(1, round(t_ar / t_one))  # about as much compute as communication
+    t_gemm = timed(lambda: gemms(k))
+    t_both = timed(lambda: (gemms(k), allreduce()))
+    hidden = (t_gemm + t_ar - t_both) / min(t_gemm, t_ar)
+    flops = 2 * 8192**3 * k
+    out = {"overlap": {"mode": mode, "gemms": k, "gemm_shape": [8192, 8192, 8192], "gemm_ms": round(t_gemm, 4),
+                       "gemm_TFLOP_per_s": round(flops / (t_gemm * 1e-3) / 1e12, 1),
+                       "allreduce_ms": round(t_ar, 4), "both_ms": round(t_both, 4),
+                       "serial_ms": round(t_gemm + t_ar, 4), "fraction_of_shorter_hidden": round(hidden, 3),
+                       "workload": w.name}}
+    log(f"overlap: {out['overlap']}")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the 8 x 512 MiB bf16 all-reduce)")
-    ap.add_argument("--mode", default="fused", choices=["fused", "ring", "ring_chained", "ring_order"])
+    ap.add_argument("--mode", default="fused", choices=["fused", "ring", "ring_chained", "ring_order", "hd", "hd_order"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra ring-mode timing")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time the all-reduce alone, a matmul stream alone, and both on two streams")
     ap.add_argument("--suite", action="store_true",
                     help="measure every workload in every mode (one JSON line each) instead of the headline")
     ap.add_argument("--probe-copy", action="store_true",
@@ -225,6 +289,8 @@ def main() -> int:
         return 1
     if args.suite:
         return run_suite(args.steps, torch, vrc, workloads)
+    if args.overlap:
+        return run_overlap(args.steps, args.mode, torch, vrc, workloads)
     if args.probe_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
         dst = torch.empty_like(src)
@@ -274,7 +340,7 @@ def main() -> int:
             extra[f"{other}_mode"] = {
                 "steps": k2, "ms_per_step": round(wall2 * 1e3 / k2, 5),
                 "GB_per_s": round(nb2 / (wall2 / k2) / 1e9, 2), "alg_bytes_per_step": nb2,
-                "launches_per_step": 2 * (w.n - 1) if other == "ring" else 1,
+                "launches_per_step": {"ring": 2 * (w.n - 1), "hd": 2 * (w.n.bit_length() - 1)}.get(other, 1),
             }
             log(f"{other} mode: {extra[f'{other}_mode']}")
 
