@@ -122,6 +122,8 @@ def suite_bytes(w, mode: str) -> int:
     """Algorithmic bytes per call for a workload's collective and mode."""
     n, size = w.n, w.count * w.esize
     fused_like = mode in ("fused", "ring_order", "hd_order")
+    if w.collective == "reduce_scatter" and mode == "hd":
+        fused_like = True  # the stand-alone halving-doubling reduce-scatter runs as one butterfly launch
     if w.collective == "allreduce":
         return 2 * n * size if fused_like else 5 * (n - 1) * size
     if w.collective == "reduce_scatter":
