@@ -31,6 +31,22 @@ FLAGS = [
 ]
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c", "vrc_c_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c", "vrc_c_check")
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Build the plain-C user of the ABI (tests/c/vrc_c_check.c) against
+    libvrc.so and /opt/rocm's HIP runtime."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", INCLUDE,
+           "-o", C_CHECK_BIN, C_CHECK_SRC, "-L", PKG, "-lvrc", "-L", "/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../ring_all_reduce_virtual_amd", "-Wl,-rpath,/opt/rocm/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return C_CHECK_BIN
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
@@ -43,4 +59,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_check(verbose=True)
     sys.exit(0)
