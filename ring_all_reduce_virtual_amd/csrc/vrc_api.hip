@@ -14,8 +14,6 @@
 #include <atomic>
 #include <cstdint>
 #include <cstdlib>
-#include <cstring>
-#include <mutex>
 #include <type_traits>
 
 #include "vrc.h"

@@ -265,3 +265,29 @@ def test_errors_through_the_binding(vrc):
         vrc.vrc_all_gather(empty, mode=mode)
     torch.cuda.synchronize()
     assert vrc.lib().vrc_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("mode", ["fused", "ring", "ring_chained", "hd"])
+def test_more_than_2_to_31_elements_per_rank(vrc, orc, mode):
+    """64-bit indexing: 2^31 + 7 bf16 elements per rank (4 GiB), 2 ranks,
+    checked on sampled elements (chunk boundary, ends, beyond 2^31)."""
+    say(f"2^31+7 elements {mode}")
+    count = (1 << 31) + 7
+    g = torch.Generator(device=DEV).manual_seed(409)
+    xs = [torch.randint(-8, 9, (count,), generator=g, device=DEV, dtype=torch.int8).to(torch.bfloat16)
+          for _ in range(2)]
+    ys = vrc.vrc_allreduce(xs, mode=mode)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(409)
+    idx = np.unique(np.concatenate([
+        rng.integers(0, count, 200000), np.arange(0, 64), np.arange(count - 64, count),
+        np.arange((1 << 31) - 64, (1 << 31) + 7), np.arange(count // 2 - 64, count // 2 + 64)])).astype(np.int64)
+    tidx = torch.from_numpy(idx).to(DEV)
+    sx = [workloads.to_numpy(x[tidx]) for x in xs]
+    # small integers: every order gives the exact sum
+    want = (sx[0].astype(np.uint32) << 16).view(np.float32) + (sx[1].astype(np.uint32) << 16).view(np.float32)
+    for r in range(2):
+        got = (workloads.to_numpy(ys[r][tidx]).astype(np.uint32) << 16).view(np.float32)
+        assert np.array_equal(got, want), f"{mode} rank {r}"
+    del xs, ys
+    torch.cuda.empty_cache()
