@@ -183,6 +183,52 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
 vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nranks, size_t count,
                             size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_stream_t stream);
 
+/*
+ * Launch plan, host only: what a call would enqueue, without touching the
+ * GPU.  vrc_plan takes the arguments of the collective named by `coll`
+ * (`outer` is ignored for the all-reduce) and fills `ops` with one entry
+ * per operation, in launch order.  Ring and halving-doubling steps give one
+ * entry per rank operation of the step (VRC_OP_ADD: d = a + b, VRC_OP_COPY:
+ * d = a, over `rows` rows of `width` elements with the given row strides in
+ * elements; a, b and d point at element (0,0) of the operands inside the
+ * caller's buffers).  Single-launch kernels give one entry per launch with
+ * only `kind`, `launch` and width = count set.  Arguments are validated as
+ * in the real call.  If more than `cap` entries are needed the first `cap`
+ * are written, *n_ops receives the full count and VRC_ERR_INVALID_ARG is
+ * returned.  Used by the tests to check the schedules on the CPU, and for
+ * debugging.
+ */
+typedef enum { VRC_COLL_ALLREDUCE = 0, VRC_COLL_REDUCE_SCATTER = 1, VRC_COLL_ALL_GATHER = 2 } vrc_coll_t;
+
+typedef enum {
+    VRC_OP_ADD = 0,
+    VRC_OP_COPY = 1,
+    VRC_OP_FUSED_ALLREDUCE = 2,
+    VRC_OP_FUSED_REDUCE_SCATTER = 3,
+    VRC_OP_FUSED_ALL_GATHER = 4,
+    VRC_OP_CHAIN_ALLREDUCE = 5,      /* VRC_RING_CHAINED */
+    VRC_OP_CHAIN_REDUCE_SCATTER = 6,
+    VRC_OP_CHAIN_ALL_GATHER = 7,
+    VRC_OP_RING_ORDER_ALLREDUCE = 8, /* VRC_RING_ORDER */
+    VRC_OP_RING_ORDER_REDUCE_SCATTER = 9,
+    VRC_OP_BUTTERFLY_ALLREDUCE = 10, /* VRC_HD_ORDER */
+    VRC_OP_BUTTERFLY_REDUCE_SCATTER = 11
+} vrc_op_kind_t;
+
+typedef struct {
+    int launch;            /* index of the kernel launch this operation belongs to */
+    int kind;              /* vrc_op_kind_t */
+    const void* a;         /* first operand, element (0,0) */
+    const void* b;         /* second operand (VRC_OP_ADD only) */
+    void* d;               /* destination */
+    size_t rows, width;    /* elements */
+    size_t stride_a, stride_b, stride_d; /* row strides, elements (rows > 1) */
+} vrc_op_desc;
+
+vrc_status_t vrc_plan(vrc_coll_t coll, const void* const* send, void* const* recv, int nranks, size_t count,
+                      size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_op_desc* ops, int cap, int* n_ops,
+                      int* n_launches);
+
 /* Offset and length (elements) of chunk `chunk` of a flat buffer of `count`
  * elements split over `nranks` [REM].  Host-only; touches no GPU. */
 vrc_status_t vrc_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* length);

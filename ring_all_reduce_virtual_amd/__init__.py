@@ -46,6 +46,19 @@ class VrcError(RuntimeError):
         self.status = status
 
 
+class OpDesc(C.Structure):
+    """One operation of a launch plan (vrc_op_desc in include/vrc.h)."""
+    _fields_ = [("launch", C.c_int), ("kind", C.c_int), ("a", C.c_void_p), ("b", C.c_void_p), ("d", C.c_void_p),
+                ("rows", C.c_size_t), ("width", C.c_size_t), ("stride_a", C.c_size_t), ("stride_b", C.c_size_t),
+                ("stride_d", C.c_size_t)]
+
+
+COLL_ALLREDUCE, COLL_REDUCE_SCATTER, COLL_ALL_GATHER = 0, 1, 2
+OP_KINDS = {0: "add", 1: "copy", 2: "fused_allreduce", 3: "fused_reduce_scatter", 4: "fused_all_gather",
+            5: "chain_allreduce", 6: "chain_reduce_scatter", 7: "chain_all_gather", 8: "ring_order_allreduce",
+            9: "ring_order_reduce_scatter", 10: "butterfly_allreduce", 11: "butterfly_reduce_scatter"}
+
+
 def _load():
     # PyTorch-ROCm ships its own HIP runtime.  Import it first so that
     # libvrc.so binds to that same runtime (the dynamic linker reuses an
@@ -69,6 +82,8 @@ def _load():
     L.vrc_reduce_scatter.restype = i
     L.vrc_all_gather.argtypes = [ptrs, ptrs, i, sz, sz, i, i, vp]
     L.vrc_all_gather.restype = i
+    L.vrc_plan.argtypes = [i, ptrs, ptrs, i, sz, sz, i, i, C.POINTER(OpDesc), i, C.POINTER(i), C.POINTER(i)]
+    L.vrc_plan.restype = i
     L.vrc_chunk_range.argtypes = [sz, i, i, C.POINTER(sz), C.POINTER(sz)]
     L.vrc_chunk_range.restype = i
     L.vrc_status_string.argtypes = [i]
@@ -111,6 +126,25 @@ def raw_reduce_scatter(send, recv, count, outer, dtype, mode, stream=0, op=VRC_S
 def raw_all_gather(send, recv, count, outer, dtype, mode, stream=0) -> int:
     return _lib.vrc_all_gather(_ptr_array(send), _ptr_array(recv), len(send), count, outer, dtype, mode,
                                stream or None)
+
+
+def plan(coll: int, send, recv, count: int, outer: int, dtype: int, mode: int):
+    """The operations a call would enqueue (host only, nothing launched):
+    a list of dicts with launch, kind, a, b, d, rows, width and strides."""
+    cap = 4096
+    ops = (OpDesc * cap)()
+    n_ops, n_launches = C.c_int(), C.c_int()
+    st = _lib.vrc_plan(coll, _ptr_array(send), _ptr_array(recv), len(send), count, outer, dtype, mode, ops, cap,
+                       C.byref(n_ops), C.byref(n_launches))
+    if st != VRC_OK:
+        raise VrcError(st, "vrc_plan")
+    out = []
+    for k in range(n_ops.value):
+        o = ops[k]
+        out.append({"launch": o.launch, "kind": OP_KINDS[o.kind], "a": o.a or 0, "b": o.b or 0, "d": o.d or 0,
+                    "rows": o.rows, "width": o.width, "stride_a": o.stride_a, "stride_b": o.stride_b,
+                    "stride_d": o.stride_d})
+    return out, n_launches.value
 
 
 def chunk_range(count: int, nranks: int, chunk: int) -> tuple[int, int]:
@@ -272,6 +306,7 @@ def _prod(shape) -> int:
 
 
 __all__ = [
+    "plan", "OpDesc", "OP_KINDS", "COLL_ALLREDUCE", "COLL_REDUCE_SCATTER", "COLL_ALL_GATHER",
     "vrc_allreduce", "vrc_reduce_scatter", "vrc_all_gather", "reduce_scatter_shape", "chunk_range",
     "version", "raw_allreduce", "raw_reduce_scatter", "raw_all_gather", "lib", "VrcError",
     "VRC_INT32", "VRC_FP32", "VRC_FP16", "VRC_BF16", "VRC_SUM", "VRC_RING", "VRC_FUSED", "VRC_RING_CHAINED",

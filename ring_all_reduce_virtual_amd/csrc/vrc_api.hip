@@ -27,6 +27,34 @@ using vrc::RowSplit;
 
 thread_local int g_last_hip_error = 0;
 
+// When set (by vrc_plan on this thread), launches are recorded here instead
+// of being enqueued.
+struct Plan {
+    vrc_op_desc* ops;
+    int cap;
+    int n;
+    int launches;
+};
+thread_local Plan* g_plan = nullptr;
+
+void plan_op(const vrc_op_desc& op)
+{
+    if (g_plan->n < g_plan->cap) g_plan->ops[g_plan->n] = op;
+    g_plan->n++;
+}
+
+// A single-launch kernel: one entry with only its kind and size.
+vrc_status_t plan_single(vrc_op_kind_t kind, uint64_t count)
+{
+    vrc_op_desc op = {};
+    op.launch = g_plan->launches++;
+    op.kind = kind;
+    op.rows = 1;
+    op.width = count;
+    plan_op(op);
+    return VRC_OK;
+}
+
 // ----------------------------------------------------------------------------
 // Device facts and launch tuning
 // ----------------------------------------------------------------------------
@@ -251,6 +279,25 @@ struct Launch {
     template <bool ADD>
     static vrc_status_t step(const vrc::StepArgs& args, int nops, uint64_t work, int cus, hipStream_t st)
     {
+        if (g_plan) {
+            for (int i = 0; i < nops; i++) {
+                const vrc::StepOp& o = args.op[i];
+                vrc_op_desc op = {};
+                op.launch = g_plan->launches;
+                op.kind = ADD ? VRC_OP_ADD : VRC_OP_COPY;
+                op.a = o.a;
+                op.b = ADD ? o.b : nullptr;
+                op.d = o.d;
+                op.rows = o.rows;
+                op.width = o.width;
+                op.stride_a = o.sa;
+                op.stride_b = ADD ? o.sb : 0;
+                op.stride_d = o.sd;
+                plan_op(op);
+            }
+            g_plan->launches++;
+            return VRC_OK;
+        }
         const int bpc = step_blocks_per_cu(step_bytes<ADD>(args, nops));
         const dim3 grid(grid_x(cus, work, nops, bpc), (unsigned)nops);
         hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true>), grid, dim3(kBlock), 0, st, args);
@@ -418,6 +465,10 @@ struct Launch {
                                         hipStream_t st)
     {
         if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        if (g_plan)
+            return plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_ALLREDUCE
+                                                                          : VRC_OP_FUSED_ALLREDUCE,
+                               count);
         vrc::FusedArArgs a;
         uintptr_t addr[2 * kMaxRanks];
         for (int r = 0; r < n; r++) {
@@ -465,6 +516,10 @@ struct Launch {
                                              uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        if (g_plan)
+            return plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_REDUCE_SCATTER
+                                                                          : VRC_OP_FUSED_REDUCE_SCATTER,
+                               count);
         vrc::FusedRsArgs a;
         uint64_t work = 0;
         for (int r = 0; r < kMaxRanks; r++) a.src[r] = r < n ? x[r] : nullptr;
@@ -509,6 +564,7 @@ struct Launch {
     static vrc_status_t fused_all_gather(const char* const* x, char* const* y, int n, uint64_t count,
                                          uint64_t outer, int cus, hipStream_t st)
     {
+        if (g_plan) return plan_single(VRC_OP_FUSED_ALL_GATHER, count);
         vrc::FusedAgArgs a;
         const uint64_t row = count / outer;
         a.rows = outer;
@@ -659,6 +715,7 @@ struct Launch {
                                         hipStream_t st)
     {
         if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        if (g_plan) return plan_single(MEM ? VRC_OP_CHAIN_ALLREDUCE : VRC_OP_RING_ORDER_ALLREDUCE, count);
         vrc::ChainArgs a;
         uint64_t work = 0;
         for (int r = 0; r < kMaxRanks; r++) {
@@ -695,6 +752,8 @@ struct Launch {
                                              uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        if (g_plan)
+            return plan_single(MEM ? VRC_OP_CHAIN_REDUCE_SCATTER : VRC_OP_RING_ORDER_REDUCE_SCATTER, count);
         vrc::ChainArgs a;
         uint64_t work = 0;
         for (int r = 0; r < kMaxRanks; r++) {
@@ -729,6 +788,7 @@ struct Launch {
                                          uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        if (g_plan) return plan_single(VRC_OP_CHAIN_ALL_GATHER, count);
         vrc::FusedAgArgs a;
         const uint64_t row = count / outer;
         a.rows = outer;
@@ -805,10 +865,12 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
 vrc_status_t run(Coll coll, vrc_mode_t mode, vrc_dtype_t dt, const void* const* send, void* const* recv, int n,
                  uint64_t count, uint64_t outer, hipStream_t st)
 {
-    int cus = 0;
-    hipError_t e = cu_count(&cus);
-    if (e != hipSuccess) return hip_fail(e);
-    (void)hipGetLastError();  // start from a clean per-thread error state
+    int cus = 256;  // a plan launches nothing and needs no device
+    if (!g_plan) {
+        hipError_t e = cu_count(&cus);
+        if (e != hipSuccess) return hip_fail(e);
+        (void)hipGetLastError();  // start from a clean per-thread error state
+    }
     const char* x[kMaxRanks];
     char* y[kMaxRanks];
     for (int r = 0; r < n; r++) {
@@ -843,6 +905,28 @@ bool ranks_ok_for(vrc_mode_t m, int n)
 // C ABI
 // ============================================================================
 extern "C" {
+
+vrc_status_t vrc_plan(vrc_coll_t coll, const void* const* send, void* const* recv, int nranks, size_t count,
+                      size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_op_desc* ops, int cap, int* n_ops,
+                      int* n_launches)
+{
+    if (!n_ops || !n_launches || cap < 0 || (cap > 0 && !ops)) return VRC_ERR_INVALID_ARG;
+    Plan plan = {ops, cap, 0, 0};
+    g_plan = &plan;
+    vrc_status_t rc = VRC_ERR_UNSUPPORTED;
+    switch (coll) {
+    case VRC_COLL_ALLREDUCE: rc = vrc_allreduce(send, recv, nranks, count, dtype, VRC_SUM, mode, nullptr); break;
+    case VRC_COLL_REDUCE_SCATTER:
+        rc = vrc_reduce_scatter(send, recv, nranks, count, outer, dtype, VRC_SUM, mode, nullptr);
+        break;
+    case VRC_COLL_ALL_GATHER: rc = vrc_all_gather(send, recv, nranks, count, outer, dtype, mode, nullptr); break;
+    }
+    g_plan = nullptr;
+    *n_ops = plan.n;
+    *n_launches = plan.launches;
+    if (rc == VRC_OK && plan.n > cap) return VRC_ERR_INVALID_ARG;
+    return rc;
+}
 
 vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
                            vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, vrc_stream_t stream)
