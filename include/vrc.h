@@ -55,7 +55,8 @@
  *               output).  The arrays are read during the call only; the
  *               buffers stay owned by the caller.  The library allocates no
  *               memory and keeps no pointer after returning.
- *   count       Elements per rank INPUT buffer.
+ *   count       Elements per rank INPUT buffer, at most 2^56 (larger values,
+ *               whose byte sizes could wrap, return VRC_ERR_INVALID_ARG).
  *   stream      A hipStream_t (NULL = the null stream) on the current device.
  *               Work is enqueued asynchronously; the call returns before it
  *               finishes.  Errors raised by running kernels surface at the

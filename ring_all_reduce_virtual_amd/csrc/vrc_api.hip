@@ -251,10 +251,15 @@ vrc_status_t check_buffers(const void* const* send, void* const* recv, int n, ui
     return VRC_OK;
 }
 
-vrc_status_t check_common(const void* const* send, void* const* recv, int n, vrc_dtype_t dtype)
+// Counts above 2^56 elements are rejected: every byte size computed from
+// them (at most count * 16 ranks * 4 bytes) then fits in 64 bits.
+constexpr uint64_t kMaxCount = 1ull << 56;
+
+vrc_status_t check_common(const void* const* send, void* const* recv, int n, uint64_t count, vrc_dtype_t dtype)
 {
     if (!send || !recv) return VRC_ERR_INVALID_ARG;
     if (n < 1 || n > kMaxRanks) return VRC_ERR_INVALID_ARG;
+    if (count > kMaxCount) return VRC_ERR_INVALID_ARG;
     if (esize(dtype) == 0) return VRC_ERR_UNSUPPORTED;
     return VRC_OK;
 }
@@ -931,7 +936,7 @@ vrc_status_t vrc_plan(vrc_coll_t coll, const void* const* send, void* const* rec
 vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
                            vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, vrc_stream_t stream)
 {
-    vrc_status_t rc = check_common(send, recv, nranks, dtype);
+    vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
     if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
@@ -948,7 +953,7 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
                                 size_t outer, vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode,
                                 vrc_stream_t stream)
 {
-    vrc_status_t rc = check_common(send, recv, nranks, dtype);
+    vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
     if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
@@ -974,7 +979,7 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
 vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nranks, size_t count,
                             size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_stream_t stream)
 {
-    vrc_status_t rc = check_common(send, recv, nranks, dtype);
+    vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
     if (!mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;

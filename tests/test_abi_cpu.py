@@ -87,6 +87,11 @@ def test_invalid_arguments_return_before_any_gpu_call():
     assert vrc.raw_reduce_scatter(x, y, 1000, 0, vrc.VRC_FP16, vrc.VRC_RING) == vrc.VRC_ERR_INVALID_ARG
     assert vrc.raw_all_gather(x, y, 1000, 3, vrc.VRC_FP16, vrc.VRC_RING) == vrc.VRC_ERR_INVALID_ARG
     assert vrc.raw_all_gather(x, y, 1000, 0, vrc.VRC_FP16, vrc.VRC_RING) == vrc.VRC_ERR_INVALID_ARG
+    # counts whose byte sizes could wrap 64 bits (2^62 int32 all-gathered over 4 ranks is 2^66 bytes)
+    huge = 1 << 62
+    assert vrc.raw_allreduce(x, y, huge, vrc.VRC_FP32, vrc.VRC_FUSED) == vrc.VRC_ERR_INVALID_ARG
+    assert vrc.raw_all_gather(x, y, huge, 1, vrc.VRC_INT32, vrc.VRC_RING) == vrc.VRC_ERR_INVALID_ARG
+    assert vrc.raw_reduce_scatter(x, y, huge, 1, vrc.VRC_FP32, vrc.VRC_RING) == vrc.VRC_ERR_INVALID_ARG
     assert vrc.lib().vrc_last_hip_error() == 0
 
 
