@@ -364,6 +364,21 @@ def main() -> int:
             }
             log(f"{other} mode: {extra[f'{other}_mode']}")
 
+        # The same bytes moved by the runtime's own device copy, on the same buffers in the same process:
+        # how close the kernel comes to what this machine's HBM gives a plain N-in/N-out stream.
+        def copy_step():
+            for x, y in zip(xs, ys):
+                y.copy_(x)
+
+        k3 = max(3, min(args.steps, 10))
+        wall3, kms3 = time_calls(copy_step, k3, 2, torch)
+        copy_gbs = 2 * w.n * size / (sum(kms3) / len(kms3) * 1e-3) / 1e9
+        extra["same_box_copy"] = {"what": f"torch copy_ of each rank's input into its output ({w.n} launches, "
+                                          f"2*N*S bytes)", "ms_per_step": round(wall3 * 1e3 / k3, 5),
+                                  "GB_per_s": round(copy_gbs, 2),
+                                  "kernel_over_copy": round(achieved / copy_gbs, 4)}
+        log(f"same-box copy: {extra['same_box_copy']}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a slice of the inputs")
