@@ -721,12 +721,13 @@ struct Launch {
     {
         if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
         if (g_plan) return plan_single(MEM ? VRC_OP_CHAIN_ALLREDUCE : VRC_OP_RING_ORDER_ALLREDUCE, count);
-        vrc::ChainArgs a;
-        uint64_t work = 0;
+        vrc::ChainArgs a = {};
         for (int r = 0; r < kMaxRanks; r++) {
             a.src[r] = r < n ? x[r] : nullptr;
             a.dst[r] = r < n ? y[r] : nullptr;
         }
+        // Tiles of one 16-byte vector per lane of a 64-lane wave, per chunk.
+        a.tile0[0] = 0;
         for (int c = 0; c < n; c++) {
             uint64_t off, len;
             chunk_range(count, n, c, &off, &len);
@@ -736,12 +737,14 @@ struct Launch {
                 addr[2 * r + 1] = (uintptr_t)(y[r] + off * E);
             }
             a.ch[c] = {off, 1, len, 0, split_rows(addr, 2 * n, 1, nullptr, 0, len, E)};
-            const uint64_t w = a.ch[c].g.nvb + a.ch[c].g.head + a.ch[c].g.tail;
-            if (w > work) work = w;
+            a.tile0[c + 1] = a.tile0[c] + (a.ch[c].g.nvb + 63) / 64;
         }
+        // At least one wave per chunk for the scalar head/tail pass.
+        const uint64_t lanes = a.tile0[n] * 64, scalar_lanes = (uint64_t)n * 64;
+        const uint64_t work = lanes > scalar_lanes ? lanes : scalar_lanes;
         const uint64_t bytes = MEM ? 5 * (uint64_t)(n - 1) * count * E : 2 * (uint64_t)n * count * E;
         const int bpc = MEM ? chain_blocks_per_cu(bytes) : fused_blocks_per_cu(bytes);
-        const dim3 grid(grid_x(cus, work, n, bpc), (unsigned)n);
+        const dim3 grid(grid_x(cus, work, 1, bpc));
         switch (n) {
 #define VRC_CASE(K) \
     case K: hipLaunchKernelGGL((vrc::k_ring_chain_allreduce<T, K, MEM, true>), grid, dim3(kBlock), 0, st, a); break;
@@ -759,7 +762,7 @@ struct Launch {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
         if (g_plan)
             return plan_single(MEM ? VRC_OP_CHAIN_REDUCE_SCATTER : VRC_OP_RING_ORDER_REDUCE_SCATTER, count);
-        vrc::ChainArgs a;
+        vrc::ChainArgs a = {};
         uint64_t work = 0;
         for (int r = 0; r < kMaxRanks; r++) {
             a.src[r] = r < n ? x[r] : nullptr;

@@ -16,21 +16,37 @@ namespace vrc {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Every buffer the library is given is device (global) memory.  Accessing it
+// through global address-space pointers gives global_load/global_store
+// instructions even where the compiler cannot trace a pointer back to a
+// kernel argument (flat instructions would also count against the LDS
+// counter).
+template <class X>
+using global_ptr = __attribute__((address_space(1))) X*;
+
 // 16-byte load/store, optionally with the non-temporal hint (streaming data
 // that is never re-read should not displace other lines from the caches).
 template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const char* p)
 {
-    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    else return *reinterpret_cast<const u32x4*>(p);
+    const auto g = (global_ptr<const u32x4>)p;
+    if constexpr (NT) return __builtin_nontemporal_load(g);
+    else return *g;
 }
 
 template <bool NT>
 __device__ __forceinline__ void st16(char* p, u32x4 v)
 {
-    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-    else *reinterpret_cast<u32x4*>(p) = v;
+    const auto g = (global_ptr<u32x4>)p;
+    if constexpr (NT) __builtin_nontemporal_store(v, g);
+    else *g = v;
 }
+
+// Compiler barrier.  A load after it is issued even when this lane has just
+// stored the value it reads (the compiler would otherwise reuse the stored
+// register): the memory-faithful ring chains read every partial back from
+// the buffer the previous step wrote it to.
+__device__ __forceinline__ void reload_fence() { __asm__ __volatile__("" ::: "memory"); }
 
 struct I32 {
     using S = uint32_t;  // stored bits
@@ -125,13 +141,13 @@ struct BF16 {
 template <class T>
 __device__ __forceinline__ typename T::S load_s(const char* p)
 {
-    return *reinterpret_cast<const typename T::S*>(p);
+    return *(global_ptr<const typename T::S>)p;
 }
 
 template <class T>
 __device__ __forceinline__ void store_s(char* p, typename T::S v)
 {
-    *reinterpret_cast<typename T::S*>(p) = v;
+    *(global_ptr<typename T::S>)p = v;
 }
 
 // One ring-step element: round(widen(a) + widen(b)) in the storage type.
