@@ -96,11 +96,13 @@ typedef enum { VRC_SUM = 0 } vrc_op_t;
  *                     all-reduce, N-1 for either half.
  *   VRC_FUSED         one launch; every input read once, every output
  *                     written once.
- *   VRC_RING_CHAINED  one launch running the same per-step reads and writes
- *                     as VRC_RING: each element of chunk c walks its chunk's
+ *   VRC_RING_CHAINED  one launch issuing the per-step reads and writes of
+ *                     VRC_RING: each element of chunk c walks its chunk's
  *                     ring steps through the rank buffers (every element's
  *                     steps depend only on that element, so no grid-wide
- *                     barrier is needed).
+ *                     barrier is needed).  A partial is read back right
+ *                     after it is stored, so the cache serves most of those
+ *                     reads.
  *   VRC_RING_ORDER    one launch with the fused traffic (read N, write N):
  *                     the ring's partials stay in registers.  For the
  *                     all-gather it equals VRC_FUSED.
