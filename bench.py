@@ -128,6 +128,8 @@ def suite_bytes(w, mode: str) -> int:
         return 2 * n * size if fused_like else 5 * (n - 1) * size
     if w.collective == "reduce_scatter":
         return (n + 1) * size if fused_like else 3 * (n - 1) * size
+    if mode == "ring_chained":
+        return (2 * n - 1) * n * size  # one input read, N-2 relay reads and N writes per input element
     return n * size + n * n * size if fused_like else 2 * n * n * size
 
 
