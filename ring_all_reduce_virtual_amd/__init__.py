@@ -197,13 +197,25 @@ def _mode(mode) -> int:
     return MODES[mode]
 
 
-def _stream(stream) -> int:
+def _stream(stream, device) -> int:
+    """The HIP stream to enqueue on: the given one, else the current stream
+    of the tensors' device (which must be the current device, since the
+    library launches on the current device)."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
+    if device.index is not None and device.index != torch.cuda.current_device():
+        raise ValueError(f"tensors live on {device} but the current device is cuda:{torch.cuda.current_device()}; "
+                         "call inside torch.cuda.device(...)")
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return s.cuda_stream
 
 
-def _outer(shape, dim) -> int:
+def _same_device(send, recv, what):
+    if recv[0].device != send[0].device:
+        raise ValueError(f"{what}: outputs must be on the inputs' device {send[0].device}")
+
+
+def _outer(shape, dim) -> tuple[int, int]:
+    """(product of the sizes before `dim`, `dim` made non-negative)."""
     nd = len(shape)
     if nd == 0:
         raise ValueError("tensors need at least one dimension")
@@ -226,8 +238,9 @@ def vrc_allreduce(send, recv=None, mode: str = "fused", stream=None):
     _check_ranks(recv, "vrc_allreduce")
     if len(recv) != len(send) or recv[0].shape != send[0].shape or recv[0].dtype != send[0].dtype:
         raise ValueError("vrc_allreduce: recv must match send")
+    _same_device(send, recv, "vrc_allreduce")
     st = raw_allreduce([t.data_ptr() for t in send], [t.data_ptr() for t in recv], send[0].numel(),
-                       _dtype_code(send[0]), _mode(mode), _stream(stream))
+                       _dtype_code(send[0]), _mode(mode), _stream(stream, send[0].device))
     if st != VRC_OK:
         raise VrcError(st, "vrc_allreduce")
     return recv
@@ -269,8 +282,10 @@ def vrc_reduce_scatter(send, recv=None, dim: int = 0, mode: str = "fused", strea
     for c, t in enumerate(recv):
         if t.numel() != _prod(shapes[c]) or t.dtype != send[0].dtype or not t.is_contiguous():
             raise ValueError(f"vrc_reduce_scatter: output {c} must be contiguous {shapes[c]} {send[0].dtype}")
+        if t.device != send[0].device:
+            raise ValueError(f"vrc_reduce_scatter: outputs must be on the inputs' device {send[0].device}")
     st = raw_reduce_scatter([t.data_ptr() for t in send], [t.data_ptr() for t in recv], send[0].numel(),
-                            outer, _dtype_code(send[0]), _mode(mode), _stream(stream))
+                            outer, _dtype_code(send[0]), _mode(mode), _stream(stream, send[0].device))
     if st != VRC_OK:
         raise VrcError(st, "vrc_reduce_scatter")
     return recv
@@ -291,8 +306,10 @@ def vrc_all_gather(send, recv=None, dim: int = 0, mode: str = "fused", stream=No
     for t in recv:
         if list(t.shape) != out_shape or t.dtype != send[0].dtype or not t.is_contiguous():
             raise ValueError(f"vrc_all_gather: outputs must be contiguous {out_shape} {send[0].dtype}")
+        if t.device != send[0].device:
+            raise ValueError(f"vrc_all_gather: outputs must be on the inputs' device {send[0].device}")
     st = raw_all_gather([t.data_ptr() for t in send], [t.data_ptr() for t in recv], send[0].numel(), outer,
-                        _dtype_code(send[0]), _mode(mode), _stream(stream))
+                        _dtype_code(send[0]), _mode(mode), _stream(stream, send[0].device))
     if st != VRC_OK:
         raise VrcError(st, "vrc_all_gather")
     return recv
