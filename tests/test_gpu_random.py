@@ -1,0 +1,133 @@
+"""Seeded random sweep: every collective, mode and dtype on random rank
+counts (1-16), shapes, split dimensions, ragged sizes, element offsets that
+misalign the buffers (equal or different per rank) and in-place all-reduce,
+compared bit for bit with the oracle.  Each case draws from its own seed, so
+a failure names a reproducible case."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity_util import assert_bitwise, host
+from tests.test_gpu_parity import DTYPES, HD_FAMILY, MODES, want_ar, want_rs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+CASES = 120
+
+
+@pytest.fixture(scope="module")
+def vrc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_all_reduce_virtual_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def draw(kind: int, k: int):
+    rng = np.random.default_rng(7919 * kind + k)
+    dtype = str(rng.choice(DTYPES))
+    mode = str(rng.choice(MODES))
+    n = int(2 ** rng.integers(0, 5)) if mode in HD_FAMILY else int(rng.integers(1, 17))
+    return rng, dtype, mode, n
+
+
+def log_uniform(rng, hi: int) -> int:
+    return int(np.exp(rng.uniform(0.0, np.log(hi + 1)))) - 1
+
+
+def offsets(rng, n: int):
+    how = rng.integers(0, 3)
+    if how == 0:
+        return [0] * n
+    if how == 1:
+        return [int(rng.integers(1, 8))] * n
+    return [int(v) for v in rng.integers(0, 8, n)]
+
+
+def place(t: torch.Tensor, off: int) -> torch.Tensor:
+    """A contiguous copy of t starting `off` elements into a fresh allocation."""
+    base = torch.empty(t.numel() + off, dtype=t.dtype, device=t.device)
+    v = base[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def empty_at(shape, dtype, off: int) -> torch.Tensor:
+    numel = int(np.prod(shape)) if len(shape) else 1
+    base = torch.empty(numel + off, dtype=dtype, device=DEV)
+    return base[off:off + numel].view(shape)
+
+
+def ranks(rng, n, shape, dtype, seed):
+    xs = workloads.random_ranks(n, shape, dtype, seed=seed, device=DEV)
+    return [place(x, o) for x, o in zip(xs, offsets(rng, n))]
+
+
+@pytest.mark.parametrize("k", range(CASES))
+def test_random_allreduce(vrc, orc, k):
+    rng, dtype, mode, n = draw(1, k)
+    count = log_uniform(rng, 70000)
+    xs = ranks(rng, n, (count,), dtype, seed=10000 + k)
+    in_place = rng.random() < 0.25
+    print(f"random allreduce case {k}: {mode} {dtype} n={n} count={count} in_place={in_place}", flush=True)
+    hx = host(xs)
+    if in_place:
+        ys = xs
+    else:
+        ys = [empty_at((count,), xs[0].dtype, o) for o in offsets(rng, n)]
+    vrc.vrc_allreduce(xs, recv=ys, mode=mode)
+    torch.cuda.synchronize()
+    want = want_ar(orc, hx, dtype, mode)
+    for r, y in enumerate(host(ys)):
+        assert_bitwise(y, want[r], f"case {k} {mode} {dtype} n={n} count={count} rank {r}")
+
+
+@pytest.mark.parametrize("k", range(CASES))
+def test_random_reduce_scatter(vrc, orc, k):
+    rng, dtype, mode, n = draw(2, k)
+    if rng.random() < 0.5:
+        shape, dim, outer = (log_uniform(rng, 70000),), 0, 1
+    else:
+        nd = int(rng.integers(2, 4))
+        dim = int(rng.integers(1, nd))
+        shape = [int(rng.integers(2, 9)) for _ in range(nd)]
+        shape[dim] = n * int(rng.integers(1, 200))
+        shape = tuple(shape)
+        outer = int(np.prod(shape[:dim]))
+    xs = ranks(rng, n, shape, dtype, seed=20000 + k)
+    print(f"random reduce_scatter case {k}: {mode} {dtype} n={n} shape={shape} dim={dim}", flush=True)
+    shapes = vrc.reduce_scatter_shape(shape, n, dim)
+    ys = [empty_at(shapes[c], xs[0].dtype, o) for c, o in enumerate(offsets(rng, n))]
+    hx = host(xs)
+    vrc.vrc_reduce_scatter(xs, recv=ys, dim=dim, mode=mode)
+    torch.cuda.synchronize()
+    want = want_rs(orc, hx, dtype, mode, outer)
+    for c, y in enumerate(host(ys)):
+        assert_bitwise(y, want[c], f"case {k} {mode} {dtype} n={n} shape={shape} dim={dim} chunk {c}")
+
+
+@pytest.mark.parametrize("k", range(CASES))
+def test_random_all_gather(vrc, orc, k):
+    rng, dtype, mode, n = draw(3, k)
+    nd = int(rng.integers(1, 4))
+    shape = tuple(int(rng.integers(1, 9)) for _ in range(nd - 1)) + (log_uniform(rng, 800) + 1,)
+    dim = int(rng.integers(0, nd))
+    outer = int(np.prod(shape[:dim])) if dim else 1
+    xs = ranks(rng, n, shape, dtype, seed=30000 + k)
+    print(f"random all_gather case {k}: {mode} {dtype} n={n} shape={shape} dim={dim}", flush=True)
+    out_shape = list(shape)
+    out_shape[dim] *= n
+    ys = [empty_at(tuple(out_shape), xs[0].dtype, o) for o in offsets(rng, n)]
+    hx = host(xs)
+    vrc.vrc_all_gather(xs, recv=ys, dim=dim, mode=mode)
+    torch.cuda.synchronize()
+    want = orc.ring_all_gather(hx, dtype, outer=outer)
+    for r, y in enumerate(host(ys)):
+        assert_bitwise(y, want[r], f"case {k} {mode} {dtype} n={n} shape={shape} dim={dim} rank {r}")
