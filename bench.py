@@ -54,6 +54,7 @@ def alg_bytes(mode: str, n: int, size_bytes: int) -> int:
     N inputs and write N outputs.  Ring and ring-chained: N-1 reduce-scatter
     steps read two chunks and write one per rank (3S per step), N-1
     all-gather steps read and write one chunk per rank (2S per step)."""
+    mode = selected(mode, n, size_bytes)
     if mode in ("fused", "ring_order", "hd_order"):
         return 2 * n * size_bytes
     return 5 * (n - 1) * size_bytes
@@ -118,9 +119,17 @@ def cpu_baseline(xs, w, mode: str):
     }
 
 
+def selected(mode: str, n: int, size: int) -> str:
+    """The algorithm VRC_SELECT runs (the rule stated in include/vrc.h)."""
+    if mode != "select":
+        return mode
+    return "hd" if n & (n - 1) == 0 and size <= (64 << 20) else "ring"
+
+
 def suite_bytes(w, mode: str) -> int:
     """Algorithmic bytes per call for a workload's collective and mode."""
     n, size = w.n, w.count * w.esize
+    mode = selected(mode, n, size)
     fused_like = mode in ("fused", "ring_order", "hd_order")
     if w.collective == "reduce_scatter" and mode == "hd":
         fused_like = True  # the stand-alone halving-doubling reduce-scatter runs as one butterfly launch
@@ -287,7 +296,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the 8 x 512 MiB bf16 all-reduce)")
-    ap.add_argument("--mode", default="fused", choices=["fused", "ring", "ring_chained", "ring_order", "hd", "hd_order"])
+    ap.add_argument("--mode", default="fused",
+                    choices=["fused", "ring", "ring_chained", "ring_order", "hd", "hd_order", "select"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the extra ring-mode timing")
     ap.add_argument("--overlap", action="store_true",
@@ -366,7 +376,8 @@ def main() -> int:
             extra[f"{other}_mode"] = {
                 "steps": k2, "ms_per_step": round(wall2 * 1e3 / k2, 5),
                 "GB_per_s": round(nb2 / (wall2 / k2) / 1e9, 2), "alg_bytes_per_step": nb2,
-                "launches_per_step": {"ring": 2 * (w.n - 1), "hd": 2 * (w.n.bit_length() - 1)}.get(other, 1),
+                "launches_per_step": {"ring": 2 * (w.n - 1), "hd": 2 * (w.n.bit_length() - 1)}.get(
+                    selected(other, w.n, size), 1),
             }
             if other == "ring_chained":
                 extra[f"{other}_mode"]["note"] = "bytes issued; L2 serves the partial re-reads"

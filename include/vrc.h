@@ -120,14 +120,26 @@ typedef enum { VRC_SUM = 0 } vrc_op_t;
  *                     partials each rank holds after its first step (the
  *                     library allocates nothing), so it runs as VRC_HD_ORDER.
  *   VRC_HD_ORDER      one launch with the fused traffic, partials in
- *                     registers.  For the all-gather it equals VRC_FUSED. */
+ *                     registers.  For the all-gather it equals VRC_FUSED.
+ * Size-based selection between the two step-by-step algorithms [TP]:
+ *   VRC_SELECT        VRC_HD when nranks is a power of two and each rank's
+ *                     input holds at most VRC_SELECT_HD_MAX_BYTES, else
+ *                     VRC_RING.  The bits are those of the algorithm chosen
+ *                     (vrc_plan shows which: 2 log2 N or 2(N-1) launches for
+ *                     the all-reduce).  Any nranks is accepted.  The limit
+ *                     is where the ring's fewer, larger launches overtake
+ *                     halving-doubling's log2 N steps on MI355X (8 ranks:
+ *                     halving-doubling 8 % faster at 16 MiB, the ring 3 %
+ *                     faster at 128 MiB per rank). */
+#define VRC_SELECT_HD_MAX_BYTES (64ull << 20)
 typedef enum {
     VRC_RING = 0,
     VRC_FUSED = 1,
     VRC_RING_CHAINED = 2,
     VRC_RING_ORDER = 3,
     VRC_HD = 4,
-    VRC_HD_ORDER = 5
+    VRC_HD_ORDER = 5,
+    VRC_SELECT = 6
 } vrc_mode_t;
 
 typedef enum {

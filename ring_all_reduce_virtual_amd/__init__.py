@@ -15,7 +15,9 @@ and per all-gather step), ``"fused"`` the single-launch N-way kernel,
 ``"ring_order"`` one launch with fused traffic but the ring's summation order
 (the three ring modes return the same bits), ``"hd"`` halving-doubling with
 one launch per step and ``"hd_order"`` halving-doubling in one launch (both
-need a power-of-two rank count and return the same bits).
+need a power-of-two rank count and return the same bits); ``"select"`` picks
+``"hd"`` for power-of-two rank counts with at most 64 MiB per rank and
+``"ring"`` otherwise, and returns the bits of the one it picks.
 """
 from __future__ import annotations
 
@@ -27,12 +29,13 @@ LIB_PATH = os.path.join(PKG, "libvrc.so")
 
 VRC_INT32, VRC_FP32, VRC_FP16, VRC_BF16 = 0, 1, 2, 3
 VRC_SUM = 0
-VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER = 0, 1, 2, 3, 4, 5
+VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER, VRC_SELECT = 0, 1, 2, 3, 4, 5, 6
+SELECT_HD_MAX_BYTES = 64 << 20  # VRC_SELECT_HD_MAX_BYTES of include/vrc.h
 VRC_OK, VRC_ERR_INVALID_ARG, VRC_ERR_UNSUPPORTED, VRC_ERR_ALIAS, VRC_ERR_HIP = range(5)
 MAX_RANKS = 16
 
 MODES = {"ring": VRC_RING, "fused": VRC_FUSED, "ring_chained": VRC_RING_CHAINED, "ring_order": VRC_RING_ORDER,
-         "hd": VRC_HD, "hd_order": VRC_HD_ORDER}
+         "hd": VRC_HD, "hd_order": VRC_HD_ORDER, "select": VRC_SELECT}
 RING_MODES = ("ring", "ring_chained", "ring_order")  # same bits as the per-step ring
 HD_MODES = ("hd", "hd_order")  # halving-doubling; nranks must be a power of two
 

@@ -869,6 +869,7 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
         case VRC_RING_ORDER: return L::template chain_allreduce<false>(x, y, n, count, cus, st);
         case VRC_HD: return L::hd_allreduce(x, y, n, count, cus, st);
         case VRC_HD_ORDER: return L::template fused_allreduce<vrc::Butterfly>(x, y, n, count, cus, st);
+        case VRC_SELECT: break;  // resolved to VRC_HD or VRC_RING by the entry point
         }
         break;
     case Coll::RS:
@@ -879,6 +880,7 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
         case VRC_RING_ORDER: return L::template chain_reduce_scatter<false>(x, y, n, count, outer, cus, st);
         case VRC_HD:
         case VRC_HD_ORDER: return L::template fused_reduce_scatter<vrc::Butterfly>(x, y, n, count, outer, cus, st);
+        case VRC_SELECT: break;
         }
         break;
     case Coll::AG:
@@ -889,6 +891,7 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
         case VRC_HD_ORDER: return L::fused_all_gather(x, y, n, count, outer, cus, st);
         case VRC_RING_CHAINED: return L::chain_all_gather(x, y, n, count, outer, cus, st);
         case VRC_HD: return L::hd_all_gather(x, y, n, count, outer, cus, st);
+        case VRC_SELECT: break;
         }
         break;
     }
@@ -922,7 +925,17 @@ vrc_status_t run(Coll coll, vrc_mode_t mode, vrc_dtype_t dt, const void* const* 
 bool mode_ok(vrc_mode_t m)
 {
     return m == VRC_RING || m == VRC_FUSED || m == VRC_RING_CHAINED || m == VRC_RING_ORDER || m == VRC_HD ||
-           m == VRC_HD_ORDER;
+           m == VRC_HD_ORDER || m == VRC_SELECT;
+}
+
+// VRC_SELECT: halving-doubling for power-of-two rank counts and inputs of at
+// most VRC_SELECT_HD_MAX_BYTES per rank (log2 N steps win while launches
+// dominate), else the ring.
+vrc_mode_t resolve_mode(vrc_mode_t m, int n, uint64_t bytes_per_rank)
+{
+    if (m != VRC_SELECT) return m;
+    const bool pow2 = (n & (n - 1)) == 0;
+    return pow2 && bytes_per_rank <= VRC_SELECT_HD_MAX_BYTES ? VRC_HD : VRC_RING;
 }
 
 // Halving-doubling pairs rank r with r XOR d, so it needs a power of two.
@@ -967,8 +980,9 @@ vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nrank
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
     if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
-    if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     const uint64_t bytes = (uint64_t)count * (uint64_t)esize(dtype);
+    mode = resolve_mode(mode, nranks, bytes);
+    if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     uint64_t rb[kMaxRanks];
     for (int r = 0; r < nranks; r++) rb[r] = bytes;
     rc = check_buffers(send, recv, nranks, bytes, rb, true);
@@ -984,10 +998,11 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
     if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
+    const int E = esize(dtype);
+    mode = resolve_mode(mode, nranks, (uint64_t)count * E);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     if (outer > 1 && (count / outer) % (uint64_t)nranks != 0) return VRC_ERR_INVALID_ARG;
-    const int E = esize(dtype);
     uint64_t rb[kMaxRanks];
     for (int c = 0; c < nranks; c++) {
         if (outer == 1) {
@@ -1010,9 +1025,10 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
     if (!mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
+    const int E = esize(dtype);
+    mode = resolve_mode(mode, nranks, (uint64_t)count * E);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
-    const int E = esize(dtype);
     uint64_t rb[kMaxRanks];
     for (int r = 0; r < nranks; r++) rb[r] = (uint64_t)count * (uint64_t)nranks * E;
     rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, false);

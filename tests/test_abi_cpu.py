@@ -134,4 +134,4 @@ def test_halving_doubling_needs_a_power_of_two():
         assert vrc.raw_allreduce(x, y, 1000, vrc.VRC_FP32, mode) == vrc.VRC_ERR_INVALID_ARG
         assert vrc.raw_reduce_scatter(x, y, 1000, 1, vrc.VRC_FP32, mode) == vrc.VRC_ERR_INVALID_ARG
         assert vrc.raw_all_gather(x, y, 1000, 1, vrc.VRC_FP32, mode) == vrc.VRC_ERR_INVALID_ARG
-    assert vrc.raw_allreduce(x, y, 1000, vrc.VRC_FP32, 6) == vrc.VRC_ERR_UNSUPPORTED
+    assert vrc.raw_allreduce(x, y, 1000, vrc.VRC_FP32, 7) == vrc.VRC_ERR_UNSUPPORTED

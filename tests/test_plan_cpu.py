@@ -27,6 +27,11 @@ def buffers(n):
     return [SEND_BASE + r * STRIDE for r in range(n)], [RECV_BASE + r * STRIDE for r in range(n)]
 
 
+def wide_buffers(n):
+    """Stand-in addresses 4 GiB apart, for plans of large buffers."""
+    return [(1 << 40) + r * (1 << 32) for r in range(n)], [(1 << 41) + r * (1 << 32) for r in range(n)]
+
+
 def owner(addr, bases):
     """(rank, byte offset) of an address inside one of the rank buffers."""
     for r, b in enumerate(bases):
@@ -200,3 +205,33 @@ def test_plan_validates_like_the_call():
     with pytest.raises(vrc.VrcError):
         vrc.plan(vrc.COLL_ALLREDUCE, send, [recv[0], recv[0], recv[2]], 100, 1, vrc.VRC_FP32, vrc.VRC_RING)
     assert vrc.lib().vrc_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("n,count,esize_dtype,want", [
+    (8, 1000, vrc.VRC_FP32, "hd"),
+    (8, (64 << 20) // 4, vrc.VRC_FP32, "hd"),          # exactly the limit: halving-doubling
+    (8, (64 << 20) // 4 + 1, vrc.VRC_FP32, "ring"),    # one element over: ring
+    (8, (64 << 20) // 2 + 1, vrc.VRC_BF16, "ring"),
+    (6, 1000, vrc.VRC_FP32, "ring"),                   # not a power of two
+    (16, 5, vrc.VRC_INT32, "hd"),
+    (2, 10, vrc.VRC_FP16, "hd"),
+])
+def test_select_follows_the_documented_rule(n, count, esize_dtype, want):
+    """VRC_SELECT: halving-doubling for power-of-two N and at most 64 MiB per
+    rank, else the ring; the plan shows which algorithm ran."""
+    send, recv = wide_buffers(n)
+    ops, launches = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, esize_dtype, vrc.VRC_SELECT)
+    ref_ops, ref_launches = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, esize_dtype,
+                                     vrc.VRC_HD if want == "hd" else vrc.VRC_RING)
+    assert (ops, launches) == (ref_ops, ref_launches)
+    assert launches == (2 * (n.bit_length() - 1) if want == "hd" else 2 * (n - 1))
+
+
+@pytest.mark.parametrize("coll", [vrc.COLL_REDUCE_SCATTER, vrc.COLL_ALL_GATHER])
+@pytest.mark.parametrize("count,want", [(4096, "hd"), ((64 << 20) // 2 + 8, "ring")])
+def test_select_for_the_halves(coll, count, want):
+    n = 8
+    send, recv = wide_buffers(n)
+    got = vrc.plan(coll, send, recv, count, 1, vrc.VRC_FP16, vrc.VRC_SELECT)
+    ref = vrc.plan(coll, send, recv, count, 1, vrc.VRC_FP16, vrc.VRC_HD if want == "hd" else vrc.VRC_RING)
+    assert got == ref
