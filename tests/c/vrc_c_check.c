@@ -53,7 +53,7 @@ static int run_dtype(vrc_dtype_t dt, size_t count)
         CHECK_HIP(hipMalloc(&ag[r], count * esz * N));
         CHECK_HIP(hipMemcpy(x[r], host, count * esz, hipMemcpyHostToDevice));
     }
-    const vrc_mode_t modes[] = {VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER};
+    const vrc_mode_t modes[] = {VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER, VRC_SELECT};
     for (size_t m = 0; m < sizeof(modes) / sizeof(modes[0]); m++) {
         vrc_status_t st = vrc_allreduce((const void* const*)x, y, N, count, dt, VRC_SUM, modes[m], NULL);
         if (st != VRC_OK) {
