@@ -95,6 +95,21 @@ def time_calls(fn, steps: int, warmup: int, torch):
     return wall, kms
 
 
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, CPUs this process may
+    use, and the CPU model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "model": model}
+
+
 def cpu_baseline(xs, w, mode: str):
     """The oracle as it stands, single-threaded, on the first 1/8 of every
     rank's buffer (inputs copied to the host beforehand, not timed)."""
@@ -398,11 +413,18 @@ def main() -> int:
                                   "kernel_over_copy": round(achieved / copy_gbs, 4)}
         log(f"same-box copy: {extra['same_box_copy']}")
 
+    # NCCL-style figures for context: algbw = S / t per rank buffer, busbw = algbw * 2(N-1)/N.
+    algbw = size / (kavg * 1e-3) / 1e9
+    extra["nccl_style"] = {"algbw_GB_per_s": round(algbw, 2),
+                           "busbw_GB_per_s": round(algbw * 2 * (w.n - 1) / w.n, 2),
+                           "note": "context only; kernel time, S = one rank's buffer"}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a slice of the inputs")
         cpu = cpu_baseline(xs, w, args.mode)
         log(f"cpu baseline {cpu['value']} GB/s")
+        extra["cpu_baseline_host"] = host_info()
 
     out = {
         "metric": "emulated all-reduce HBM GB/s and % of peak, 8 ranks x 512 MB; bit-exact/tol",
