@@ -78,8 +78,10 @@ int env_int(const char* name, int dflt, int lo, int hi)
 //    per rank: 5.6 TB/s); 8 per CU below that, where the Infinity Cache
 //    holds much of the data and latency hiding matters more than open DRAM
 //    rows;
-//  - ring steps: 4 workgroups per CU (summed over the N per-rank operations)
-//    once a step moves >= 1 GiB, 8 below.
+//  - ring and halving-doubling steps: 4 workgroups per CU (summed over the N
+//    per-rank operations) once a step moves >= 256 MiB, 8 below (4 is 2-3 %
+//    faster for 8 x 128 MiB and the same at 8 x 512 MiB; 1 or 2 keep too
+//    few loads in flight).
 // Each lane keeps two 16-byte vectors per rank in flight (unroll 2).  Loads
 // and stores carry the non-temporal hint (measured faster for this
 // never-reused stream), except small relay copies (step_nontemporal) and the
@@ -116,7 +118,7 @@ int fused_blocks_per_cu(uint64_t bytes_moved)
 int step_blocks_per_cu(uint64_t bytes_moved)
 {
     if (tuning().step_blocks_per_cu) return tuning().step_blocks_per_cu;
-    return bytes_moved >= kGiB ? 4 : 8;
+    return bytes_moved >= kGiB / 4 ? 4 : 8;
 }
 
 // Cache hint of a ring or halving-doubling step.  Adds stream with the
