@@ -138,6 +138,16 @@ bool step_nontemporal(bool add, uint64_t bytes_moved)
     return add || bytes_moved / 2 > 64 * (1ull << 20);
 }
 
+// The single-launch ring with partials in registers (VRC_RING_ORDER) walks
+// wave-sized tiles and does best with few workgroups at every size: 2 per CU
+// from 1 GiB to 4 GiB moved, 1 otherwise (8 x 16 MiB fp32: 53.5 us at 1 per
+// CU against 58.0 us at 8).
+int order_blocks_per_cu(uint64_t bytes_moved)
+{
+    if (tuning().fused_blocks_per_cu) return tuning().fused_blocks_per_cu;
+    return (bytes_moved >= kGiB && bytes_moved < 4 * kGiB) ? 2 : 1;
+}
+
 // Memory-faithful chains wait on their own stores between steps, so they
 // need more resident waves than the fused loop to hide latency.
 int chain_blocks_per_cu(uint64_t bytes_moved)
@@ -770,7 +780,7 @@ struct Launch {
         const uint64_t lanes = a.tile0[n] * 64, scalar_lanes = (uint64_t)n * 64;
         const uint64_t work = lanes > scalar_lanes ? lanes : scalar_lanes;
         const uint64_t bytes = MEM ? 5 * (uint64_t)(n - 1) * count * E : 2 * (uint64_t)n * count * E;
-        const int bpc = MEM ? chain_blocks_per_cu(bytes) : fused_blocks_per_cu(bytes);
+        const int bpc = MEM ? chain_blocks_per_cu(bytes) : order_blocks_per_cu(bytes);
         const dim3 grid(grid_x(cus, work, 1, bpc));
         switch (n) {
 #define VRC_CASE(K) \
