@@ -72,8 +72,8 @@ int env_int(const char* name, int dflt, int lo, int hi)
 }
 
 // Launch shape, from measurements on MI355X (HIP events, 8 ranks):
-//  - fused kernels: one 256-lane workgroup per CU is fastest once the whole
-//    operation moves >= 4 GiB (5.4 TB/s for 8 x 512 MiB bf16, the speed of a
+//  - fused kernels: one 256-lane workgroup per CU (two at 2 ranks) is fastest
+//    once the whole operation moves >= 4 GiB (5.4 TB/s for 8 x 512 MiB bf16, the speed of a
 //    plain 8-in/8-out copy on the same buffers); 2 per CU from 1 GiB (128 MiB
 //    per rank: 5.6 TB/s); 8 per CU below that, where the Infinity Cache
 //    holds much of the data and latency hiding matters more than open DRAM
@@ -107,10 +107,13 @@ const Tuning& tuning()
 
 constexpr uint64_t kGiB = 1ull << 30;
 
-int fused_blocks_per_cu(uint64_t bytes_moved)
+// Two ranks keep only a quarter of the eight-rank loads in flight per lane,
+// so at 2 ranks the large-size grid doubles (8 GiB moved: 1.64-1.70 ms
+// against 1.78-1.80 ms at one workgroup per CU; 4 and 16 ranks are best at one).
+int fused_blocks_per_cu(uint64_t bytes_moved, int n)
 {
     if (tuning().fused_blocks_per_cu) return tuning().fused_blocks_per_cu;
-    if (bytes_moved >= 4 * kGiB) return 1;
+    if (bytes_moved >= 4 * kGiB) return n <= 2 ? 2 : 1;
     if (bytes_moved >= kGiB) return 2;
     return 8;
 }
@@ -142,9 +145,10 @@ bool step_nontemporal(bool add, uint64_t bytes_moved)
 // wave-sized tiles and does best with few workgroups at every size: 2 per CU
 // from 1 GiB to 4 GiB moved, 1 otherwise (8 x 16 MiB fp32: 53.5 us at 1 per
 // CU against 58.0 us at 8).
-int order_blocks_per_cu(uint64_t bytes_moved)
+int order_blocks_per_cu(uint64_t bytes_moved, int n)
 {
     if (tuning().fused_blocks_per_cu) return tuning().fused_blocks_per_cu;
+    if (n <= 2) return 2;  // 2 ranks, 8 GiB moved: 1.57-1.58 ms against 2.19 ms at one per CU
     return (bytes_moved >= kGiB && bytes_moved < 4 * kGiB) ? 2 : 1;
 }
 
@@ -526,7 +530,7 @@ struct Launch {
         a.count = count;
         a.g = split_rows(addr, 2 * n, 1, nullptr, 0, count, E);
         const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
-        const dim3 grid(grid_x(cus, work, 1, fused_blocks_per_cu(2 * (uint64_t)n * count * E)));
+        const dim3 grid(grid_x(cus, work, 1, fused_blocks_per_cu(2 * (uint64_t)n * count * E, n)));
         if constexpr (std::is_same<Fold, vrc::Butterfly>::value) {
             switch (n) {
             case 2: launch_fused_ar_n<2, Fold>(a, grid, st); break;
@@ -582,7 +586,7 @@ struct Launch {
             const uint64_t w = k.rows * (ch.g.nvb + ch.g.head + ch.g.tail);
             if (w > work) work = w;
         }
-        const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * count * E)), (unsigned)n);
+        const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * count * E, n)), (unsigned)n);
         if constexpr (std::is_same<Fold, vrc::Butterfly>::value) {
             switch (n) {
             case 2: launch_fused_rs_n<2, Fold>(a, grid, st); break;
@@ -626,7 +630,7 @@ struct Launch {
             const uint64_t w = outer * (a.g[q].nvb + a.g[q].head + a.g[q].tail);
             if (w > work) work = w;
         }
-        const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * n * count * E)), (unsigned)n);
+        const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * n * count * E, n)), (unsigned)n);
         hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
         return check_launch();
     }
@@ -780,7 +784,7 @@ struct Launch {
         const uint64_t lanes = a.tile0[n] * 64, scalar_lanes = (uint64_t)n * 64;
         const uint64_t work = lanes > scalar_lanes ? lanes : scalar_lanes;
         const uint64_t bytes = MEM ? 5 * (uint64_t)(n - 1) * count * E : 2 * (uint64_t)n * count * E;
-        const int bpc = MEM ? chain_blocks_per_cu(bytes) : order_blocks_per_cu(bytes);
+        const int bpc = MEM ? chain_blocks_per_cu(bytes) : order_blocks_per_cu(bytes, n);
         const dim3 grid(grid_x(cus, work, 1, bpc));
         switch (n) {
 #define VRC_CASE(K) \
@@ -816,7 +820,7 @@ struct Launch {
             if (w > work) work = w;
         }
         const uint64_t bytes = MEM ? 3 * (uint64_t)(n - 1) * count * E : (uint64_t)(n + 1) * count * E;
-        const int bpc = MEM ? chain_blocks_per_cu(bytes) : fused_blocks_per_cu(bytes);
+        const int bpc = MEM ? chain_blocks_per_cu(bytes) : fused_blocks_per_cu(bytes, n);
         const dim3 grid(grid_x(cus, work, n, bpc), (unsigned)n);
         switch (n) {
 #define VRC_CASE(K) \
