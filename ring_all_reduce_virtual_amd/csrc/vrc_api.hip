@@ -343,11 +343,23 @@ struct Launch {
         const uint64_t bytes = step_bytes<ADD>(args, nops);
         const int bpc = step_blocks_per_cu(bytes);
         const dim3 grid(grid_x(cus, work, nops, bpc), (unsigned)nops);
-        if (step_nontemporal(ADD, bytes))
-            hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true>), grid, dim3(kBlock), 0, st, args);
-        else
-            hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, false>), grid, dim3(kBlock), 0, st, args);
+        const bool nt = step_nontemporal(ADD, bytes);
+        if (nops <= 4) launch_step<ADD, 4>(args, nops, nt, grid, st);
+        else if (nops <= 8) launch_step<ADD, 8>(args, nops, nt, grid, st);
+        else if (nops <= 16) launch_step<ADD, 16>(args, nops, nt, grid, st);
+        else launch_step<ADD, vrc::kMaxStepOps>(args, nops, nt, grid, st);
         return check_launch();
+    }
+
+    // Launch a step with an argument block of K operation slots (the first
+    // nops filled; blockIdx.y < nops never reads the others).
+    template <bool ADD, int K>
+    static void launch_step(const vrc::StepArgs& args, int nops, bool nt, dim3 grid, hipStream_t st)
+    {
+        vrc::StepArgsK<K> a = {};
+        for (int i = 0; i < nops && i < K; i++) a.op[i] = args.op[i];
+        if (nt) hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true, K>), grid, dim3(kBlock), 0, st, a);
+        else hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, false, K>), grid, dim3(kBlock), 0, st, a);
     }
 
     // Work items of one operation: vectors plus scalar slots.
