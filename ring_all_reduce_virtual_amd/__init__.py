@@ -180,16 +180,19 @@ def _dtype_code(t) -> int:
 
 
 def _check_ranks(tensors, what):
+    # One pass, with rank 0's attributes read once: this check is most of the
+    # host cost of a small call.
     if not isinstance(tensors, (list, tuple)) or not tensors:
         raise ValueError(f"{what}: expected a non-empty list of tensors, one per rank")
     if len(tensors) > MAX_RANKS:
         raise ValueError(f"{what}: at most {MAX_RANKS} ranks")
     t0 = tensors[0]
+    dtype, shape, device = t0.dtype, t0.shape, t0.device
+    if device.type != "cuda":
+        raise ValueError(f"{what}: tensors must live on the GPU")
     for t in tensors:
-        if t.dtype != t0.dtype or t.shape != t0.shape or t.device != t0.device:
+        if t.dtype is not dtype or t.shape != shape or t.device != device:
             raise ValueError(f"{what}: all ranks need the same dtype, shape and device")
-        if t.device.type != "cuda":
-            raise ValueError(f"{what}: tensors must live on the GPU")
         if not t.is_contiguous():
             raise ValueError(f"{what}: tensors must be contiguous")
 
