@@ -121,6 +121,9 @@ typedef enum { VRC_SUM = 0 } vrc_op_t;
  *                     library allocates nothing), so it runs as VRC_HD_ORDER.
  *   VRC_HD_ORDER      one launch with the fused traffic, partials in
  *                     registers.  For the all-gather it equals VRC_FUSED.
+ *                     At 2 ranks the butterfly is a single add rounded once,
+ *                     bit for bit the rank-order fold, so it runs (and
+ *                     vrc_plan reports it) as the fused kernel.
  * Size-based selection between the two step-by-step algorithms [TP]:
  *   VRC_SELECT        VRC_HD when nranks is a power of two and each rank's
  *                     input holds at most VRC_SELECT_HD_MAX_BYTES, else
