@@ -16,7 +16,9 @@ only while the kernel sources still hash to the value recorded with it.
 `cpu_baseline` times the CPU oracle (single thread) on a bounded slice of the
 same inputs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode fused|ring]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--mode fused|ring|ring_chained|ring_order|hd|hd_order|select]
+       python bench.py --suite | --overlap | --probe-copy
 """
 from __future__ import annotations
 
@@ -64,7 +66,10 @@ def recorded_traffic(workload: str, mode: str):
     """Measured HBM bytes per launch from profiles/<kernel>.<workload>.counters.md,
     if those counters were taken on the current kernel sources."""
     kernel = {"fused": "k_fused_allreduce", "ring": "k_ring_step", "ring_chained": "k_ring_chain_allreduce",
-              "ring_order": "k_ring_chain_allreduce", "hd": "k_ring_step", "hd_order": "k_fused_allreduce_butterfly"}[mode]
+              "ring_order": "k_ring_chain_allreduce", "hd": "k_ring_step",
+              "hd_order": "k_fused_allreduce_butterfly"}.get(mode)
+    if kernel is None:
+        return None
     path = os.path.join(PROFILES, f"{kernel}.{workload}.counters.md")
     if not os.path.exists(path):
         return None
@@ -119,7 +124,9 @@ def cpu_baseline(xs, w, mode: str):
     orc = oracle.get()
     sample = max(1, w.count // 8)
     hx = [workloads.to_numpy(x.reshape(-1)[:sample]) for x in xs]
-    fn = orc.fused_allreduce if mode == "fused" else orc.ring_allreduce
+    algorithm = selected(mode, w.n, w.count * w.esize)
+    fn = {"fused": orc.fused_allreduce, "hd": orc.hd_allreduce, "hd_order": orc.hd_allreduce}.get(
+        algorithm, orc.ring_allreduce)
     t0 = time.perf_counter()
     fn(hx, w.dtype)
     dt = time.perf_counter() - t0
