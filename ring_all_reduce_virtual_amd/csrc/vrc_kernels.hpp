@@ -183,6 +183,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_allreduce(FusedArArgs a)
             for (int u = 0; u < U; u++)
 #pragma unroll
                 for (int r = 0; r < N; r++) in[u][r] = ld16<NT>(a.src[r] + body + (v + u * nthreads) * 16);
+            issue_loads_first();
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const u32x4 s = Fold::template vec<T, N>(in[u]);
@@ -195,6 +196,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_allreduce(FusedArArgs a)
         u32x4 in[N];
 #pragma unroll
         for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
+        issue_loads_first();
         const u32x4 s = Fold::template vec<T, N>(in);
 #pragma unroll
         for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, s);
@@ -244,6 +246,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_reduce_scatter(FusedRsArgs a)
         u32x4 in[N];
 #pragma unroll
         for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + so);
+        issue_loads_first();
         st16<NT>(c.d + row * c.s_dst * E + col, Fold::template vec<T, N>(in));
     }
     const uint64_t ns = c.rows * (c.g.head + c.g.tail);
