@@ -21,6 +21,13 @@ N = 8
 
 SRC = f"""
 #include "vrc_kernels.hpp"
+template __global__ void vrc::k_fused_allreduce<vrc::BF16, {N}, 2, true, vrc::RankFold>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_allreduce<vrc::F16, {N}, 2, true, vrc::RankFold>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_allreduce<vrc::F32, {N}, 2, true, vrc::RankFold>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_allreduce<vrc::I32, {N}, 2, true, vrc::RankFold>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_allreduce<vrc::F32, {N}, 2, true, vrc::Butterfly>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_reduce_scatter<vrc::F32, {N}, true, vrc::RankFold>(vrc::FusedRsArgs);
+template __global__ void vrc::k_ring_chain_allreduce<vrc::F32, {N}, false, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, true, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, false, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_reduce_scatter<vrc::F16, {N}, true, true>(vrc::ChainArgs);
@@ -70,3 +77,33 @@ def test_chain_kernels_issue_every_access(asm, pattern, loads, stores):
     assert count(text, "global_load_dwordx4") == loads
     assert count(text, "global_store_dwordx4") == stores
     assert count(text, r"flat_(load|store)\w*") == 0
+
+
+def longest_load_run(text):
+    """Longest run of 16-byte global loads with no wait on the vector memory counter between them."""
+    best = run = 0
+    for line in text.splitlines():
+        line = line.strip()
+        if re.match(r"global_load_dwordx4\b", line):
+            run += 1
+            best = max(best, run)
+        elif re.match(r"s_waitcnt\b.*vmcnt", line):
+            run = 0
+    return best
+
+
+@pytest.mark.parametrize("pattern,loads", [
+    (r"k_fused_allreduceINS_4BF16ELi8ELi2ELb1ENS_8RankFold", 2 * N),
+    (r"k_fused_allreduceINS_3F16ELi8ELi2ELb1ENS_8RankFold", 2 * N),
+    (r"k_fused_allreduceINS_3F32ELi8ELi2ELb1ENS_8RankFold", 2 * N),
+    (r"k_fused_allreduceINS_3I32ELi8ELi2ELb1ENS_8RankFold", 2 * N),
+    (r"k_fused_allreduceINS_3F32ELi8ELi2ELb1ENS_9Butterfly", 2 * N),
+    (r"k_fused_reduce_scatterINS_3F32ELi8ELb1ENS_8RankFold", N),
+    (r"k_ring_chain_allreduceINS_3F32ELi8ELb0", N),
+])
+def test_single_pass_kernels_keep_all_loads_in_flight(asm, pattern, loads):
+    """Every lane issues all of its loads (2N with two vectors per rank) before
+    it waits for the first one.  A compiler that interleaves the fold with
+    the loads leaves two in flight and runs the 8 x 512 MiB fused all-reduce
+    at 3.8 TB/s instead of 5.4."""
+    assert longest_load_run(body(asm, pattern)) >= loads
