@@ -120,12 +120,13 @@ struct BF16 {
     // bfloat16 is the upper half of an IEEE binary32.
     __device__ static A widen(S s) { return __uint_as_float((uint32_t)s << 16); }
     // Round to nearest even on the 16 discarded bits; NaN stays a quiet NaN.
+    // Both results are computed and one selected, so no lane branches.
     __device__ static S narrow(A a)
     {
-        uint32_t u = __float_as_uint(a);
-        if ((u & 0x7fffffffu) > 0x7f800000u) return (S)((u >> 16) | 0x40u);
-        u += 0x7fffu + ((u >> 16) & 1u);
-        return (S)(u >> 16);
+        const uint32_t u = __float_as_uint(a);
+        const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+        const uint32_t quiet_nan = (u >> 16) | 0x40u;
+        return (S)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded);
     }
     __device__ static A add(A a, A b) { return a + b; }
     __device__ static void unpack(u32x4 v, A* a)

@@ -60,7 +60,7 @@ struct StepArgsK {
 };
 using StepArgs = StepArgsK<kMaxStepOps>;
 
-template <class T, bool ADD, bool NT, int K>
+template <class T, bool ADD, bool NT, int K, int U = 1>
 __global__ __launch_bounds__(kBlock) void k_ring_step(StepArgsK<K> args)
 {
     const StepOp& op = args.op[blockIdx.y];
@@ -71,18 +71,39 @@ __global__ __launch_bounds__(kBlock) void k_ring_step(StepArgsK<K> args)
     const uint64_t nv = op.rows * op.g.nvb;
     const uint64_t body = op.g.head * E;
     if (op.rows == 1) {
-        for (uint64_t v = tid; v < nv; v += nthreads) {
+        uint64_t v = tid;
+        if constexpr (U > 1) {
+            for (; v + (U - 1) * nthreads < nv; v += U * nthreads) {
+                u32x4 x[U], y[U];
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    x[u] = ld16<NT>(op.a + body + (v + u * nthreads) * 16);
+                    if constexpr (ADD) y[u] = ld16<NT>(op.b + body + (v + u * nthreads) * 16);
+                }
+                issue_loads_first();
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    if constexpr (ADD) x[u] = add_v<T>(x[u], y[u]);
+                    st16<NT>(op.d + body + (v + u * nthreads) * 16, x[u]);
+                }
+            }
+        }
+        for (; v < nv; v += nthreads) {
             const uint64_t off = body + v * 16;
-            u32x4 x = ld16<NT>(op.a + off);
-            if constexpr (ADD) x = add_v<T>(x, ld16<NT>(op.b + off));
+            u32x4 x = ld16<NT>(op.a + off), y;
+            if constexpr (ADD) y = ld16<NT>(op.b + off);
+            issue_loads_first();
+            if constexpr (ADD) x = add_v<T>(x, y);
             st16<NT>(op.d + off, x);
         }
     } else {
         for (uint64_t v = tid; v < nv; v += nthreads) {
             const uint64_t row = v / op.g.nvb;
             const uint64_t col = (v - row * op.g.nvb) * 16 + body;
-            u32x4 x = ld16<NT>(op.a + row * op.sa * E + col);
-            if constexpr (ADD) x = add_v<T>(x, ld16<NT>(op.b + row * op.sb * E + col));
+            u32x4 x = ld16<NT>(op.a + row * op.sa * E + col), y;
+            if constexpr (ADD) y = ld16<NT>(op.b + row * op.sb * E + col);
+            issue_loads_first();
+            if constexpr (ADD) x = add_v<T>(x, y);
             st16<NT>(op.d + row * op.sd * E + col, x);
         }
     }
@@ -392,6 +413,7 @@ __device__ __forceinline__ void chain_block(const char* const* in, char* const* 
     V x[N];
 #pragma unroll
     for (int t = 0; t < N; t++) x[t] = IO::ld_in(in[t] + o);
+    issue_loads_first();
     V p = x[0];
     if constexpr (MEM) {
 #pragma unroll
@@ -486,6 +508,7 @@ __device__ __forceinline__ void chain_rs_block(const char* const* in, uint64_t s
     V x[N];
 #pragma unroll
     for (int t = 0; t < N; t++) x[t] = IO::ld_in(in[t] + so);
+    issue_loads_first();
     V p = x[0];
 #pragma unroll
     for (int t = 1; t < N; t++) {

@@ -32,6 +32,8 @@ template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, true, true>
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, false, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_reduce_scatter<vrc::F16, {N}, true, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_all_gather<vrc::F32, {N}, true>(vrc::FusedAgArgs);
+template __global__ void vrc::k_ring_step<vrc::BF16, true, true, 8>(vrc::StepArgsK<8>);
+template __global__ void vrc::k_ring_step<vrc::F32, true, false, 8>(vrc::StepArgsK<8>);
 """
 
 
@@ -100,10 +102,15 @@ def longest_load_run(text):
     (r"k_fused_allreduceINS_3F32ELi8ELi2ELb1ENS_9Butterfly", 2 * N),
     (r"k_fused_reduce_scatterINS_3F32ELi8ELb1ENS_8RankFold", N),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0", N),
+    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1", N),
+    (r"k_ring_chain_reduce_scatterINS_3F16ELi8ELb1", N),
+    (r"k_ring_stepINS_4BF16ELb1ELb1ELi8", 2),
+    (r"k_ring_stepINS_3F32ELb1ELb0ELi8", 2),
 ])
 def test_single_pass_kernels_keep_all_loads_in_flight(asm, pattern, loads):
     """Every lane issues all of its loads (2N with two vectors per rank) before
     it waits for the first one.  A compiler that interleaves the fold with
     the loads leaves two in flight and runs the 8 x 512 MiB fused all-reduce
-    at 3.8 TB/s instead of 5.4."""
+    at 3.8 TB/s instead of 5.4.  A ring step's chunk-add has both of its
+    operands in flight together."""
     assert longest_load_run(body(asm, pattern)) >= loads
