@@ -78,15 +78,13 @@ int env_int(const char* name, int dflt, int lo, int hi)
 //    per rank: 5.6 TB/s); 8 per CU below that, where the Infinity Cache
 //    holds much of the data and latency hiding matters more than open DRAM
 //    rows;
-//  - ring and halving-doubling steps: 4 workgroups per CU (summed over the N
-//    per-rank operations) once a step moves >= 256 MiB, 8 below (4 is 2-3 %
-//    faster for 8 x 128 MiB and the same at 8 x 512 MiB; 1 or 2 keep too
-//    few loads in flight).
-// Each lane keeps two 16-byte vectors per rank in flight (unroll 2).  Loads
-// and stores carry the non-temporal hint (measured faster for this
-// never-reused stream), except small relay copies (step_nontemporal) and the
-// partials the single-launch ring reads back.  The environment variables
-// override the policy, for measurement.
+//  - ring and halving-doubling steps: by the bytes a step moves and its number
+//    of per-rank operations (step_shape), workgroups counted over all of them.
+// In the fused kernels each lane keeps two 16-byte vectors per rank in flight
+// (unroll 2).  Loads and stores carry the non-temporal hint (measured faster
+// for this never-reused stream), except small relay copies (step_nontemporal)
+// and the partials the single-launch ring reads back.  The environment
+// variables override the policy, for measurement.
 struct Tuning {
     int fused_blocks_per_cu;  // 0: size policy
     int step_blocks_per_cu;   // 0: size policy
@@ -106,6 +104,7 @@ const Tuning& tuning()
     return t;
 }
 
+constexpr uint64_t kMiB = 1ull << 20;
 constexpr uint64_t kGiB = 1ull << 30;
 
 // Two ranks keep only a quarter of the eight-rank loads in flight per lane,
@@ -119,24 +118,39 @@ int fused_blocks_per_cu(uint64_t bytes_moved, int n)
     return 8;
 }
 
-// Launch shape of a ring or halving-doubling step, by the bytes it moves.
-// Large steps keep two vectors per lane in flight (four loads for an add).
-// Measured on MI355X, bf16 all-reduce of 8 ranks, ms per call, against one
-// vector per lane at 4 workgroups per CU (>= 256 MiB) or 8 (below):
-//   512 MiB per rank (1.5 GiB per reduce step), 8 per CU: ring 3.280 vs 3.327, hd 3.373 vs 3.494;
-//   256 MiB per rank, 8 per CU: ring 1.596 vs 1.628;
-//   64 MiB per rank (192 MiB per reduce step), 16 per CU: ring 0.384 vs 0.420, hd 0.384 vs 0.403;
-//   16 MiB per rank: one vector at 8 per CU stays best (launch-bound steps).
+// Launch shape of a ring or halving-doubling step of `nops` per-rank
+// operations moving `bytes_moved` in all.  Launch-bound steps (< 64 MiB) use
+// one vector per lane at 8 workgroups per CU.  Larger steps of up to 7
+// operations that each move >= 48 MiB use one vector at 4 per CU.  Other
+// steps keep two vectors per lane in flight (four loads for an add): at 8 per
+// CU when there are fewer than 12 operations and each moves >= 128 MiB, else
+// at 16 per CU.
+// Measured on MI355X, bf16 all-reduce, ms per call for (vectors per lane,
+// workgroups per CU) on one box; ring unless marked hd:
+//   2 ranks x 2 GiB:     (1, 4) 2.012; (2, 8) 2.310; (2, 16) 2.237
+//   4 ranks x 1 GiB:     (1, 4) 2.886 (hd 2.930); (2, 8) 3.031 (hd 3.211)
+//   5 ranks x 819 MiB:   (1, 4) 3.376; (2, 8) 3.649; (2, 16) 3.769
+//   6 ranks x 682 MiB:   (1, 4) 3.542; (2, 8) 3.763
+//   7 ranks x 73 MiB:    (2, 16) 0.423; (1, 4) 0.438 (31 MiB per reduce operation)
+//   8 ranks x 512 MiB:   (2, 8) 3.310 (hd 3.385); (1, 4) 3.271 (hd 3.480); (2, 16) 3.302 (hd 3.483)
+//   8 ranks x 64 MiB:    (2, 16) 0.384; (2, 8) 0.403; (1, 4) 0.409
+//   12 ranks x 341 MiB:  (2, 16) 3.876; (1, 4) 3.848; (2, 8) 3.985
+//   16 ranks x 256 MiB:  (2, 16) 3.423 (hd 3.578); (2, 8) 3.584 (hd 3.705); (1, 4) 3.958
+//   8 ranks x 16 MiB:    (1, 8) 0.115; (2, 16) 0.122 (48 MiB steps)
 struct StepShape {
     int blocks_per_cu;
     int unroll;
 };
 
-StepShape step_shape(uint64_t bytes_moved)
+StepShape step_shape(uint64_t bytes_moved, int nops)
 {
     StepShape s = {8, 1};
-    if (bytes_moved >= kGiB / 2) s = {8, 2};
-    else if (bytes_moved >= kGiB / 16) s = {16, 2};
+    const uint64_t per_op = bytes_moved / (uint64_t)(nops > 0 ? nops : 1);
+    if (bytes_moved >= kGiB / 16) {
+        if (nops <= 7 && per_op >= 48 * kMiB) s = {4, 1};
+        else if (nops < 12 && per_op >= kGiB / 8) s = {8, 2};
+        else s = {16, 2};
+    }
     if (tuning().step_blocks_per_cu) s.blocks_per_cu = tuning().step_blocks_per_cu;
     if (tuning().step_unroll) s.unroll = tuning().step_unroll;
     return s;
@@ -156,7 +170,7 @@ bool step_nontemporal(bool add, uint64_t bytes_moved)
     case 1: return true;
     case 2: return add;
     }
-    return add || bytes_moved / 2 > 64 * (1ull << 20);
+    return add || bytes_moved / 2 > 64 * kMiB;
 }
 
 // The single-launch ring with partials in registers (VRC_RING_ORDER) walks
@@ -359,7 +373,7 @@ struct Launch {
             return VRC_OK;
         }
         const uint64_t bytes = step_bytes<ADD>(args, nops);
-        const StepShape shape = step_shape(bytes);
+        const StepShape shape = step_shape(bytes, nops);
         const dim3 grid(grid_x(cus, work, nops, shape.blocks_per_cu), (unsigned)nops);
         const bool nt = step_nontemporal(ADD, bytes);
         const bool u2 = shape.unroll == 2;

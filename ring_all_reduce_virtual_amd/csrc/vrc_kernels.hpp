@@ -39,7 +39,8 @@ __device__ __forceinline__ void scalar_slot(uint64_t k, const RowSplit& g, uint6
 // ---------------------------------------------------------------------------
 // Ring step: one launch runs one reduce-scatter step (d = a + b) or one
 // all-gather step (d = a) for every rank at once; blockIdx.y is the rank's
-// operation.
+// operation.  Both operands of an add are loaded before the add, and with
+// U = 2 a lane keeps two vectors (four loads of an add) in flight.
 // ---------------------------------------------------------------------------
 struct StepOp {
     const char* a;  // element (0,0) of the first operand region
