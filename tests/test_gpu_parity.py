@@ -287,3 +287,34 @@ def test_workload_reduce_scatter_fp16_n8_act(vrc, orc):
         for c in range(w.n):
             blocks = [x[:, c * 512:(c + 1) * 512].contiguous() for x in xs]
             tolerance_gate_torch([ys[c]], blocks, w.rtol, f"{w.name} {mode} chunk {c}")
+
+
+# ---------------------------------------------------------------------------
+# every step launch shape (vectors per lane, workgroups per CU), ragged sizes
+# ---------------------------------------------------------------------------
+SHAPE_CASES = [  # (n, count, dtype, modes): the shape each case's large steps take
+    (3, 50_331_653, "fp16", ("ring",)),               # <= 7 operations of >= 48 MiB: one vector, 4 per CU
+    (7, 8_388_613, "fp32", ("ring",)),                # <= 7 small operations: two vectors, 16 per CU
+    (9, 104_857_601, "fp32", ("ring",)),              # 8-11 operations of >= 128 MiB: two vectors, 8 per CU
+    (16, 16_777_219, "fp16", ("ring", "hd")),         # >= 12 operations: two vectors, 16 per CU
+    (2, 268_435_459, "bf16", ("ring", "hd")),         # 2 operations of 768 MiB: one vector, 4 per CU
+]
+
+
+@pytest.mark.parametrize("n,count,dtype,modes", SHAPE_CASES)
+def test_step_launch_shapes(vrc, orc, n, count, dtype, modes):
+    say(f"step shapes n={n} count={count} {dtype} {modes}")
+    xs = workloads.random_ranks(n, count, dtype, seed=500 + n, device=DEV)
+    hx = host(xs)
+    idx = sample_indices(count, n, 1 << 18, seed=n)
+    tidx = torch.from_numpy(idx.astype(np.int64)).to(DEV)
+    for mode in modes:
+        ys = vrc.vrc_allreduce(xs, mode=mode)
+        torch.cuda.synchronize()
+        ranks_identical(ys, f"{mode} n={n}")
+        want = (orc.ring_allreduce_at if mode in RING_FAMILY else orc.hd_allreduce_at)(hx, dtype, idx)
+        for r in (0, n - 1):
+            got = workloads.to_numpy(ys[r].reshape(-1)[tidx])
+            assert_bitwise(got, want, f"{mode} {dtype} n={n} count={count} rank {r} sampled")
+        del ys
+        torch.cuda.empty_cache()
