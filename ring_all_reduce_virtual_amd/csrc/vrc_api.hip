@@ -71,36 +71,37 @@ int env_int(const char* name, int dflt, int lo, int hi)
     return (int)v;
 }
 
-// Launch shape, from measurements on MI355X (HIP events, 8 ranks):
-//  - fused kernels: one 256-lane workgroup per CU (two at 2 ranks) is fastest
-//    once the whole operation moves >= 4 GiB (5.4 TB/s for 8 x 512 MiB bf16, the speed of a
-//    plain 8-in/8-out copy on the same buffers); 2 per CU from 1 GiB (128 MiB
-//    per rank: 5.6 TB/s); 8 per CU below that, where the Infinity Cache
-//    holds much of the data and latency hiding matters more than open DRAM
-//    rows;
+// Launch shape, from measurements on MI355X (HIP events):
+//  - fused all-reduce: one-wave workgroups sized to the rank count
+//    (fused_ar_shape);
+//  - fused reduce-scatter and all-gather: 256-lane workgroups, one per CU
+//    (two at 2 ranks) once the whole operation moves >= 4 GiB, 2 per CU from
+//    1 GiB, 8 per CU below that, where the Infinity Cache holds much of the
+//    data and latency hiding matters more than open DRAM rows;
 //  - ring and halving-doubling steps: by the bytes a step moves and its number
 //    of per-rank operations (step_shape), workgroups counted over all of them.
-// In the fused kernels each lane keeps two 16-byte vectors per rank in flight
-// (unroll 2).  Loads and stores carry the non-temporal hint (measured faster
-// for this never-reused stream), except small relay copies (step_nontemporal)
-// and the partials the single-launch ring reads back.  The environment
-// variables override the policy, for measurement.
+// Loads and stores carry the non-temporal hint (measured faster for this
+// never-reused stream), except small relay copies (step_nontemporal) and the
+// partials the single-launch ring reads back.  The environment variables
+// override the policy, for measurement.
 struct Tuning {
     int fused_blocks_per_cu;  // 0: size policy
     int step_blocks_per_cu;   // 0: size policy
     int chain_blocks_per_cu;  // 0: size policy
-    int unroll;               // independent vectors per lane per fused iteration (1 or 2)
+    int unroll;               // 0: size policy; else vectors per rank per lane per fused all-reduce iteration
     int step_nt;              // -1: size policy; 1: non-temporal steps; 0: regular loads/stores;
                               // 2: non-temporal adds and regular copies
     int step_unroll;          // 0: size policy; else vectors per lane per step iteration (1 or 2)
+    int fused_block;          // 0: size policy; else lanes per fused all-reduce workgroup (64 or 256)
 };
 
 const Tuning& tuning()
 {
     static const Tuning t = {env_int("VRC_FUSED_BLOCKS_PER_CU", 0, 1, 64),
                              env_int("VRC_STEP_BLOCKS_PER_CU", 0, 1, 64),
-                             env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 2, 1, 2),
-                             env_int("VRC_STEP_NT", -1, 0, 2), env_int("VRC_STEP_UNROLL", 0, 1, 2)};
+                             env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 0, 1, 2),
+                             env_int("VRC_STEP_NT", -1, 0, 2), env_int("VRC_STEP_UNROLL", 0, 1, 2),
+                             env_int("VRC_FUSED_BLOCK", 0, 64, 256)};
     return t;
 }
 
@@ -116,6 +117,45 @@ int fused_blocks_per_cu(uint64_t bytes_moved, int n)
     if (bytes_moved >= 4 * kGiB) return n <= 2 ? 2 : 1;
     if (bytes_moved >= kGiB) return 2;
     return 8;
+}
+
+// Launch shape of the fused all-reduce (rank-order and butterfly folds):
+// lanes per workgroup, workgroups per CU and vectors per rank that a lane
+// keeps in flight.
+//
+// From 64 MiB moved the kernel runs one-wave workgroups.  Workgroups are
+// handed to the 8 XCDs in turn, so consecutive 1 KiB tiles of every buffer
+// are served by different XCDs; with 256-lane workgroups each XCD owned 4 KiB
+// runs.  The grid keeps about 32 KiB of loads in flight per CU (workgroups per
+// CU x ranks x vectors per rank <= 32, at most 8 workgroups): more
+// outstanding requests made the mixed read/write stream slower, not faster.
+// Two vectors per rank at 3 and 4 ranks, one otherwise.  Measured on MI355X,
+// all shapes compared in one process on the same buffers (GB/s, old shape:
+// 256 lanes, two vectors, 1-2 per CU at these sizes -> this policy):
+//   8 x 512 MiB bf16 5,454 -> 5,648;  8 x 64 MiB 5,460 -> 5,902;
+//   16 x 256 MiB 5,025 -> 5,522;      4 x 128 MiB 5,428 -> 5,978;
+//   2 x 2 GiB 5,180 -> 5,576;         8 x 16 MiB (cache flushed) 4,505 -> 5,314.
+// Below 64 MiB moved a call is launch-bound and keeps 256-lane workgroups,
+// 8 per CU, two vectors per rank.
+struct FusedShape {
+    int block;
+    int blocks_per_cu;
+    int unroll;
+};
+
+FusedShape fused_ar_shape(uint64_t bytes_moved, int n)
+{
+    FusedShape s = {kBlock, 8, 2};
+    if (bytes_moved >= 64 * kMiB) {
+        s.block = 64;
+        s.unroll = (n == 3 || n == 4) ? 2 : 1;
+        s.blocks_per_cu = 8;
+        while (s.blocks_per_cu > 1 && s.blocks_per_cu * n * s.unroll > 32) s.blocks_per_cu /= 2;
+    }
+    if (tuning().fused_blocks_per_cu) s.blocks_per_cu = tuning().fused_blocks_per_cu;
+    if (tuning().fused_block) s.block = tuning().fused_block == 64 ? 64 : kBlock;
+    if (tuning().unroll) s.unroll = tuning().unroll;
+    return s;
 }
 
 // Launch shape of a ring or halving-doubling step of `nops` per-rank
@@ -217,9 +257,9 @@ hipError_t cu_count(int* out)
 
 // Grid x for `ops` operations of at most `work` lane-items each, capped at
 // blocks_per_cu workgroups per CU over the whole grid.
-unsigned grid_x(int cus, uint64_t work, int ops, int blocks_per_cu)
+unsigned grid_x(int cus, uint64_t work, int ops, int blocks_per_cu, int block = kBlock)
 {
-    const uint64_t want = (work + kBlock - 1) / kBlock;
+    const uint64_t want = (work + block - 1) / block;
     uint64_t cap = (uint64_t)cus * (uint64_t)blocks_per_cu / (uint64_t)(ops > 0 ? ops : 1);
     if (cap < 1) cap = 1;
     uint64_t g = want < cap ? want : cap;
@@ -548,12 +588,19 @@ struct Launch {
 
     // ---- fused family ----------------------------------------------------
     template <int N, class Fold>
-    static void launch_fused_ar_n(const vrc::FusedArArgs& a, dim3 grid, hipStream_t st)
+    static void launch_fused_ar_n(const vrc::FusedArArgs& a, dim3 grid, FusedShape sh, hipStream_t st)
     {
-        if (tuning().unroll == 2)
-            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 2, true, Fold>), grid, dim3(kBlock), 0, st, a);
-        else
-            hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 1, true, Fold>), grid, dim3(kBlock), 0, st, a);
+        if (sh.block == 64) {
+            if (sh.unroll == 2)
+                hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 2, true, Fold, 64>), grid, dim3(64), 0, st, a);
+            else
+                hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 1, true, Fold, 64>), grid, dim3(64), 0, st, a);
+        } else {
+            if (sh.unroll == 2)
+                hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 2, true, Fold>), grid, dim3(kBlock), 0, st, a);
+            else
+                hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 1, true, Fold>), grid, dim3(kBlock), 0, st, a);
+        }
     }
 
     template <class Fold = vrc::RankFold>
@@ -580,19 +627,20 @@ struct Launch {
         a.count = count;
         a.g = split_rows(addr, 2 * n, 1, nullptr, 0, count, E);
         const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
-        const dim3 grid(grid_x(cus, work, 1, fused_blocks_per_cu(2 * (uint64_t)n * count * E, n)));
+        const FusedShape sh = fused_ar_shape(2 * (uint64_t)n * count * E, n);
+        const dim3 grid(grid_x(cus, work, 1, sh.blocks_per_cu, sh.block));
         if constexpr (std::is_same<Fold, vrc::Butterfly>::value) {
             switch (n) {
-            case 2: launch_fused_ar_n<2, Fold>(a, grid, st); break;
-            case 4: launch_fused_ar_n<4, Fold>(a, grid, st); break;
-            case 8: launch_fused_ar_n<8, Fold>(a, grid, st); break;
-            case 16: launch_fused_ar_n<16, Fold>(a, grid, st); break;
+            case 2: launch_fused_ar_n<2, Fold>(a, grid, sh, st); break;
+            case 4: launch_fused_ar_n<4, Fold>(a, grid, sh, st); break;
+            case 8: launch_fused_ar_n<8, Fold>(a, grid, sh, st); break;
+            case 16: launch_fused_ar_n<16, Fold>(a, grid, sh, st); break;
             default: return VRC_ERR_INVALID_ARG;
             }
         } else {
             switch (n) {
 #define VRC_CASE(K) \
-    case K: launch_fused_ar_n<K, Fold>(a, grid, st); break;
+    case K: launch_fused_ar_n<K, Fold>(a, grid, sh, st); break;
                 VRC_FOR_N(VRC_CASE)
 #undef VRC_CASE
             default: return VRC_ERR_INVALID_ARG;

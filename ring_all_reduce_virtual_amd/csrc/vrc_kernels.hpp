@@ -188,11 +188,11 @@ struct Butterfly {
     }
 };
 
-template <class T, int N, int U, bool NT, class Fold = RankFold>
-__global__ __launch_bounds__(kBlock) void k_fused_allreduce(FusedArArgs a)
+template <class T, int N, int U, bool NT, class Fold = RankFold, int B = kBlock>
+__global__ __launch_bounds__(B) void k_fused_allreduce(FusedArArgs a)
 {
-    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    const uint64_t tid = (uint64_t)blockIdx.x * B + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * B;
     constexpr uint64_t E = T::ESZ;
     const uint64_t body = a.g.head * E;
     const uint64_t nv = a.g.nvb;

@@ -26,6 +26,10 @@ template __global__ void vrc::k_fused_allreduce<vrc::F16, {N}, 2, true, vrc::Ran
 template __global__ void vrc::k_fused_allreduce<vrc::F32, {N}, 2, true, vrc::RankFold>(vrc::FusedArArgs);
 template __global__ void vrc::k_fused_allreduce<vrc::I32, {N}, 2, true, vrc::RankFold>(vrc::FusedArArgs);
 template __global__ void vrc::k_fused_allreduce<vrc::F32, {N}, 2, true, vrc::Butterfly>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_allreduce<vrc::BF16, {N}, 1, true, vrc::RankFold, 64>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_allreduce<vrc::F32, {N}, 1, true, vrc::Butterfly, 64>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_allreduce<vrc::I32, 4, 2, true, vrc::RankFold, 64>(vrc::FusedArArgs);
+template __global__ void vrc::k_fused_allreduce<vrc::F16, 16, 1, true, vrc::RankFold, 64>(vrc::FusedArArgs);
 template __global__ void vrc::k_fused_reduce_scatter<vrc::F32, {N}, true, vrc::RankFold>(vrc::FusedRsArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::F32, {N}, false, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, true, true>(vrc::ChainArgs);
@@ -100,6 +104,10 @@ def longest_load_run(text):
     (r"k_fused_allreduceINS_3F32ELi8ELi2ELb1ENS_8RankFold", 2 * N),
     (r"k_fused_allreduceINS_3I32ELi8ELi2ELb1ENS_8RankFold", 2 * N),
     (r"k_fused_allreduceINS_3F32ELi8ELi2ELb1ENS_9Butterfly", 2 * N),
+    (r"k_fused_allreduceINS_4BF16ELi8ELi1ELb1ENS_8RankFoldELi64", N),
+    (r"k_fused_allreduceINS_3F32ELi8ELi1ELb1ENS_9ButterflyELi64", N),
+    (r"k_fused_allreduceINS_3I32ELi4ELi2ELb1ENS_8RankFoldELi64", 8),
+    (r"k_fused_allreduceINS_3F16ELi16ELi1ELb1ENS_8RankFoldELi64", 16),
     (r"k_fused_reduce_scatterINS_3F32ELi8ELb1ENS_8RankFold", N),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0", N),
     (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1", N),
@@ -108,8 +116,8 @@ def longest_load_run(text):
     (r"k_ring_stepINS_3F32ELb1ELb0ELi8", 2),
 ])
 def test_single_pass_kernels_keep_all_loads_in_flight(asm, pattern, loads):
-    """Every lane issues all of its loads (2N with two vectors per rank) before
-    it waits for the first one.  A compiler that interleaves the fold with
+    """Every lane issues all of its loads (N per vector per rank it keeps in
+    flight) before it waits for the first one.  A compiler that interleaves the fold with
     the loads leaves two in flight and runs the 8 x 512 MiB fused all-reduce
     at 3.8 TB/s instead of 5.4.  A ring step's chunk-add has both of its
     operands in flight together."""

@@ -318,3 +318,29 @@ def test_step_launch_shapes(vrc, orc, n, count, dtype, modes):
             assert_bitwise(got, want, f"{mode} {dtype} n={n} count={count} rank {r} sampled")
         del ys
         torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# fused all-reduce launch shapes: from 64 MiB moved the workgroup count and
+# the vectors each lane keeps in flight depend on the rank count; every rank
+# count 2..16 at a ragged size above that limit, on misaligned views too
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", list(range(2, 17)))
+def test_fused_launch_shapes(vrc, orc, n):
+    dtype = ("fp32", "bf16", "fp16", "int32")[n % 4]
+    esz = 2 if dtype in ("fp16", "bf16") else 4
+    count = (64 << 20) // (2 * n * esz) + 4099  # just above 64 MiB moved, not a whole number of vectors
+    say(f"fused shapes n={n} count={count} {dtype}")
+    base = workloads.random_ranks(n, count + 1, dtype, seed=700 + n, device=DEV, sigma=1e-2)
+    modes = ("fused", "hd_order") if pow2(n) else ("fused",)
+    for offset in (0, 1):  # offset 1: every buffer starts one element past a 16-byte boundary
+        xs = [b[offset:offset + count] for b in base]
+        hx = host(xs)
+        for mode in modes:
+            ys = vrc.vrc_allreduce(xs, mode=mode)
+            torch.cuda.synchronize()
+            ranks_identical(ys, f"{mode} n={n} offset={offset}")
+            want = want_ar(orc, hx, dtype, mode)
+            for r in (0, n - 1):
+                assert_bitwise(workloads.to_numpy(ys[r]), want[r], f"{mode} {dtype} n={n} offset={offset} rank {r}")
+            del ys
