@@ -73,11 +73,13 @@ int env_int(const char* name, int dflt, int lo, int hi)
 
 // Launch shape, from measurements on MI355X (HIP events):
 //  - fused all-reduce: one-wave workgroups sized to the rank count
-//    (fused_ar_shape);
-//  - fused reduce-scatter and all-gather: 256-lane workgroups, one per CU
-//    (two at 2 ranks) once the whole operation moves >= 4 GiB, 2 per CU from
-//    1 GiB, 8 per CU below that, where the Infinity Cache holds much of the
-//    data and latency hiding matters more than open DRAM rows;
+//    (fused_ar_shape); single-launch ring all-reduce: one-wave workgroups
+//    (chain_ar_shape);
+//  - fused reduce-scatter: 256-lane workgroups, one per CU (two at 2 ranks)
+//    once the whole operation moves >= 4 GiB, 2 per CU from 1 GiB, 8 per CU
+//    below that, where the Infinity Cache holds much of the data and latency
+//    hiding matters more than open DRAM rows; fused all-gather: 16 per CU
+//    (ag_blocks_per_cu);
 //  - ring and halving-doubling steps: by the bytes a step moves and its number
 //    of per-rank operations (step_shape), workgroups counted over all of them.
 // Loads and stores carry the non-temporal hint (measured faster for this
@@ -93,6 +95,7 @@ struct Tuning {
                               // 2: non-temporal adds and regular copies
     int step_unroll;          // 0: size policy; else vectors per lane per step iteration (1 or 2)
     int fused_block;          // 0: size policy; else lanes per fused all-reduce workgroup (64 or 256)
+    int chain_block;          // 0: policy; else lanes per single-launch ring all-reduce workgroup (64 or 256)
 };
 
 const Tuning& tuning()
@@ -101,7 +104,7 @@ const Tuning& tuning()
                              env_int("VRC_STEP_BLOCKS_PER_CU", 0, 1, 64),
                              env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 0, 1, 2),
                              env_int("VRC_STEP_NT", -1, 0, 2), env_int("VRC_STEP_UNROLL", 0, 1, 2),
-                             env_int("VRC_FUSED_BLOCK", 0, 64, 256)};
+                             env_int("VRC_FUSED_BLOCK", 0, 64, 256), env_int("VRC_CHAIN_BLOCK", 0, 64, 256)};
     return t;
 }
 
@@ -213,23 +216,51 @@ bool step_nontemporal(bool add, uint64_t bytes_moved)
     return add || bytes_moved / 2 > 64 * kMiB;
 }
 
-// The single-launch ring with partials in registers (VRC_RING_ORDER) walks
-// wave-sized tiles and does best with few workgroups at every size: 2 per CU
-// from 1 GiB to 4 GiB moved, 1 otherwise (8 x 16 MiB fp32: 53.5 us at 1 per
-// CU against 58.0 us at 8).
-int order_blocks_per_cu(uint64_t bytes_moved, int n)
+// The fused all-gather reads each input once and stores it N times: 16
+// workgroups per CU at every size.  Measured on MI355X in one process on the
+// same buffers (us, 8 / 16 per CU): 8 x 5 MiB fp16 heads 77.2 / 75.2 and
+// 81.4 / 77.0 (cache flushed); 8 x 64 MiB 953 / 943; 16 x 5 MiB 292 / 289;
+// 4 x 5 MiB 24.6 / 24.8.  One-wave workgroups were slower (79-89 us on the
+// heads).
+int ag_blocks_per_cu()
 {
     if (tuning().fused_blocks_per_cu) return tuning().fused_blocks_per_cu;
-    if (n <= 2) return 2;  // 2 ranks, 8 GiB moved: 1.57-1.58 ms against 2.19 ms at one per CU
-    return (bytes_moved >= kGiB && bytes_moved < 4 * kGiB) ? 2 : 1;
+    return 16;
 }
 
 // Memory-faithful chains wait on their own stores between steps, so they
-// need more resident waves than the fused loop to hide latency.
+// need more resident waves than the fused loop to hide latency.  This shape
+// serves the single-launch reduce-scatter and all-gather relays (256-lane
+// workgroups).
 int chain_blocks_per_cu(uint64_t bytes_moved)
 {
     if (tuning().chain_blocks_per_cu) return tuning().chain_blocks_per_cu;
     return bytes_moved >= 4 * kGiB ? 4 : 8;
+}
+
+// Launch shape of the single-launch ring all-reduce.  Like the fused kernel
+// it runs one-wave workgroups, so consecutive wave tiles go to different
+// XCDs.  The ring-order kernel (partials in registers, N loads in flight per
+// lane) uses 4 per CU (8 at 2 ranks); the memory-faithful chain, whose lanes
+// wait on their own stores at every step, uses 16.  Measured on MI355X in one
+// process on the same buffers (GB/s of 2·N·S; 256-lane shape -> this one):
+//   ring order:  8 x 512 MiB 5,498 -> 5,565; 8 x 128 MiB 5,304 -> 5,663;
+//                8 x 16 MiB (cache flushed) 5,077 -> 5,187; 16 x 256 MiB 5,262 -> 5,259;
+//                2 x 2 GiB 5,485 -> 5,493; 4 x 1 GiB 5,420 -> 5,297;
+//   chained:     8 x 512 MiB 4,521 -> 4,835; 8 x 16 MiB 3,779 -> 4,012;
+//                4 x 1 GiB 4,790 -> 4,846; 2 x 2 GiB 4,857 -> 4,999.
+struct ChainShape {
+    int block;
+    int blocks_per_cu;
+};
+
+ChainShape chain_ar_shape(bool mem, int n)
+{
+    ChainShape s = {64, mem ? 16 : (n <= 2 ? 8 : 4)};
+    if (mem && tuning().chain_blocks_per_cu) s.blocks_per_cu = tuning().chain_blocks_per_cu;
+    if (!mem && tuning().fused_blocks_per_cu) s.blocks_per_cu = tuning().fused_blocks_per_cu;
+    if (tuning().chain_block) s.block = tuning().chain_block == 256 ? kBlock : 64;
+    return s;
 }
 
 #define VRC_FOR_N(X) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
@@ -728,7 +759,7 @@ struct Launch {
             const uint64_t w = outer * (a.g[q].nvb + a.g[q].head + a.g[q].tail);
             if (w > work) work = w;
         }
-        const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * n * count * E, n)), (unsigned)n);
+        const dim3 grid(grid_x(cus, work, n, ag_blocks_per_cu()), (unsigned)n);
         hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
         return check_launch();
     }
@@ -881,12 +912,16 @@ struct Launch {
         // At least one wave per chunk for the scalar head/tail pass.
         const uint64_t lanes = a.tile0[n] * 64, scalar_lanes = (uint64_t)n * 64;
         const uint64_t work = lanes > scalar_lanes ? lanes : scalar_lanes;
-        const uint64_t bytes = MEM ? 5 * (uint64_t)(n - 1) * count * E : 2 * (uint64_t)n * count * E;
-        const int bpc = MEM ? chain_blocks_per_cu(bytes) : order_blocks_per_cu(bytes, n);
-        const dim3 grid(grid_x(cus, work, 1, bpc));
+        const ChainShape sh = chain_ar_shape(MEM, n);
+        const dim3 grid(grid_x(cus, work, 1, sh.blocks_per_cu, sh.block));
         switch (n) {
-#define VRC_CASE(K) \
-    case K: hipLaunchKernelGGL((vrc::k_ring_chain_allreduce<T, K, MEM, true>), grid, dim3(kBlock), 0, st, a); break;
+#define VRC_CASE(K)                                                                                      \
+    case K:                                                                                              \
+        if (sh.block == 64)                                                                              \
+            hipLaunchKernelGGL((vrc::k_ring_chain_allreduce<T, K, MEM, true, 64>), grid, dim3(64), 0, st, a); \
+        else                                                                                             \
+            hipLaunchKernelGGL((vrc::k_ring_chain_allreduce<T, K, MEM, true>), grid, dim3(kBlock), 0, st, a); \
+        break;
             VRC_FOR_N(VRC_CASE)
 #undef VRC_CASE
         default: return VRC_ERR_INVALID_ARG;

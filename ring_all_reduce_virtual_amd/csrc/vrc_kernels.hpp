@@ -456,14 +456,14 @@ __device__ __forceinline__ void rotate_ranks(const ChainArgs& a, int c, const ch
 // the chunk (and with it the ring order) is uniform across the wave; a wave
 // reloads the chunk's geometry and rotated rank pointers only when its next
 // tile lies in another chunk.
-template <class T, int N, bool MEM, bool NT>
-__global__ __launch_bounds__(kBlock) void k_ring_chain_allreduce(ChainArgs a)
+template <class T, int N, bool MEM, bool NT, int B = kBlock>
+__global__ __launch_bounds__(B) void k_ring_chain_allreduce(ChainArgs a)
 {
     constexpr uint64_t W = 64;
     constexpr uint64_t E = T::ESZ;
     const uint64_t lane = threadIdx.x % W;
-    const uint64_t wave = (uint64_t)blockIdx.x * (kBlock / W) + threadIdx.x / W;
-    const uint64_t nwaves = (uint64_t)gridDim.x * (kBlock / W);
+    const uint64_t wave = (uint64_t)blockIdx.x * (B / W) + threadIdx.x / W;
+    const uint64_t nwaves = (uint64_t)gridDim.x * (B / W);
     const uint64_t ntiles = a.tile0[N];
     const char* in[N];
     char* out[N];

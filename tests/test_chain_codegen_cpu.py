@@ -34,6 +34,8 @@ template __global__ void vrc::k_fused_reduce_scatter<vrc::F32, {N}, true, vrc::R
 template __global__ void vrc::k_ring_chain_allreduce<vrc::F32, {N}, false, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, true, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, false, true>(vrc::ChainArgs);
+template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, true, true, 64>(vrc::ChainArgs);
+template __global__ void vrc::k_ring_chain_allreduce<vrc::F32, {N}, false, true, 64>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_reduce_scatter<vrc::F16, {N}, true, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_all_gather<vrc::F32, {N}, true>(vrc::FusedAgArgs);
 template __global__ void vrc::k_ring_step<vrc::BF16, true, true, 8>(vrc::StepArgsK<8>);
@@ -73,8 +75,10 @@ def count(text, op):
 
 
 @pytest.mark.parametrize("pattern,loads,stores", [
-    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1", 3 * N - 3, 2 * (N - 1)),
-    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb0", N, N),
+    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1ELb1ELi256", 3 * N - 3, 2 * (N - 1)),
+    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb0ELb1ELi256", N, N),
+    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1ELb1ELi64", 3 * N - 3, 2 * (N - 1)),
+    (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi64", N, N),
     (r"k_ring_chain_reduce_scatterINS_3F16ELi8ELb1", 2 * (N - 1), N - 1),
     (r"k_ring_chain_all_gatherINS_3F32ELi8", N - 1, N),
 ])
@@ -109,8 +113,10 @@ def longest_load_run(text):
     (r"k_fused_allreduceINS_3I32ELi4ELi2ELb1ENS_8RankFoldELi64", 8),
     (r"k_fused_allreduceINS_3F16ELi16ELi1ELb1ENS_8RankFoldELi64", 16),
     (r"k_fused_reduce_scatterINS_3F32ELi8ELb1ENS_8RankFold", N),
-    (r"k_ring_chain_allreduceINS_3F32ELi8ELb0", N),
-    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1", N),
+    (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi256", N),
+    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1ELb1ELi256", N),
+    (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi64", N),
+    (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1ELb1ELi64", N),
     (r"k_ring_chain_reduce_scatterINS_3F16ELi8ELb1", N),
     (r"k_ring_stepINS_4BF16ELb1ELb1ELi8", 2),
     (r"k_ring_stepINS_3F32ELb1ELb0ELi8", 2),
