@@ -1,10 +1,12 @@
 // vrc_kernels.hpp -- HIP kernels (gfx950) for the virtual-rank collectives.
 //
-// All kernels are bandwidth-bound streaming loops: 256-lane workgroups (four
-// wave64s), a grid sized to the CU count, grid-stride iteration over 16-byte
-// vectors, and a scalar pass for the elements before the first 16-byte
-// boundary and after the last one.  No MFMA: the work is a sum, not a
-// contraction.
+// All kernels are bandwidth-bound streaming loops: a grid sized to the CU
+// count, grid-stride iteration over 16-byte vectors, and a scalar pass for
+// the elements before the first 16-byte boundary and after the last one.
+// Workgroups have 256 lanes (four wave64s), except in the all-reduce kernels
+// that read every rank at once (fused and single-launch ring), which the host
+// may launch with workgroups of one wave (template argument B = 64).  No MFMA:
+// the work is a sum, not a contraction.
 //
 // Geometry.  An operand region is `rows` rows of `width` elements with a row
 // stride in elements.  The host splits each row into `head` scalar elements
@@ -124,7 +126,9 @@ __global__ __launch_bounds__(kBlock) void k_ring_step(StepArgsK<K> args)
 // them in rank order in the accumulator, rounds once and writes the result
 // to all N outputs.  Reads precede writes within a lane, so in-place calls
 // are safe.  U independent vectors per lane per iteration keep U*N 16-byte
-// loads in flight.
+// loads in flight.  B lanes per workgroup: with B = 64 consecutive 1 KiB
+// wave tiles belong to consecutive workgroups, which the hardware hands to
+// different XCDs in turn.
 // ---------------------------------------------------------------------------
 struct FusedArArgs {
     const char* src[kMaxRanks];
@@ -331,7 +335,9 @@ __global__ __launch_bounds__(kBlock) void k_fused_all_gather(FusedAgArgs a)
 // all-gather relays the finished chunk from rank c-1 to c, c+1, ..., c+N-2.
 // Each element is therefore an independent chain of 2(N-1) operations, and
 // one launch can run every chain to the end with no grid-wide barrier.
-// blockIdx.y = chunk c, so the rank rotation is uniform per workgroup.
+// The all-reduce chain walks wave tiles that never cross a chunk; the
+// reduce-scatter chain takes blockIdx.y = chunk c.  Either way the rank
+// rotation is uniform per wave.
 //
 // MEM = true ("chained"): every step writes its partial into the next
 // rank's buffer and the following step reads it back from there, so the
