@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define VRC_VERSION 100 /* 1.0.0 */
+#define VRC_VERSION 101 /* 1.0.1: vrc_op_desc reports the launch geometry */
 #define VRC_MAX_RANKS 16
 
 struct ihipStream_t;
@@ -210,7 +210,7 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
  * d = a, over `rows` rows of `width` elements with the given row strides in
  * elements; a, b and d point at element (0,0) of the operands inside the
  * caller's buffers).  Single-launch kernels give one entry per launch with
- * only `kind`, `launch` and width = count set.  Arguments are validated as
+ * only `kind`, `launch`, width = count and the launch geometry set.  Arguments are validated as
  * in the real call.  If more than `cap` entries are needed the first `cap`
  * are written, *n_ops receives the full count and VRC_ERR_INVALID_ARG is
  * returned.  Used by the tests to check the schedules on the CPU, and for
@@ -241,6 +241,12 @@ typedef struct {
     void* d;               /* destination */
     size_t rows, width;    /* elements */
     size_t stride_a, stride_b, stride_d; /* row strides, elements (rows > 1) */
+    /* Launch geometry of the kernel launch, the same in every entry of one
+     * launch, computed for a device of 256 CUs (MI355X; a real call uses the
+     * device's own CU count): workgroups in x and y, lanes per workgroup, and
+     * 16-byte vectors per rank (per operand for a ring step) that a lane of
+     * the main loop keeps in flight. */
+    unsigned grid_x, grid_y, block, vectors;
 } vrc_op_desc;
 
 vrc_status_t vrc_plan(vrc_coll_t coll, const void* const* send, void* const* recv, int nranks, size_t count,

@@ -49,11 +49,15 @@ class VrcError(RuntimeError):
         self.status = status
 
 
+ABI_VERSION = 101  # VRC_VERSION of include/vrc.h that these mirrors follow
+
+
 class OpDesc(C.Structure):
     """One operation of a launch plan (vrc_op_desc in include/vrc.h)."""
     _fields_ = [("launch", C.c_int), ("kind", C.c_int), ("a", C.c_void_p), ("b", C.c_void_p), ("d", C.c_void_p),
                 ("rows", C.c_size_t), ("width", C.c_size_t), ("stride_a", C.c_size_t), ("stride_b", C.c_size_t),
-                ("stride_d", C.c_size_t)]
+                ("stride_d", C.c_size_t), ("grid_x", C.c_uint), ("grid_y", C.c_uint), ("block", C.c_uint),
+                ("vectors", C.c_uint)]
 
 
 COLL_ALLREDUCE, COLL_REDUCE_SCATTER, COLL_ALL_GATHER = 0, 1, 2
@@ -95,6 +99,11 @@ def _load():
     L.vrc_last_hip_error.restype = i
     L.vrc_version.argtypes = []
     L.vrc_version.restype = i
+    if L.vrc_version() != ABI_VERSION:
+        # OpDesc mirrors vrc_op_desc of this version; another layout would
+        # be read (or written by vrc_plan) with the wrong size.
+        raise ImportError(f"{LIB_PATH} reports ABI version {L.vrc_version()}, this binding needs {ABI_VERSION}: "
+                          "rebuild the library")
     return L
 
 
@@ -133,7 +142,8 @@ def raw_all_gather(send, recv, count, outer, dtype, mode, stream=0) -> int:
 
 def plan(coll: int, send, recv, count: int, outer: int, dtype: int, mode: int):
     """The operations a call would enqueue (host only, nothing launched):
-    a list of dicts with launch, kind, a, b, d, rows, width and strides."""
+    a list of dicts with launch, kind, a, b, d, rows, width, strides and the
+    launch geometry (grid_x, grid_y, block, vectors) for a 256-CU device."""
     cap = 4096
     ops = (OpDesc * cap)()
     n_ops, n_launches = C.c_int(), C.c_int()
@@ -146,7 +156,8 @@ def plan(coll: int, send, recv, count: int, outer: int, dtype: int, mode: int):
         o = ops[k]
         out.append({"launch": o.launch, "kind": OP_KINDS[o.kind], "a": o.a or 0, "b": o.b or 0, "d": o.d or 0,
                     "rows": o.rows, "width": o.width, "stride_a": o.stride_a, "stride_b": o.stride_b,
-                    "stride_d": o.stride_d})
+                    "stride_d": o.stride_d, "grid_x": o.grid_x, "grid_y": o.grid_y, "block": o.block,
+                    "vectors": o.vectors})
     return out, n_launches.value
 
 

@@ -43,14 +43,18 @@ void plan_op(const vrc_op_desc& op)
     g_plan->n++;
 }
 
-// A single-launch kernel: one entry with only its kind and size.
-vrc_status_t plan_single(vrc_op_kind_t kind, uint64_t count)
+// A single-launch kernel: one entry with its kind, size and launch geometry.
+vrc_status_t plan_single(vrc_op_kind_t kind, uint64_t count, dim3 grid, int block, int vectors)
 {
     vrc_op_desc op = {};
     op.launch = g_plan->launches++;
     op.kind = kind;
     op.rows = 1;
     op.width = count;
+    op.grid_x = grid.x;
+    op.grid_y = grid.y;
+    op.block = (unsigned)block;
+    op.vectors = (unsigned)vectors;
     plan_op(op);
     return VRC_OK;
 }
@@ -424,6 +428,9 @@ struct Launch {
     template <bool ADD>
     static vrc_status_t step(const vrc::StepArgs& args, int nops, uint64_t work, int cus, hipStream_t st)
     {
+        const uint64_t bytes = step_bytes<ADD>(args, nops);
+        const StepShape shape = step_shape(bytes, nops);
+        const dim3 grid(grid_x(cus, work, nops, shape.blocks_per_cu), (unsigned)nops);
         if (g_plan) {
             for (int i = 0; i < nops; i++) {
                 const vrc::StepOp& o = args.op[i];
@@ -438,14 +445,15 @@ struct Launch {
                 op.stride_a = o.sa;
                 op.stride_b = ADD ? o.sb : 0;
                 op.stride_d = o.sd;
+                op.grid_x = grid.x;
+                op.grid_y = grid.y;
+                op.block = kBlock;
+                op.vectors = (unsigned)shape.unroll;
                 plan_op(op);
             }
             g_plan->launches++;
             return VRC_OK;
         }
-        const uint64_t bytes = step_bytes<ADD>(args, nops);
-        const StepShape shape = step_shape(bytes, nops);
-        const dim3 grid(grid_x(cus, work, nops, shape.blocks_per_cu), (unsigned)nops);
         const bool nt = step_nontemporal(ADD, bytes);
         const bool u2 = shape.unroll == 2;
         if (nops <= 4) launch_step<ADD, 4>(args, nops, nt, u2, grid, st);
@@ -639,10 +647,6 @@ struct Launch {
                                         hipStream_t st)
     {
         if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
-        if (g_plan)
-            return plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_ALLREDUCE
-                                                                          : VRC_OP_FUSED_ALLREDUCE,
-                               count);
         vrc::FusedArArgs a;
         uintptr_t addr[2 * kMaxRanks];
         for (int r = 0; r < n; r++) {
@@ -660,6 +664,10 @@ struct Launch {
         const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
         const FusedShape sh = fused_ar_shape(2 * (uint64_t)n * count * E, n);
         const dim3 grid(grid_x(cus, work, 1, sh.blocks_per_cu, sh.block));
+        if (g_plan)
+            return plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_ALLREDUCE
+                                                                          : VRC_OP_FUSED_ALLREDUCE,
+                               count, grid, sh.block, sh.unroll);
         if constexpr (std::is_same<Fold, vrc::Butterfly>::value) {
             switch (n) {
             case 2: launch_fused_ar_n<2, Fold>(a, grid, sh, st); break;
@@ -691,10 +699,6 @@ struct Launch {
                                              uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
-        if (g_plan)
-            return plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_REDUCE_SCATTER
-                                                                          : VRC_OP_FUSED_REDUCE_SCATTER,
-                               count);
         vrc::FusedRsArgs a;
         uint64_t work = 0;
         for (int r = 0; r < kMaxRanks; r++) a.src[r] = r < n ? x[r] : nullptr;
@@ -716,6 +720,10 @@ struct Launch {
             if (w > work) work = w;
         }
         const dim3 grid(grid_x(cus, work, n, fused_blocks_per_cu((uint64_t)(n + 1) * count * E, n)), (unsigned)n);
+        if (g_plan)
+            return plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_REDUCE_SCATTER
+                                                                          : VRC_OP_FUSED_REDUCE_SCATTER,
+                               count, grid, kBlock, 1);
         if constexpr (std::is_same<Fold, vrc::Butterfly>::value) {
             switch (n) {
             case 2: launch_fused_rs_n<2, Fold>(a, grid, st); break;
@@ -739,7 +747,6 @@ struct Launch {
     static vrc_status_t fused_all_gather(const char* const* x, char* const* y, int n, uint64_t count,
                                          uint64_t outer, int cus, hipStream_t st)
     {
-        if (g_plan) return plan_single(VRC_OP_FUSED_ALL_GATHER, count);
         vrc::FusedAgArgs a;
         const uint64_t row = count / outer;
         a.rows = outer;
@@ -760,6 +767,7 @@ struct Launch {
             if (w > work) work = w;
         }
         const dim3 grid(grid_x(cus, work, n, ag_blocks_per_cu()), (unsigned)n);
+        if (g_plan) return plan_single(VRC_OP_FUSED_ALL_GATHER, count, grid, kBlock, 1);
         hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
         return check_launch();
     }
@@ -890,7 +898,6 @@ struct Launch {
                                         hipStream_t st)
     {
         if (n == 1) return x[0] == y[0] ? VRC_OK : copy(x[0], y[0], 1, count, 0, 0, cus, st);
-        if (g_plan) return plan_single(MEM ? VRC_OP_CHAIN_ALLREDUCE : VRC_OP_RING_ORDER_ALLREDUCE, count);
         vrc::ChainArgs a = {};
         for (int r = 0; r < kMaxRanks; r++) {
             a.src[r] = r < n ? x[r] : nullptr;
@@ -914,6 +921,8 @@ struct Launch {
         const uint64_t work = lanes > scalar_lanes ? lanes : scalar_lanes;
         const ChainShape sh = chain_ar_shape(MEM, n);
         const dim3 grid(grid_x(cus, work, 1, sh.blocks_per_cu, sh.block));
+        if (g_plan)
+            return plan_single(MEM ? VRC_OP_CHAIN_ALLREDUCE : VRC_OP_RING_ORDER_ALLREDUCE, count, grid, sh.block, 1);
         switch (n) {
 #define VRC_CASE(K)                                                                                      \
     case K:                                                                                              \
@@ -934,8 +943,6 @@ struct Launch {
                                              uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
-        if (g_plan)
-            return plan_single(MEM ? VRC_OP_CHAIN_REDUCE_SCATTER : VRC_OP_RING_ORDER_REDUCE_SCATTER, count);
         vrc::ChainArgs a = {};
         uint64_t work = 0;
         for (int r = 0; r < kMaxRanks; r++) {
@@ -955,6 +962,9 @@ struct Launch {
         const uint64_t bytes = MEM ? 3 * (uint64_t)(n - 1) * count * E : (uint64_t)(n + 1) * count * E;
         const int bpc = MEM ? chain_blocks_per_cu(bytes) : fused_blocks_per_cu(bytes, n);
         const dim3 grid(grid_x(cus, work, n, bpc), (unsigned)n);
+        if (g_plan)
+            return plan_single(MEM ? VRC_OP_CHAIN_REDUCE_SCATTER : VRC_OP_RING_ORDER_REDUCE_SCATTER, count, grid,
+                               kBlock, 1);
         switch (n) {
 #define VRC_CASE(K) \
     case K:         \
@@ -970,7 +980,6 @@ struct Launch {
                                          uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
-        if (g_plan) return plan_single(VRC_OP_CHAIN_ALL_GATHER, count);
         vrc::FusedAgArgs a;
         const uint64_t row = count / outer;
         a.rows = outer;
@@ -991,6 +1000,7 @@ struct Launch {
             if (w > work) work = w;
         }
         const dim3 grid(grid_x(cus, work, n, chain_blocks_per_cu(2 * (uint64_t)n * n * count * E)), (unsigned)n);
+        if (g_plan) return plan_single(VRC_OP_CHAIN_ALL_GATHER, count, grid, kBlock, 1);
         switch (n) {
 #define VRC_CASE(K) \
     case K: hipLaunchKernelGGL((vrc::k_ring_chain_all_gather<T, K, true>), grid, dim3(kBlock), 0, st, a); break;

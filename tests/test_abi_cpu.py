@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert vrc.version() == 100
+    assert vrc.version() == 101 == vrc.ABI_VERSION
     for st in range(5):
         assert vrc.lib().vrc_status_string(st).decode().startswith("VRC_")
     assert b"unknown" in vrc.lib().vrc_status_string(99)

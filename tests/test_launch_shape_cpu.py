@@ -1,0 +1,182 @@
+"""The library's launch shapes, checked on the CPU through vrc_plan (which
+reports each launch's geometry for a 256-CU device and launches nothing).
+
+These are the host-side rules behind the measured performance: one-wave
+workgroups and a loads-in-flight budget for the fused all-reduce from 64 MiB
+moved, one-wave workgroups for the single-launch ring all-reduce, 16
+workgroups per CU for the fused all-gather, and the ring step shapes by size
+and operation count.  The environment overrides are checked in a child
+process, since the library reads them once."""
+import ctypes as C
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+import ring_all_reduce_virtual_amd as vrc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CUS = 256
+ESZ = {vrc.VRC_INT32: 4, vrc.VRC_FP32: 4, vrc.VRC_FP16: 2, vrc.VRC_BF16: 2}
+
+
+def wide(n):
+    """Stand-in rank addresses 4 GiB apart (256-byte aligned)."""
+    return [(1 << 40) + r * (1 << 32) for r in range(n)], [(1 << 42) + r * (1 << 32) for r in range(n)]
+
+
+def gather_out(n, count, esz):
+    """All-gather outputs hold n * count elements each: space them further apart."""
+    return [(1 << 44) + r * ((n * count * esz + (1 << 32)) // (1 << 32) * (1 << 32)) for r in range(n)]
+
+
+def launches(ops):
+    """One geometry per launch: (kind, grid_x, grid_y, block, vectors), in launch order."""
+    out = {}
+    for op in ops:
+        g = (op["kind"], op["grid_x"], op["grid_y"], op["block"], op["vectors"])
+        assert out.setdefault(op["launch"], g) == g, "operations of one launch disagree on its geometry"
+    return [out[k] for k in sorted(out)]
+
+
+def plan_ar(n, count, dtype, mode):
+    send, recv = wide(n)
+    ops, nl = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, dtype, mode)
+    got = launches(ops)
+    assert len(got) == nl
+    return got
+
+
+def budget_blocks_per_cu(n, vectors):
+    """Largest power of two <= 8 with workgroups x ranks x vectors <= 32."""
+    b = 8
+    while b > 1 and b * n * vectors > 32:
+        b //= 2
+    return b
+
+
+def test_op_desc_layout_matches_the_header():
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    src = os.path.join(ROOT, "tests", "_sizeof_op_desc.c")
+    exe = os.path.join(ROOT, "tests", "_sizeof_op_desc")
+    try:
+        with open(src, "w") as fh:
+            fh.write('#include <stdio.h>\n#include <stddef.h>\n#include "vrc.h"\n'
+                     'int main(void) { printf("%zu %zu %zu\\n", sizeof(vrc_op_desc), '
+                     'offsetof(vrc_op_desc, grid_x), offsetof(vrc_op_desc, vectors)); return 0; }\n')
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", exe, src], check=True)
+        size, off_grid, off_vec = map(int, subprocess.run([exe], check=True, capture_output=True,
+                                                          text=True).stdout.split())
+    finally:
+        for p in (src, exe):
+            if os.path.exists(p):
+                os.remove(p)
+    assert C.sizeof(vrc.OpDesc) == size
+    assert vrc.OpDesc.grid_x.offset == off_grid and vrc.OpDesc.vectors.offset == off_vec
+
+
+@pytest.mark.parametrize("n", list(range(2, 17)))
+def test_fused_allreduce_one_wave_budget(n):
+    """8 GiB moved: one-wave workgroups, two vectors per rank at 3-4 ranks,
+    workgroups per CU from the 32-loads budget (8 at 2 ranks, 4 at 3-8,
+    2 at 9-16)."""
+    count = (4 << 30) // n // 2 // 64 * 64
+    vectors = 2 if n in (3, 4) else 1
+    bpc = budget_blocks_per_cu(n, vectors)
+    assert bpc == (8 if n == 2 else 4 if n <= 8 else 2)
+    got = plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_FUSED)
+    assert got == [("fused_allreduce", CUS * bpc, 1, 64, vectors)]
+    if n & (n - 1) == 0 and n > 2:  # halving-doubling in one launch: the same kernel with the butterfly fold
+        assert plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_HD_ORDER) == [("butterfly_allreduce", CUS * bpc, 1, 64,
+                                                                      vectors)]
+
+
+def test_headline_shape():
+    """8 ranks x 512 MiB bf16: 1,024 one-wave workgroups, one vector per rank per lane."""
+    assert plan_ar(8, 268435456, vrc.VRC_BF16, vrc.VRC_FUSED) == [("fused_allreduce", 1024, 1, 64, 1)]
+
+
+def test_fused_allreduce_launch_bound_shape_below_64_mib():
+    """Exactly 64 MiB moved takes the one-wave shape; one vector less keeps
+    256-lane workgroups, 8 per CU, two vectors per rank."""
+    n, esz = 8, 2
+    at = (64 << 20) // (2 * n * esz)
+    assert plan_ar(n, at, vrc.VRC_BF16, vrc.VRC_FUSED) == [("fused_allreduce", 1024, 1, 64, 1)]
+    below = at - 8
+    nv = below * esz // 16
+    assert plan_ar(n, below, vrc.VRC_BF16, vrc.VRC_FUSED) == [
+        ("fused_allreduce", min((nv + 255) // 256, CUS * 8), 1, 256, 2)]
+    small = plan_ar(n, 524288, vrc.VRC_FP16, vrc.VRC_FUSED)  # 8 x 1 MiB fp16
+    assert small == [("fused_allreduce", 524288 * 2 // 16 // 256, 1, 256, 2)]
+
+
+@pytest.mark.parametrize("n,per_cu_order", [(2, 8), (3, 4), (8, 4), (16, 4)])
+def test_single_launch_ring_one_wave(n, per_cu_order):
+    """Ring order: one-wave workgroups, 4 per CU (8 at 2 ranks); the
+    memory-faithful chain: 16 per CU."""
+    count = (4 << 30) // n // 2 // 64 * 64
+    assert plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_RING_ORDER) == [
+        ("ring_order_allreduce", CUS * per_cu_order, 1, 64, 1)]
+    assert plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_RING_CHAINED) == [("chain_allreduce", CUS * 16, 1, 64, 1)]
+
+
+def test_single_launch_ring_small_grid_covers_every_chunk():
+    """4 x 4,099 int32: the grid is sized to the tiles (one per wave) and
+    never below one wave per chunk for the scalar pass."""
+    got = plan_ar(4, 4099, vrc.VRC_INT32, vrc.VRC_RING_ORDER)
+    (kind, gx, gy, block, vectors), = got
+    assert (kind, gy, block, vectors) == ("ring_order_allreduce", 1, 64, 1)
+    tiles = sum((ln * 4 // 16 + 63) // 64 for ln in (1024, 1024, 1024, 1027))
+    assert gx == max(tiles, 4)
+
+
+def test_fused_all_gather_sixteen_per_cu():
+    """8 x [1, 5, 4096, 128] fp16 heads: 256-lane workgroups, 16 per CU over
+    the 8 source rows."""
+    n, count, esz = 8, 5 * 4096 * 128, 2
+    send, _ = wide(n)
+    recv = gather_out(n, count, esz)
+    ops, nl = vrc.plan(vrc.COLL_ALL_GATHER, send, recv, count, 1, vrc.VRC_FP16, vrc.VRC_FUSED)
+    nv = count * esz // 16
+    assert nl == 1
+    assert launches(ops) == [("fused_all_gather", min((nv + 255) // 256, CUS * 16 // n), n, 256, 1)]
+
+
+@pytest.mark.parametrize("n,count,dtype,per_cu,vectors", [
+    (8, 268435456, vrc.VRC_BF16, 8, 2),    # 8 operations of >= 128 MiB: two vectors, 8 per CU
+    (4, 536870912, vrc.VRC_BF16, 4, 1),    # <= 7 operations of >= 48 MiB: one vector, 4 per CU
+    (16, 134217728, vrc.VRC_BF16, 16, 2),  # >= 12 operations: two vectors, 16 per CU
+])
+def test_ring_step_shapes(n, count, dtype, per_cu, vectors):
+    got = plan_ar(n, count, dtype, vrc.VRC_RING)
+    assert len(got) == 2 * (n - 1)
+    for kind, gx, gy, block, vec in got:
+        assert kind in ("add", "copy")
+        assert (gx, gy, block, vec) == (CUS * per_cu // n, n, 256, vectors)
+
+
+def test_ring_steps_launch_bound_below_64_mib():
+    """4 x 4,099 int32: every step is launch-bound, one vector per lane."""
+    for kind, gx, gy, block, vec in plan_ar(4, 4099, vrc.VRC_INT32, vrc.VRC_RING):
+        assert (gy, block, vec) == (4, 256, 1)
+        assert 1 <= gx <= CUS * 8 // 4
+
+
+def test_environment_overrides_reach_the_plan():
+    """VRC_FUSED_BLOCK / VRC_FUSED_BLOCKS_PER_CU / VRC_UNROLL and
+    VRC_CHAIN_BLOCK / VRC_CHAIN_BLOCKS_PER_CU replace the policy (read once
+    per process, so a child process checks them)."""
+    code = (
+        "import ring_all_reduce_virtual_amd as v\n"
+        "s=[(1<<40)+r*(1<<32) for r in range(8)]; d=[(1<<42)+r*(1<<32) for r in range(8)]\n"
+        "f,_=v.plan(v.COLL_ALLREDUCE,s,d,268435456,1,v.VRC_BF16,v.VRC_FUSED)\n"
+        "c,_=v.plan(v.COLL_ALLREDUCE,s,d,268435456,1,v.VRC_BF16,v.VRC_RING_CHAINED)\n"
+        "print(f[0]['grid_x'],f[0]['block'],f[0]['vectors'],c[0]['grid_x'],c[0]['block'])\n")
+    env = dict(os.environ, VRC_FUSED_BLOCK="256", VRC_FUSED_BLOCKS_PER_CU="1", VRC_UNROLL="2",
+               VRC_CHAIN_BLOCK="256", VRC_CHAIN_BLOCKS_PER_CU="4", PYTHONPATH=ROOT)
+    out = subprocess.run([sys.executable, "-c", code], env=env, check=True, capture_output=True, text=True,
+                         cwd=ROOT).stdout.split()
+    assert list(map(int, out)) == [256, 256, 2, 1024, 256]
