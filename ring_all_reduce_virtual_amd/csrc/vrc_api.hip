@@ -79,11 +79,12 @@ int env_int(const char* name, int dflt, int lo, int hi)
 //  - fused all-reduce: one-wave workgroups sized to the rank count
 //    (fused_ar_shape); single-launch ring all-reduce: one-wave workgroups
 //    (chain_ar_shape);
-//  - fused reduce-scatter: 256-lane workgroups, one per CU (two at 2 ranks)
-//    once the whole operation moves >= 4 GiB, 2 per CU from 1 GiB, 8 per CU
-//    below that, where the Infinity Cache holds much of the data and latency
-//    hiding matters more than open DRAM rows; fused all-gather: 16 per CU
-//    (ag_blocks_per_cu);
+//  - fused reduce-scatter: over flat chunks from 64 MiB moved, one-wave
+//    workgroups (fused_rs_flat_blocks_per_cu); otherwise 256-lane
+//    workgroups, one per CU (two at 2 ranks) once the whole operation moves
+//    >= 4 GiB, 2 per CU from 1 GiB, 8 per CU below that, where the Infinity
+//    Cache holds much of the data and latency hiding matters more than open
+//    DRAM rows; fused all-gather: 16 per CU (ag_blocks_per_cu);
 //  - ring and halving-doubling steps: by the bytes a step moves and its number
 //    of per-rank operations (step_shape), workgroups counted over all of them.
 // Loads and stores carry the non-temporal hint (measured faster for this
@@ -218,6 +219,23 @@ bool step_nontemporal(bool add, uint64_t bytes_moved)
     case 2: return add;
     }
     return add || bytes_moved / 2 > 64 * kMiB;
+}
+
+// The fused reduce-scatter over flat chunks, from 64 MiB moved: one-wave
+// workgroups walking all chunks in address order, 8 per CU up to 4 ranks and
+// 4 above.  Measured on MI355X in one process on the same buffers (GB/s of
+// (N+1)·S; one grid row per chunk with 256-lane workgroups, as below 64 MiB
+// -> this shape, rank-order fold): 8 x 512 MiB 5,402 -> 5,885;
+// 8 x 128 MiB 5,109 -> 6,156; 16 x 256 MiB 5,350 -> 5,615; 4 x 1 GiB
+// 5,457 -> 5,916.  The butterfly fold of the halving-doubling reduce-scatter
+// does N-1 rounded adds per element over fewer bytes per fold than an
+// all-reduce, and turns ALU-bound with too few waves: at 16 ranks it took
+// 1,480 us at 2 per CU against 847-853 us at 4 (the rank fold: 863-871 us
+// at either), so 4 per CU is the floor from 5 ranks up.
+int fused_rs_flat_blocks_per_cu(int n)
+{
+    if (tuning().fused_blocks_per_cu) return tuning().fused_blocks_per_cu;
+    return n <= 4 ? 8 : 4;
 }
 
 // The fused all-gather reads each input once and stores it N times: 16
@@ -694,11 +712,80 @@ struct Launch {
         hipLaunchKernelGGL((vrc::k_fused_reduce_scatter<T, N, true, Fold>), grid, dim3(kBlock), 0, st, a);
     }
 
+    template <int N, class Fold>
+    static void launch_fused_rs_flat_n(const vrc::ChainArgs& a, dim3 grid, hipStream_t st)
+    {
+        hipLaunchKernelGGL((vrc::k_fused_reduce_scatter_flat<T, N, true, Fold>), grid, dim3(64), 0, st, a);
+    }
+
+    // Flat chunks (outer == 1) from 64 MiB moved: one-wave tiles over all
+    // chunks in address order (fused_rs_flat_blocks_per_cu).  The flat
+    // kernel's scalar pass runs one wave per chunk, so it is used only when
+    // every chunk's operands share their offset modulo 16 bytes (at most a
+    // head and a tail run scalar); otherwise the caller takes the per-chunk
+    // grid, which spreads scalar elements over all lanes.  Returns false,
+    // enqueueing nothing, in that case.
+    template <class Fold>
+    static bool fused_reduce_scatter_flat(const char* const* x, char* const* y, int n, uint64_t count, int cus,
+                                          hipStream_t st, vrc_status_t* rc)
+    {
+        vrc::ChainArgs a = {};
+        for (int r = 0; r < kMaxRanks; r++) {
+            a.src[r] = r < n ? x[r] : nullptr;
+            a.dst[r] = r < n ? y[r] : nullptr;
+        }
+        a.tile0[0] = 0;
+        for (int c = 0; c < n; c++) {
+            uint64_t off, len;
+            chunk_range(count, n, c, &off, &len);
+            uintptr_t addr[kMaxRanks + 1];
+            for (int r = 0; r < n; r++) addr[r] = (uintptr_t)(x[r] + off * E);
+            addr[n] = (uintptr_t)y[c];
+            a.ch[c] = {off, 1, len, 0, split_rows(addr, n + 1, 1, nullptr, 0, len, E)};
+            if (a.ch[c].g.head + a.ch[c].g.tail >= 2 * (uint64_t)T::VEC) return false;
+            a.tile0[c + 1] = a.tile0[c] + (a.ch[c].g.nvb + 63) / 64;
+        }
+        // At least one wave per chunk for the scalar head/tail pass.
+        const uint64_t lanes = a.tile0[n] * 64, scalar_lanes = (uint64_t)n * 64;
+        const uint64_t work = lanes > scalar_lanes ? lanes : scalar_lanes;
+        const dim3 grid(grid_x(cus, work, 1, fused_rs_flat_blocks_per_cu(n), 64));
+        if (g_plan) {
+            *rc = plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_REDUCE_SCATTER
+                                                                         : VRC_OP_FUSED_REDUCE_SCATTER,
+                              count, grid, 64, 1);
+            return true;
+        }
+        *rc = VRC_OK;
+        if constexpr (std::is_same<Fold, vrc::Butterfly>::value) {
+            switch (n) {
+            case 2: launch_fused_rs_flat_n<2, Fold>(a, grid, st); break;
+            case 4: launch_fused_rs_flat_n<4, Fold>(a, grid, st); break;
+            case 8: launch_fused_rs_flat_n<8, Fold>(a, grid, st); break;
+            case 16: launch_fused_rs_flat_n<16, Fold>(a, grid, st); break;
+            default: *rc = VRC_ERR_INVALID_ARG; return true;
+            }
+        } else {
+            switch (n) {
+#define VRC_CASE(K) \
+    case K: launch_fused_rs_flat_n<K, Fold>(a, grid, st); break;
+                VRC_FOR_N(VRC_CASE)
+#undef VRC_CASE
+            default: *rc = VRC_ERR_INVALID_ARG; return true;
+            }
+        }
+        *rc = check_launch();
+        return true;
+    }
+
     template <class Fold = vrc::RankFold>
     static vrc_status_t fused_reduce_scatter(const char* const* x, char* const* y, int n, uint64_t count,
                                              uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        vrc_status_t rc = VRC_OK;
+        if (outer == 1 && (uint64_t)(n + 1) * count * E >= 64 * kMiB &&
+            fused_reduce_scatter_flat<Fold>(x, y, n, count, cus, st, &rc))
+            return rc;
         vrc::FusedRsArgs a;
         uint64_t work = 0;
         for (int r = 0; r < kMaxRanks; r++) a.src[r] = r < n ? x[r] : nullptr;

@@ -503,6 +503,57 @@ __global__ __launch_bounds__(B) void k_ring_chain_allreduce(ChainArgs a)
     }
 }
 
+// Fused reduce-scatter over flat chunks (outer == 1), walked like the
+// all-reduce chain: wave-sized tiles of all chunks in address order, so the
+// whole grid streams through the inputs together instead of one grid row
+// per chunk.  Output c (its own buffer, a.dst[c]) is the fold of chunk c of
+// every input.  Scalar head and tail elements of each chunk: one wave per
+// chunk.
+template <class T, int N, bool NT, class Fold = RankFold, int B = 64>
+__global__ __launch_bounds__(B) void k_fused_reduce_scatter_flat(ChainArgs a)
+{
+    constexpr uint64_t W = 64;
+    constexpr uint64_t E = T::ESZ;
+    const uint64_t lane = threadIdx.x % W;
+    const uint64_t wave = (uint64_t)blockIdx.x * (B / W) + threadIdx.x / W;
+    const uint64_t nwaves = (uint64_t)gridDim.x * (B / W);
+    const uint64_t ntiles = a.tile0[N];
+    int cur = -1;
+    uint64_t in_body = 0, out_body = 0, nvb = 0, first = 0;
+    char* out = nullptr;
+    for (uint64_t t = wave; t < ntiles; t += nwaves) {
+        const int c = __builtin_amdgcn_readfirstlane(range_of<N>(t, a.tile0));
+        if (c != cur) {
+            cur = c;
+            in_body = (a.ch[c].off + a.ch[c].g.head) * E;
+            out_body = a.ch[c].g.head * E;
+            nvb = a.ch[c].g.nvb;
+            first = a.tile0[c];
+            out = a.dst[c];
+        }
+        const uint64_t v = (t - first) * W + lane;
+        if (v < nvb) {
+            u32x4 in[N];
+#pragma unroll
+            for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + in_body + v * 16);
+            issue_loads_first();
+            st16<NT>(out + out_body + v * 16, Fold::template vec<T, N>(in));
+        }
+    }
+    for (uint64_t cw = wave; cw < (uint64_t)N; cw += nwaves) {
+        const int c = __builtin_amdgcn_readfirstlane((int)cw);
+        const ChainChunk& k = a.ch[c];
+        const uint64_t ns = k.g.head + k.g.tail;
+        for (uint64_t j = lane; j < ns; j += W) {
+            const uint64_t col = (j < k.g.head) ? j : k.g.head + k.g.nvb * T::VEC + (j - k.g.head);
+            typename T::S in[N];
+#pragma unroll
+            for (int r = 0; r < N; r++) in[r] = load_s<T>(a.src[r] + (k.off + col) * E);
+            store_s<T>(a.dst[c] + col * E, Fold::template scalar<T, N>(in));
+        }
+    }
+}
+
 // Reduce-scatter chain: chunk c of every rank ([rows, width] with row stride
 // `stride`) is summed in ring order into output c ([rows, width], dense).
 // MEM keeps the running partial in output c and reads it back before each

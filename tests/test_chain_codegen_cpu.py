@@ -31,6 +31,8 @@ template __global__ void vrc::k_fused_allreduce<vrc::F32, {N}, 1, true, vrc::But
 template __global__ void vrc::k_fused_allreduce<vrc::I32, 4, 2, true, vrc::RankFold, 64>(vrc::FusedArArgs);
 template __global__ void vrc::k_fused_allreduce<vrc::F16, 16, 1, true, vrc::RankFold, 64>(vrc::FusedArArgs);
 template __global__ void vrc::k_fused_reduce_scatter<vrc::F32, {N}, true, vrc::RankFold>(vrc::FusedRsArgs);
+template __global__ void vrc::k_fused_reduce_scatter_flat<vrc::BF16, {N}, true, vrc::RankFold, 64>(vrc::ChainArgs);
+template __global__ void vrc::k_fused_reduce_scatter_flat<vrc::F32, {N}, true, vrc::Butterfly, 64>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::F32, {N}, false, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, true, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, false, true>(vrc::ChainArgs);
@@ -113,6 +115,8 @@ def longest_load_run(text):
     (r"k_fused_allreduceINS_3I32ELi4ELi2ELb1ENS_8RankFoldELi64", 8),
     (r"k_fused_allreduceINS_3F16ELi16ELi1ELb1ENS_8RankFoldELi64", 16),
     (r"k_fused_reduce_scatterINS_3F32ELi8ELb1ENS_8RankFold", N),
+    (r"k_fused_reduce_scatter_flatINS_4BF16ELi8ELb1ENS_8RankFoldELi64", N),
+    (r"k_fused_reduce_scatter_flatINS_3F32ELi8ELb1ENS_9ButterflyELi64", N),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi256", N),
     (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1ELb1ELi256", N),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi64", N),

@@ -344,3 +344,40 @@ def test_fused_launch_shapes(vrc, orc, n):
             for r in (0, n - 1):
                 assert_bitwise(workloads.to_numpy(ys[r]), want[r], f"{mode} {dtype} n={n} offset={offset} rank {r}")
             del ys
+
+
+# ---------------------------------------------------------------------------
+# fused reduce-scatter over flat chunks from 64 MiB moved: one-wave tiles over
+# all chunks (every chunk 16-byte compatible), else one grid row per chunk
+# ---------------------------------------------------------------------------
+RS_FLAT_LAYOUTS = {
+    "aligned": (0, 0),         # inputs and outputs on 16-byte boundaries: vector body, ragged tail
+    "both_offset": (1, 1),     # inputs and outputs one element past a boundary: scalar heads
+    "inputs_offset": (1, 0),   # offsets differ between inputs and outputs: the per-chunk grid
+}
+
+
+@pytest.mark.parametrize("layout", list(RS_FLAT_LAYOUTS))
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 7, 8, 11, 16])
+def test_fused_reduce_scatter_flat_shapes(vrc, orc, n, layout):
+    dtype = ("fp32", "bf16", "fp16", "int32")[n % 4]
+    esz = 2 if dtype in ("fp16", "bf16") else 4
+    vec = 16 // esz
+    base = ((64 << 20) // ((n + 1) * n * esz) // vec + 1) * vec  # chunk bytes a multiple of 16
+    count = n * base + n - 1  # the last chunk takes the remainder and ends in a scalar tail
+    in_off, out_off = RS_FLAT_LAYOUTS[layout]
+    say(f"fused rs flat n={n} count={count} {dtype} {layout}")
+    src = workloads.random_ranks(n, count + 1, dtype, seed=900 + n, device=DEV, sigma=1e-2)
+    xs = [t[in_off:in_off + count] for t in src]
+    lens = [base] * (n - 1) + [count - (n - 1) * base]
+    hx = host(xs)
+    modes = ("fused", "hd_order", "hd") if pow2(n) else ("fused",)
+    for mode in modes:
+        outs = [torch.empty(ln + 1, dtype=xs[0].dtype, device=DEV) for ln in lens]
+        ys = [o[out_off:out_off + ln] for o, ln in zip(outs, lens)]
+        vrc.vrc_reduce_scatter(xs, recv=ys, mode=mode)
+        torch.cuda.synchronize()
+        want = want_rs(orc, hx, dtype, mode)
+        for c, y in enumerate(host(ys)):
+            assert_bitwise(y, want[c], f"rs {mode} {dtype} n={n} {layout} chunk {c}")
+        del outs, ys

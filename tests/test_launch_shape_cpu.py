@@ -180,3 +180,38 @@ def test_environment_overrides_reach_the_plan():
     out = subprocess.run([sys.executable, "-c", code], env=env, check=True, capture_output=True, text=True,
                          cwd=ROOT).stdout.split()
     assert list(map(int, out)) == [256, 256, 2, 1024, 256]
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8, 9, 16])
+def test_fused_reduce_scatter_flat_shape(n):
+    """Flat chunks from 64 MiB moved: one-wave workgroups over all chunks,
+    8 per CU up to 4 ranks and 4 above (the butterfly fold of the
+    halving-doubling reduce-scatter, which takes the same shape, turns
+    ALU-bound with fewer)."""
+    count = (4 << 30) // n // 2 // n // 64 * 64 * n  # whole 16-byte vectors in every chunk
+    send, recv = wide(n)
+    bpc = 8 if n <= 4 else 4
+    ops, nl = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
+    assert nl == 1 and launches(ops) == [("fused_reduce_scatter", CUS * bpc, 1, 64, 1)]
+    if n & (n - 1) == 0:
+        # at 2 ranks the butterfly is one add rounded once: the rank-fold kernel runs
+        kind = "fused_reduce_scatter" if n == 2 else "butterfly_reduce_scatter"
+        for mode in (vrc.VRC_HD_ORDER, vrc.VRC_HD):
+            ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, count, 1, vrc.VRC_BF16, mode)
+            assert launches(ops) == [(kind, CUS * bpc, 1, 64, 1)]
+
+
+def test_fused_reduce_scatter_keeps_the_chunk_grid_when_chunks_cannot_vectorize():
+    """Chunk offsets that leave inputs and outputs on different 16-byte
+    offsets, split dimensions, and calls below 64 MiB moved keep one grid row
+    per chunk with 256-lane workgroups."""
+    n = 8
+    send, recv = wide(n)
+    ragged = 268435456 + n * 3 + 5  # chunk bytes not a multiple of 16
+    ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, ragged, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
+    (kind, gx, gy, block, vec), = launches(ops)
+    assert (kind, gy, block) == ("fused_reduce_scatter", n, 256)
+    ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, 268435456, 8, vrc.VRC_BF16, vrc.VRC_FUSED)
+    assert launches(ops)[0][2:4] == (n, 256)
+    ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, 1 << 20, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
+    assert launches(ops)[0][2:4] == (n, 256)
