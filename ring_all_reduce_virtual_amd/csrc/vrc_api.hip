@@ -79,8 +79,8 @@ int env_int(const char* name, int dflt, int lo, int hi)
 //  - fused all-reduce: one-wave workgroups sized to the rank count
 //    (fused_ar_shape); single-launch ring all-reduce: one-wave workgroups
 //    (chain_ar_shape);
-//  - fused reduce-scatter: over flat chunks from 64 MiB moved, one-wave
-//    workgroups (fused_rs_flat_blocks_per_cu); otherwise 256-lane
+//  - fused and ring-order reduce-scatter: over flat chunks from 64 MiB moved,
+//    one-wave workgroups (fused_rs_flat_blocks_per_cu); otherwise 256-lane
 //    workgroups, one per CU (two at 2 ranks) once the whole operation moves
 //    >= 4 GiB, 2 per CU from 1 GiB, 8 per CU below that, where the Infinity
 //    Cache holds much of the data and latency hiding matters more than open
@@ -719,17 +719,18 @@ struct Launch {
     }
 
     // Flat chunks (outer == 1) from 64 MiB moved: one-wave tiles over all
-    // chunks in address order (fused_rs_flat_blocks_per_cu).  The flat
-    // kernel's scalar pass runs one wave per chunk, so it is used only when
-    // every chunk's operands share their offset modulo 16 bytes (at most a
-    // head and a tail run scalar); otherwise the caller takes the per-chunk
-    // grid, which spreads scalar elements over all lanes.  Returns false,
-    // enqueueing nothing, in that case.
-    template <class Fold>
-    static bool fused_reduce_scatter_flat(const char* const* x, char* const* y, int n, uint64_t count, int cus,
-                                          hipStream_t st, vrc_status_t* rc)
+    // chunks in address order (fused_rs_flat_blocks_per_cu), for the fused
+    // and ring-order reduce-scatters.  The flat kernels' scalar pass runs one
+    // wave per chunk, so they are used only when every chunk's operands share
+    // their offset modulo 16 bytes (at most a head and a tail run scalar);
+    // otherwise the caller takes the per-chunk grid, which spreads scalar
+    // elements over all lanes.  Fills the chunk table and grid and returns
+    // false in that case.
+    static bool rs_flat_layout(const char* const* x, char* const* y, int n, uint64_t count, int cus,
+                               vrc::ChainArgs* pa, dim3* grid)
     {
-        vrc::ChainArgs a = {};
+        vrc::ChainArgs& a = *pa;
+        a = {};
         for (int r = 0; r < kMaxRanks; r++) {
             a.src[r] = r < n ? x[r] : nullptr;
             a.dst[r] = r < n ? y[r] : nullptr;
@@ -748,7 +749,17 @@ struct Launch {
         // At least one wave per chunk for the scalar head/tail pass.
         const uint64_t lanes = a.tile0[n] * 64, scalar_lanes = (uint64_t)n * 64;
         const uint64_t work = lanes > scalar_lanes ? lanes : scalar_lanes;
-        const dim3 grid(grid_x(cus, work, 1, fused_rs_flat_blocks_per_cu(n), 64));
+        *grid = dim3(grid_x(cus, work, 1, fused_rs_flat_blocks_per_cu(n), 64));
+        return true;
+    }
+
+    template <class Fold>
+    static bool fused_reduce_scatter_flat(const char* const* x, char* const* y, int n, uint64_t count, int cus,
+                                          hipStream_t st, vrc_status_t* rc)
+    {
+        vrc::ChainArgs a;
+        dim3 grid;
+        if (!rs_flat_layout(x, y, n, count, cus, &a, &grid)) return false;
         if (g_plan) {
             *rc = plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_REDUCE_SCATTER
                                                                          : VRC_OP_FUSED_REDUCE_SCATTER,
@@ -1030,6 +1041,24 @@ struct Launch {
                                              uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        if (!MEM && outer == 1 && (uint64_t)(n + 1) * count * E >= 64 * kMiB) {
+            // Ring order over flat chunks: the flat walk of the fused reduce-scatter.
+            vrc::ChainArgs fa;
+            dim3 fgrid;
+            if (rs_flat_layout(x, y, n, count, cus, &fa, &fgrid)) {
+                if (g_plan) return plan_single(VRC_OP_RING_ORDER_REDUCE_SCATTER, count, fgrid, 64, 1);
+                switch (n) {
+#define VRC_CASE(K)                                                                                         \
+    case K:                                                                                                 \
+        hipLaunchKernelGGL((vrc::k_ring_order_reduce_scatter_flat<T, K, true>), fgrid, dim3(64), 0, st, fa); \
+        break;
+                    VRC_FOR_N(VRC_CASE)
+#undef VRC_CASE
+                default: return VRC_ERR_INVALID_ARG;
+                }
+                return check_launch();
+            }
+        }
         vrc::ChainArgs a = {};
         uint64_t work = 0;
         for (int r = 0; r < kMaxRanks; r++) {

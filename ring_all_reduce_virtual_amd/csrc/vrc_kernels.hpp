@@ -580,6 +580,52 @@ __device__ __forceinline__ void chain_rs_block(const char* const* in, uint64_t s
     IO::st_out(out, p);
 }
 
+// Ring-order reduce-scatter over flat chunks (partials in registers): the
+// per-chunk grid of k_ring_chain_reduce_scatter<MEM = false> replaced by the
+// flat walk of k_fused_reduce_scatter_flat.  Chunk c folds the ranks in ring
+// order from rank c, as in the per-chunk kernel, so the bits are the same.
+template <class T, int N, bool NT, int B = 64>
+__global__ __launch_bounds__(B) void k_ring_order_reduce_scatter_flat(ChainArgs a)
+{
+    constexpr uint64_t W = 64;
+    constexpr uint64_t E = T::ESZ;
+    const uint64_t lane = threadIdx.x % W;
+    const uint64_t wave = (uint64_t)blockIdx.x * (B / W) + threadIdx.x / W;
+    const uint64_t nwaves = (uint64_t)gridDim.x * (B / W);
+    const uint64_t ntiles = a.tile0[N];
+    const char* in[N];
+    int cur = -1;
+    uint64_t in_body = 0, out_body = 0, nvb = 0, first = 0;
+    char* out = nullptr;
+    for (uint64_t t = wave; t < ntiles; t += nwaves) {
+        const int c = __builtin_amdgcn_readfirstlane(range_of<N>(t, a.tile0));
+        if (c != cur) {
+            cur = c;
+#pragma unroll
+            for (int k = 0; k < N; k++) in[k] = a.src[(c + k) % N];
+            in_body = (a.ch[c].off + a.ch[c].g.head) * E;
+            out_body = a.ch[c].g.head * E;
+            nvb = a.ch[c].g.nvb;
+            first = a.tile0[c];
+            out = a.dst[c];
+        }
+        const uint64_t v = (t - first) * W + lane;
+        if (v < nvb) chain_rs_block<N, false, VecIO<T, NT>>(in, in_body + v * 16, out + out_body + v * 16);
+    }
+    for (uint64_t cw = wave; cw < (uint64_t)N; cw += nwaves) {
+        const int c = __builtin_amdgcn_readfirstlane((int)cw);
+        const ChainChunk& k = a.ch[c];
+        const uint64_t ns = k.g.head + k.g.tail;
+        if (lane >= ns) continue;
+#pragma unroll
+        for (int q = 0; q < N; q++) in[q] = a.src[(c + q) % N];
+        for (uint64_t j = lane; j < ns; j += W) {
+            const uint64_t col = (j < k.g.head) ? j : k.g.head + k.g.nvb * T::VEC + (j - k.g.head);
+            chain_rs_block<N, false, ScalarIO<T>>(in, (k.off + col) * E, a.dst[c] + col * E);
+        }
+    }
+}
+
 template <class T, int N, bool MEM, bool NT>
 __global__ __launch_bounds__(kBlock) void k_ring_chain_reduce_scatter(ChainArgs a)
 {

@@ -33,6 +33,7 @@ template __global__ void vrc::k_fused_allreduce<vrc::F16, 16, 1, true, vrc::Rank
 template __global__ void vrc::k_fused_reduce_scatter<vrc::F32, {N}, true, vrc::RankFold>(vrc::FusedRsArgs);
 template __global__ void vrc::k_fused_reduce_scatter_flat<vrc::BF16, {N}, true, vrc::RankFold, 64>(vrc::ChainArgs);
 template __global__ void vrc::k_fused_reduce_scatter_flat<vrc::F32, {N}, true, vrc::Butterfly, 64>(vrc::ChainArgs);
+template __global__ void vrc::k_ring_order_reduce_scatter_flat<vrc::BF16, {N}, true, 64>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::F32, {N}, false, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, true, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, false, true>(vrc::ChainArgs);
@@ -117,6 +118,7 @@ def longest_load_run(text):
     (r"k_fused_reduce_scatterINS_3F32ELi8ELb1ENS_8RankFold", N),
     (r"k_fused_reduce_scatter_flatINS_4BF16ELi8ELb1ENS_8RankFoldELi64", N),
     (r"k_fused_reduce_scatter_flatINS_3F32ELi8ELb1ENS_9ButterflyELi64", N),
+    (r"k_ring_order_reduce_scatter_flatINS_4BF16ELi8ELb1ELi64", N),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi256", N),
     (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1ELb1ELi256", N),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi64", N),

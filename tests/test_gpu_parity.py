@@ -347,8 +347,9 @@ def test_fused_launch_shapes(vrc, orc, n):
 
 
 # ---------------------------------------------------------------------------
-# fused reduce-scatter over flat chunks from 64 MiB moved: one-wave tiles over
-# all chunks (every chunk 16-byte compatible), else one grid row per chunk
+# fused and ring-order reduce-scatter over flat chunks from 64 MiB moved:
+# one-wave tiles over all chunks (every chunk 16-byte compatible), else one
+# grid row per chunk
 # ---------------------------------------------------------------------------
 RS_FLAT_LAYOUTS = {
     "aligned": (0, 0),         # inputs and outputs on 16-byte boundaries: vector body, ragged tail
@@ -371,7 +372,7 @@ def test_fused_reduce_scatter_flat_shapes(vrc, orc, n, layout):
     xs = [t[in_off:in_off + count] for t in src]
     lens = [base] * (n - 1) + [count - (n - 1) * base]
     hx = host(xs)
-    modes = ("fused", "hd_order", "hd") if pow2(n) else ("fused",)
+    modes = ("fused", "ring_order", "hd_order", "hd") if pow2(n) else ("fused", "ring_order")
     for mode in modes:
         outs = [torch.empty(ln + 1, dtype=xs[0].dtype, device=DEV) for ln in lens]
         ys = [o[out_off:out_off + ln] for o, ln in zip(outs, lens)]

@@ -193,6 +193,8 @@ def test_fused_reduce_scatter_flat_shape(n):
     bpc = 8 if n <= 4 else 4
     ops, nl = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
     assert nl == 1 and launches(ops) == [("fused_reduce_scatter", CUS * bpc, 1, 64, 1)]
+    ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_RING_ORDER)
+    assert launches(ops) == [("ring_order_reduce_scatter", CUS * bpc, 1, 64, 1)]
     if n & (n - 1) == 0:
         # at 2 ranks the butterfly is one add rounded once: the rank-fold kernel runs
         kind = "fused_reduce_scatter" if n == 2 else "butterfly_reduce_scatter"
@@ -211,6 +213,8 @@ def test_fused_reduce_scatter_keeps_the_chunk_grid_when_chunks_cannot_vectorize(
     ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, ragged, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
     (kind, gx, gy, block, vec), = launches(ops)
     assert (kind, gy, block) == ("fused_reduce_scatter", n, 256)
+    ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, ragged, 1, vrc.VRC_BF16, vrc.VRC_RING_ORDER)
+    assert launches(ops)[0][0] == "ring_order_reduce_scatter" and launches(ops)[0][2:4] == (n, 256)
     ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, 268435456, 8, vrc.VRC_BF16, vrc.VRC_FUSED)
     assert launches(ops)[0][2:4] == (n, 256)
     ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, 1 << 20, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
