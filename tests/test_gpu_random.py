@@ -1,8 +1,9 @@
 """Seeded random sweep: every collective, mode and dtype on random rank
 counts (1-16), shapes, split dimensions, ragged sizes, element offsets that
 misalign the buffers (equal or different per rank) and in-place all-reduce,
-compared bit for bit with the oracle.  Each case draws from its own seed, so
-a failure names a reproducible case."""
+compared bit for bit with the oracle; and a smaller sweep above 64 MiB moved,
+where the all-reduce and reduce-scatter take their one-wave and flat shapes.
+Each case draws from its own seed, so a failure names a reproducible case."""
 import numpy as np
 import pytest
 import torch
@@ -131,3 +132,74 @@ def test_random_all_gather(vrc, orc, k):
     want = orc.ring_all_gather(hx, dtype, outer=outer)
     for r, y in enumerate(host(ys)):
         assert_bitwise(y, want[r], f"case {k} {mode} {dtype} n={n} shape={shape} dim={dim} rank {r}")
+
+
+# ---------------------------------------------------------------------------
+# Above 64 MiB moved the all-reduce and reduce-scatter take their one-wave
+# shapes (and, for flat chunks that vectorize, the flat reduce-scatter
+# kernels): a smaller seeded sweep there, single-launch modes, random rank
+# counts, dtypes, ragged counts and per-rank element offsets.
+# ---------------------------------------------------------------------------
+LARGE_CASES = 12
+LARGE_AR_MODES = ("fused", "ring_order", "ring_chained", "hd_order")
+LARGE_RS_MODES = ("fused", "ring_order", "hd_order", "hd")
+
+
+def draw_large(kind: int, k: int, modes):
+    rng = np.random.default_rng(104729 * kind + k)
+    dtype = str(rng.choice(DTYPES))
+    mode = str(rng.choice(modes))
+    n = int(2 ** rng.integers(1, 5)) if mode in HD_FAMILY else int(rng.integers(2, 17))
+    esz = 2 if dtype in ("fp16", "bf16") else 4
+    return rng, dtype, mode, n, esz
+
+
+@pytest.mark.parametrize("k", range(LARGE_CASES))
+def test_random_large_allreduce(vrc, orc, k):
+    rng, dtype, mode, n, esz = draw_large(4, k, LARGE_AR_MODES)
+    moved = int(rng.uniform(64, 160) * (1 << 20))
+    count = moved // (2 * n * esz) + int(rng.integers(0, 64))
+    if k % 3 != 2:  # one element offset shared by every input and output: the vector path
+        off = int(rng.integers(0, 8))
+        in_off, out_off = [off] * n, [off] * n
+    else:
+        in_off, out_off = offsets(rng, n), offsets(rng, n)
+    xs = [place(x, o) for x, o in zip(workloads.random_ranks(n, (count,), dtype, seed=40000 + k, device=DEV),
+                                      in_off)]
+    print(f"random large allreduce case {k}: {mode} {dtype} n={n} count={count} offsets {in_off[0]}/"
+          f"{out_off[0]}", flush=True)
+    hx = host(xs)
+    ys = [empty_at((count,), xs[0].dtype, o) for o in out_off]
+    vrc.vrc_allreduce(xs, recv=ys, mode=mode)
+    torch.cuda.synchronize()
+    want = want_ar(orc, hx, dtype, mode)
+    for r, y in enumerate(host(ys)):
+        assert_bitwise(y, want[r], f"large case {k} {mode} {dtype} n={n} count={count} rank {r}")
+
+
+@pytest.mark.parametrize("k", range(LARGE_CASES))
+def test_random_large_reduce_scatter(vrc, orc, k):
+    rng, dtype, mode, n, esz = draw_large(5, k, LARGE_RS_MODES)
+    moved = int(rng.uniform(64, 160) * (1 << 20))
+    vec = 16 // esz
+    base = moved // ((n + 1) * n * esz)
+    if k % 4 != 3:
+        base = base // vec * vec  # whole 16-byte vectors per chunk: the flat kernels can take it
+    count = n * base + int(rng.integers(0, n))
+    if k % 3 != 2:  # one element offset shared by every input and output
+        off = int(rng.integers(0, 8))
+        in_off, out_off = [off] * n, [off] * n
+    else:
+        in_off, out_off = offsets(rng, n), offsets(rng, n)
+    xs = [place(x, o) for x, o in zip(workloads.random_ranks(n, (count,), dtype, seed=50000 + k, device=DEV),
+                                      in_off)]
+    print(f"random large reduce_scatter case {k}: {mode} {dtype} n={n} count={count} offsets {in_off[0]}/"
+          f"{out_off[0]}", flush=True)
+    shapes = vrc.reduce_scatter_shape((count,), n, 0)
+    ys = [empty_at(shapes[c], xs[0].dtype, o) for c, o in enumerate(out_off)]
+    hx = host(xs)
+    vrc.vrc_reduce_scatter(xs, recv=ys, mode=mode)
+    torch.cuda.synchronize()
+    want = want_rs(orc, hx, dtype, mode)
+    for c, y in enumerate(host(ys)):
+        assert_bitwise(y, want[c], f"large case {k} {mode} {dtype} n={n} count={count} chunk {c}")
