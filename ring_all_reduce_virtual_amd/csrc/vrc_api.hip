@@ -238,6 +238,15 @@ int fused_rs_flat_blocks_per_cu(int n)
     return n <= 4 ? 8 : 4;
 }
 
+// The memory-faithful reduce-scatter chain over flat chunks (one-wave
+// workgroups): its lanes wait on their own stores at every step, so like the
+// all-reduce chain it keeps more waves resident.
+int chain_rs_flat_blocks_per_cu()
+{
+    if (tuning().chain_blocks_per_cu) return tuning().chain_blocks_per_cu;
+    return 16;
+}
+
 // The fused all-gather reads each input once and stores it N times: 16
 // workgroups per CU at every size.  Measured on MI355X in one process on the
 // same buffers (us, 8 / 16 per CU): 8 x 5 MiB fp16 heads 77.2 / 75.2 and
@@ -1041,16 +1050,22 @@ struct Launch {
                                              uint64_t outer, int cus, hipStream_t st)
     {
         if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
-        if (!MEM && outer == 1 && (uint64_t)(n + 1) * count * E >= 64 * kMiB) {
-            // Ring order over flat chunks: the flat walk of the fused reduce-scatter.
+        if (outer == 1 && (uint64_t)(n + 1) * count * E >= 64 * kMiB) {
+            // Flat chunks: the flat walk of the fused reduce-scatter.
             vrc::ChainArgs fa;
             dim3 fgrid;
             if (rs_flat_layout(x, y, n, count, cus, &fa, &fgrid)) {
-                if (g_plan) return plan_single(VRC_OP_RING_ORDER_REDUCE_SCATTER, count, fgrid, 64, 1);
+                if (MEM) {
+                    const uint64_t lanes = fa.tile0[n] * 64, scalar_lanes = (uint64_t)n * 64;
+                    fgrid.x = grid_x(cus, lanes > scalar_lanes ? lanes : scalar_lanes, 1, chain_rs_flat_blocks_per_cu(), 64);
+                }
+                if (g_plan)
+                    return plan_single(MEM ? VRC_OP_CHAIN_REDUCE_SCATTER : VRC_OP_RING_ORDER_REDUCE_SCATTER, count,
+                                       fgrid, 64, 1);
                 switch (n) {
-#define VRC_CASE(K)                                                                                         \
-    case K:                                                                                                 \
-        hipLaunchKernelGGL((vrc::k_ring_order_reduce_scatter_flat<T, K, true>), fgrid, dim3(64), 0, st, fa); \
+#define VRC_CASE(K)                                                                                              \
+    case K:                                                                                                      \
+        hipLaunchKernelGGL((vrc::k_ring_chain_reduce_scatter_flat<T, K, MEM, true>), fgrid, dim3(64), 0, st, fa); \
         break;
                     VRC_FOR_N(VRC_CASE)
 #undef VRC_CASE

@@ -580,12 +580,13 @@ __device__ __forceinline__ void chain_rs_block(const char* const* in, uint64_t s
     IO::st_out(out, p);
 }
 
-// Ring-order reduce-scatter over flat chunks (partials in registers): the
-// per-chunk grid of k_ring_chain_reduce_scatter<MEM = false> replaced by the
-// flat walk of k_fused_reduce_scatter_flat.  Chunk c folds the ranks in ring
-// order from rank c, as in the per-chunk kernel, so the bits are the same.
-template <class T, int N, bool NT, int B = 64>
-__global__ __launch_bounds__(B) void k_ring_order_reduce_scatter_flat(ChainArgs a)
+// Ring reduce-scatter chain over flat chunks: the per-chunk grid of
+// k_ring_chain_reduce_scatter replaced by the flat walk of
+// k_fused_reduce_scatter_flat.  Chunk c folds the ranks in ring order from
+// rank c, as in the per-chunk kernel, so the bits are the same; MEM keeps the
+// running partial in output c and reads it back before each step's add.
+template <class T, int N, bool MEM, bool NT, int B = 64>
+__global__ __launch_bounds__(B) void k_ring_chain_reduce_scatter_flat(ChainArgs a)
 {
     constexpr uint64_t W = 64;
     constexpr uint64_t E = T::ESZ;
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(B) void k_ring_order_reduce_scatter_flat(ChainArgs 
             out = a.dst[c];
         }
         const uint64_t v = (t - first) * W + lane;
-        if (v < nvb) chain_rs_block<N, false, VecIO<T, NT>>(in, in_body + v * 16, out + out_body + v * 16);
+        if (v < nvb) chain_rs_block<N, MEM, VecIO<T, NT>>(in, in_body + v * 16, out + out_body + v * 16);
     }
     for (uint64_t cw = wave; cw < (uint64_t)N; cw += nwaves) {
         const int c = __builtin_amdgcn_readfirstlane((int)cw);
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(B) void k_ring_order_reduce_scatter_flat(ChainArgs 
         for (int q = 0; q < N; q++) in[q] = a.src[(c + q) % N];
         for (uint64_t j = lane; j < ns; j += W) {
             const uint64_t col = (j < k.g.head) ? j : k.g.head + k.g.nvb * T::VEC + (j - k.g.head);
-            chain_rs_block<N, false, ScalarIO<T>>(in, (k.off + col) * E, a.dst[c] + col * E);
+            chain_rs_block<N, MEM, ScalarIO<T>>(in, (k.off + col) * E, a.dst[c] + col * E);
         }
     }
 }

@@ -33,7 +33,8 @@ template __global__ void vrc::k_fused_allreduce<vrc::F16, 16, 1, true, vrc::Rank
 template __global__ void vrc::k_fused_reduce_scatter<vrc::F32, {N}, true, vrc::RankFold>(vrc::FusedRsArgs);
 template __global__ void vrc::k_fused_reduce_scatter_flat<vrc::BF16, {N}, true, vrc::RankFold, 64>(vrc::ChainArgs);
 template __global__ void vrc::k_fused_reduce_scatter_flat<vrc::F32, {N}, true, vrc::Butterfly, 64>(vrc::ChainArgs);
-template __global__ void vrc::k_ring_order_reduce_scatter_flat<vrc::BF16, {N}, true, 64>(vrc::ChainArgs);
+template __global__ void vrc::k_ring_chain_reduce_scatter_flat<vrc::BF16, {N}, false, true, 64>(vrc::ChainArgs);
+template __global__ void vrc::k_ring_chain_reduce_scatter_flat<vrc::F16, {N}, true, true, 64>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::F32, {N}, false, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, true, true>(vrc::ChainArgs);
 template __global__ void vrc::k_ring_chain_allreduce<vrc::BF16, {N}, false, true>(vrc::ChainArgs);
@@ -83,6 +84,7 @@ def count(text, op):
     (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1ELb1ELi64", 3 * N - 3, 2 * (N - 1)),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi64", N, N),
     (r"k_ring_chain_reduce_scatterINS_3F16ELi8ELb1", 2 * (N - 1), N - 1),
+    (r"k_ring_chain_reduce_scatter_flatINS_3F16ELi8ELb1", 2 * (N - 1), N - 1),
     (r"k_ring_chain_all_gatherINS_3F32ELi8", N - 1, N),
 ])
 def test_chain_kernels_issue_every_access(asm, pattern, loads, stores):
@@ -118,7 +120,8 @@ def longest_load_run(text):
     (r"k_fused_reduce_scatterINS_3F32ELi8ELb1ENS_8RankFold", N),
     (r"k_fused_reduce_scatter_flatINS_4BF16ELi8ELb1ENS_8RankFoldELi64", N),
     (r"k_fused_reduce_scatter_flatINS_3F32ELi8ELb1ENS_9ButterflyELi64", N),
-    (r"k_ring_order_reduce_scatter_flatINS_4BF16ELi8ELb1ELi64", N),
+    (r"k_ring_chain_reduce_scatter_flatINS_4BF16ELi8ELb0ELb1ELi64", N),
+    (r"k_ring_chain_reduce_scatter_flatINS_3F16ELi8ELb1ELb1ELi64", N),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi256", N),
     (r"k_ring_chain_allreduceINS_4BF16ELi8ELb1ELb1ELi256", N),
     (r"k_ring_chain_allreduceINS_3F32ELi8ELb0ELb1ELi64", N),

@@ -347,7 +347,7 @@ def test_fused_launch_shapes(vrc, orc, n):
 
 
 # ---------------------------------------------------------------------------
-# fused and ring-order reduce-scatter over flat chunks from 64 MiB moved:
+# fused and single-launch ring reduce-scatter over flat chunks from 64 MiB moved:
 # one-wave tiles over all chunks (every chunk 16-byte compatible), else one
 # grid row per chunk
 # ---------------------------------------------------------------------------
@@ -372,7 +372,8 @@ def test_fused_reduce_scatter_flat_shapes(vrc, orc, n, layout):
     xs = [t[in_off:in_off + count] for t in src]
     lens = [base] * (n - 1) + [count - (n - 1) * base]
     hx = host(xs)
-    modes = ("fused", "ring_order", "hd_order", "hd") if pow2(n) else ("fused", "ring_order")
+    modes = ("fused", "ring_order", "ring_chained", "hd_order", "hd") if pow2(n) else ("fused", "ring_order",
+                                                                                       "ring_chained")
     for mode in modes:
         outs = [torch.empty(ln + 1, dtype=xs[0].dtype, device=DEV) for ln in lens]
         ys = [o[out_off:out_off + ln] for o, ln in zip(outs, lens)]

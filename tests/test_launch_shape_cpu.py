@@ -195,6 +195,8 @@ def test_fused_reduce_scatter_flat_shape(n):
     assert nl == 1 and launches(ops) == [("fused_reduce_scatter", CUS * bpc, 1, 64, 1)]
     ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_RING_ORDER)
     assert launches(ops) == [("ring_order_reduce_scatter", CUS * bpc, 1, 64, 1)]
+    ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_RING_CHAINED)
+    assert launches(ops) == [("chain_reduce_scatter", CUS * 16, 1, 64, 1)]
     if n & (n - 1) == 0:
         # at 2 ranks the butterfly is one add rounded once: the rank-fold kernel runs
         kind = "fused_reduce_scatter" if n == 2 else "butterfly_reduce_scatter"
