@@ -267,7 +267,7 @@ def test_errors_through_the_binding(vrc):
     assert vrc.lib().vrc_last_hip_error() == 0
 
 
-@pytest.mark.parametrize("mode", ["fused", "ring", "ring_chained", "hd"])
+@pytest.mark.parametrize("mode", MODES)
 def test_more_than_2_to_31_elements_per_rank(vrc, orc, mode):
     """64-bit indexing: 2^31 + 7 bf16 elements per rank (4 GiB), 2 ranks,
     checked on sampled elements (chunk boundary, ends, beyond 2^31)."""
@@ -289,5 +289,69 @@ def test_more_than_2_to_31_elements_per_rank(vrc, orc, mode):
     for r in range(2):
         got = (workloads.to_numpy(ys[r][tidx]).astype(np.uint32) << 16).view(np.float32)
         assert np.array_equal(got, want), f"{mode} rank {r}"
+    del xs, ys
+    torch.cuda.empty_cache()
+
+
+def small_int_bf16(count, n, seed):
+    """n bf16 tensors of small integers: any summation order gives the exact sum."""
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return [torch.randint(-8, 9, (count,), generator=g, device=DEV, dtype=torch.int8).to(torch.bfloat16)
+            for _ in range(n)]
+
+
+def as_f32(t, idx):
+    """bf16 values of t at indices idx, widened to float32 on the host."""
+    return (workloads.to_numpy(t[torch.from_numpy(idx).to(t.device)]).astype(np.uint32) << 16).view(np.float32)
+
+
+def sample_idx(length, seed):
+    """Random indices of [0, length) plus both ends and the 2^31 and 2^32 boundaries."""
+    rng = np.random.default_rng(seed)
+    parts = [rng.integers(0, length, 200000), np.arange(0, 64), np.arange(length - 64, length)]
+    for b in (1 << 31, 1 << 32):
+        if b < length:
+            parts.append(np.arange(b - 64, min(b + 64, length)))
+    return np.unique(np.concatenate(parts)).astype(np.int64)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_reduce_scatter_chunks_past_2_to_31_elements(vrc, orc, mode):
+    """64-bit indexing in the reduce-scatter: 2 ranks of 2^32 + 17 bf16 elements
+    (8 GiB each), so both chunks hold more than 2^31 elements and chunk 1
+    starts 4 GiB into every input; chunk 1 has a one-element tail.  Checked
+    on sampled elements."""
+    say(f"reduce-scatter 2^32+17 elements {mode}")
+    count = (1 << 32) + 17
+    xs = small_int_bf16(count, 2, 411)
+    ys = vrc.vrc_reduce_scatter(xs, mode=mode)
+    torch.cuda.synchronize()
+    for c in range(2):
+        base = count // 2  # chunk c starts at c*base; the last chunk takes the remainder
+        off, length = c * base, (base if c == 0 else count - base)
+        assert ys[c].numel() == length
+        idx = sample_idx(length, 411 + c)
+        want = as_f32(xs[0], idx + off) + as_f32(xs[1], idx + off)
+        assert np.array_equal(as_f32(ys[c], idx), want), f"{mode} chunk {c}"
+    del xs, ys
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_all_gather_output_past_2_to_32_elements(vrc, orc, mode):
+    """64-bit indexing in the all-gather: 2 ranks of 2^31 + 8 bf16 elements,
+    so every output holds 2^32 + 16 elements (8 GiB) and slab 1 starts past
+    2^31 elements.  Checked on sampled elements of both outputs."""
+    say(f"all-gather 2^31+8 elements {mode}")
+    count = (1 << 31) + 8
+    xs = small_int_bf16(count, 2, 413)
+    ys = vrc.vrc_all_gather(xs, mode=mode)
+    torch.cuda.synchronize()
+    idx = sample_idx(2 * count, 413)
+    src = np.where(idx < count, 0, 1)
+    want = np.where(src == 0, as_f32(xs[0], np.minimum(idx, count - 1)),
+                    as_f32(xs[1], np.maximum(idx - count, 0)))
+    for r in range(2):
+        assert np.array_equal(as_f32(ys[r], idx), want), f"{mode} rank {r}"
     del xs, ys
     torch.cuda.empty_cache()
