@@ -3,7 +3,11 @@ counts (1-16), shapes, split dimensions, ragged sizes, element offsets that
 misalign the buffers (equal or different per rank) and in-place all-reduce,
 compared bit for bit with the oracle; and a smaller sweep above 64 MiB moved,
 where the all-reduce and reduce-scatter take their one-wave and flat shapes.
-Each case draws from its own seed, so a failure names a reproducible case."""
+Each case draws from its own seed, so a failure names a reproducible case.
+VRC_RANDOM_SEED_BASE (an integer, default 0) moves every case to a fresh
+seed family, for longer sweeps run by hand; 0 gives the committed cases."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +20,16 @@ from tests.test_gpu_parity import DTYPES, HD_FAMILY, MODES, want_ar, want_rs
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 CASES = 120
+SEED_BASE = int(os.environ.get("VRC_RANDOM_SEED_BASE", "0"))
+
+
+def case_rng(seed: int):
+    """The generator of one case: its own seed, in the chosen seed family."""
+    return np.random.default_rng(seed if SEED_BASE == 0 else [SEED_BASE, seed])
+
+
+def input_seed(seed: int) -> int:
+    return seed + 1_000_003 * SEED_BASE
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +46,7 @@ def orc():
 
 
 def draw(kind: int, k: int):
-    rng = np.random.default_rng(7919 * kind + k)
+    rng = case_rng(7919 * kind + k)
     dtype = str(rng.choice(DTYPES))
     mode = str(rng.choice(MODES))
     n = int(2 ** rng.integers(0, 5)) if mode in HD_FAMILY else int(rng.integers(1, 17))
@@ -75,7 +89,7 @@ def ranks(rng, n, shape, dtype, seed):
 def test_random_allreduce(vrc, orc, k):
     rng, dtype, mode, n = draw(1, k)
     count = log_uniform(rng, 70000)
-    xs = ranks(rng, n, (count,), dtype, seed=10000 + k)
+    xs = ranks(rng, n, (count,), dtype, seed=input_seed(10000 + k))
     in_place = rng.random() < 0.25
     print(f"random allreduce case {k}: {mode} {dtype} n={n} count={count} in_place={in_place}", flush=True)
     hx = host(xs)
@@ -102,7 +116,7 @@ def test_random_reduce_scatter(vrc, orc, k):
         shape[dim] = n * int(rng.integers(1, 200))
         shape = tuple(shape)
         outer = int(np.prod(shape[:dim]))
-    xs = ranks(rng, n, shape, dtype, seed=20000 + k)
+    xs = ranks(rng, n, shape, dtype, seed=input_seed(20000 + k))
     print(f"random reduce_scatter case {k}: {mode} {dtype} n={n} shape={shape} dim={dim}", flush=True)
     shapes = vrc.reduce_scatter_shape(shape, n, dim)
     ys = [empty_at(shapes[c], xs[0].dtype, o) for c, o in enumerate(offsets(rng, n))]
@@ -121,7 +135,7 @@ def test_random_all_gather(vrc, orc, k):
     shape = tuple(int(rng.integers(1, 9)) for _ in range(nd - 1)) + (log_uniform(rng, 800) + 1,)
     dim = int(rng.integers(0, nd))
     outer = int(np.prod(shape[:dim])) if dim else 1
-    xs = ranks(rng, n, shape, dtype, seed=30000 + k)
+    xs = ranks(rng, n, shape, dtype, seed=input_seed(30000 + k))
     print(f"random all_gather case {k}: {mode} {dtype} n={n} shape={shape} dim={dim}", flush=True)
     out_shape = list(shape)
     out_shape[dim] *= n
@@ -142,11 +156,11 @@ def test_random_all_gather(vrc, orc, k):
 # ---------------------------------------------------------------------------
 LARGE_CASES = 12
 LARGE_AR_MODES = ("fused", "ring_order", "ring_chained", "hd_order")
-LARGE_RS_MODES = ("fused", "ring_order", "hd_order", "hd")
+LARGE_RS_MODES = ("fused", "ring_order", "ring_chained", "hd_order", "hd")
 
 
 def draw_large(kind: int, k: int, modes):
-    rng = np.random.default_rng(104729 * kind + k)
+    rng = case_rng(104729 * kind + k)
     dtype = str(rng.choice(DTYPES))
     mode = str(rng.choice(modes))
     n = int(2 ** rng.integers(1, 5)) if mode in HD_FAMILY else int(rng.integers(2, 17))
@@ -164,8 +178,8 @@ def test_random_large_allreduce(vrc, orc, k):
         in_off, out_off = [off] * n, [off] * n
     else:
         in_off, out_off = offsets(rng, n), offsets(rng, n)
-    xs = [place(x, o) for x, o in zip(workloads.random_ranks(n, (count,), dtype, seed=40000 + k, device=DEV),
-                                      in_off)]
+    xs = workloads.random_ranks(n, (count,), dtype, seed=input_seed(40000 + k), device=DEV)
+    xs = [place(x, o) for x, o in zip(xs, in_off)]
     print(f"random large allreduce case {k}: {mode} {dtype} n={n} count={count} offsets {in_off[0]}/"
           f"{out_off[0]}", flush=True)
     hx = host(xs)
@@ -191,8 +205,8 @@ def test_random_large_reduce_scatter(vrc, orc, k):
         in_off, out_off = [off] * n, [off] * n
     else:
         in_off, out_off = offsets(rng, n), offsets(rng, n)
-    xs = [place(x, o) for x, o in zip(workloads.random_ranks(n, (count,), dtype, seed=50000 + k, device=DEV),
-                                      in_off)]
+    xs = workloads.random_ranks(n, (count,), dtype, seed=input_seed(50000 + k), device=DEV)
+    xs = [place(x, o) for x, o in zip(xs, in_off)]
     print(f"random large reduce_scatter case {k}: {mode} {dtype} n={n} count={count} offsets {in_off[0]}/"
           f"{out_off[0]}", flush=True)
     shapes = vrc.reduce_scatter_shape((count,), n, 0)
