@@ -101,6 +101,7 @@ struct Tuning {
     int step_unroll;          // 0: size policy; else vectors per lane per step iteration (1 or 2)
     int fused_block;          // 0: size policy; else lanes per fused all-reduce workgroup (64 or 256)
     int chain_block;          // 0: policy; else lanes per single-launch ring all-reduce workgroup (64 or 256)
+    int step_block;           // 0: size policy; else lanes per step workgroup (64, with one vector per lane, or 256)
 };
 
 const Tuning& tuning()
@@ -109,7 +110,8 @@ const Tuning& tuning()
                              env_int("VRC_STEP_BLOCKS_PER_CU", 0, 1, 64),
                              env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 0, 1, 2),
                              env_int("VRC_STEP_NT", -1, 0, 2), env_int("VRC_STEP_UNROLL", 0, 1, 2),
-                             env_int("VRC_FUSED_BLOCK", 0, 64, 256), env_int("VRC_CHAIN_BLOCK", 0, 64, 256)};
+                             env_int("VRC_FUSED_BLOCK", 0, 64, 256), env_int("VRC_CHAIN_BLOCK", 0, 64, 256),
+                             env_int("VRC_STEP_BLOCK", 0, 64, 256)};
     return t;
 }
 
@@ -185,22 +187,35 @@ FusedShape fused_ar_shape(uint64_t bytes_moved, int n)
 //   12 ranks x 341 MiB:  (2, 16) 3.876; (1, 4) 3.848; (2, 8) 3.985
 //   16 ranks x 256 MiB:  (2, 16) 3.423 (hd 3.578); (2, 8) 3.584 (hd 3.705); (1, 4) 3.958
 //   8 ranks x 16 MiB:    (1, 8) 0.115; (2, 16) 0.122 (48 MiB steps)
+// Adds of up to 7 operations of >= 48 MiB whose operations all vectorize
+// run one-wave workgroups, 8 per CU, one vector per lane.  One process, same
+// buffers, one reduce-scatter add step (GB/s; 256 lanes at 4 per CU -> one
+// wave at 8 per CU): 2 x 2 GiB 5,473 -> 5,804; 4 x 1 GiB 5,456 -> 5,779.
+// The copy steps lost with one wave (2 x 2 GiB 5,477 -> 5,051; 4 x 1 GiB
+// 5,740 -> 4,431) and keep 256 lanes; at 8 and 16 ranks neither kind gained
+// reliably.  A step with a scalar operation (operands on different 16-byte
+// offsets) keeps 256 lanes: its scalar elements need the lanes in flight
+// (5 x 819 MiB ring reduce-scatter: 3.05 ms with 256 lanes, 7.97 ms with one
+// wave).
 struct StepShape {
     int blocks_per_cu;
     int unroll;
+    int block;  // lanes per workgroup; 64 implies unroll 1
 };
 
-StepShape step_shape(uint64_t bytes_moved, int nops)
+StepShape step_shape(uint64_t bytes_moved, int nops, bool vector_add)
 {
-    StepShape s = {8, 1};
+    StepShape s = {8, 1, kBlock};
     const uint64_t per_op = bytes_moved / (uint64_t)(nops > 0 ? nops : 1);
     if (bytes_moved >= kGiB / 16) {
-        if (nops <= 7 && per_op >= 48 * kMiB) s = {4, 1};
-        else if (nops < 12 && per_op >= kGiB / 8) s = {8, 2};
-        else s = {16, 2};
+        if (nops <= 7 && per_op >= 48 * kMiB) s = vector_add ? StepShape{8, 1, 64} : StepShape{4, 1, kBlock};
+        else if (nops < 12 && per_op >= kGiB / 8) s = {8, 2, kBlock};
+        else s = {16, 2, kBlock};
     }
     if (tuning().step_blocks_per_cu) s.blocks_per_cu = tuning().step_blocks_per_cu;
     if (tuning().step_unroll) s.unroll = tuning().step_unroll;
+    if (tuning().step_block) s.block = tuning().step_block == 64 ? 64 : kBlock;
+    if (s.block == 64) s.unroll = 1;
     return s;
 }
 
@@ -456,8 +471,11 @@ struct Launch {
     static vrc_status_t step(const vrc::StepArgs& args, int nops, uint64_t work, int cus, hipStream_t st)
     {
         const uint64_t bytes = step_bytes<ADD>(args, nops);
-        const StepShape shape = step_shape(bytes, nops);
-        const dim3 grid(grid_x(cus, work, nops, shape.blocks_per_cu), (unsigned)nops);
+        bool vector = true;  // every operation's body runs 16-byte vectors
+        for (int i = 0; i < nops; i++)
+            if (args.op[i].g.head + args.op[i].g.tail >= 2 * (uint64_t)(16 / E)) vector = false;
+        const StepShape shape = step_shape(bytes, nops, ADD && vector);
+        const dim3 grid(grid_x(cus, work, nops, shape.blocks_per_cu, shape.block), (unsigned)nops);
         if (g_plan) {
             for (int i = 0; i < nops; i++) {
                 const vrc::StepOp& o = args.op[i];
@@ -474,7 +492,7 @@ struct Launch {
                 op.stride_d = o.sd;
                 op.grid_x = grid.x;
                 op.grid_y = grid.y;
-                op.block = kBlock;
+                op.block = (unsigned)shape.block;
                 op.vectors = (unsigned)shape.unroll;
                 plan_op(op);
             }
@@ -482,22 +500,27 @@ struct Launch {
             return VRC_OK;
         }
         const bool nt = step_nontemporal(ADD, bytes);
-        const bool u2 = shape.unroll == 2;
-        if (nops <= 4) launch_step<ADD, 4>(args, nops, nt, u2, grid, st);
-        else if (nops <= 8) launch_step<ADD, 8>(args, nops, nt, u2, grid, st);
-        else if (nops <= 16) launch_step<ADD, 16>(args, nops, nt, u2, grid, st);
-        else launch_step<ADD, vrc::kMaxStepOps>(args, nops, nt, u2, grid, st);
+        const bool u2 = shape.unroll == 2, wave = shape.block == 64;
+        if (nops <= 4) launch_step<ADD, 4>(args, nops, nt, u2, wave, grid, st);
+        else if (nops <= 8) launch_step<ADD, 8>(args, nops, nt, u2, wave, grid, st);
+        else if (nops <= 16) launch_step<ADD, 16>(args, nops, nt, u2, wave, grid, st);
+        else launch_step<ADD, vrc::kMaxStepOps>(args, nops, nt, u2, wave, grid, st);
         return check_launch();
     }
 
     // Launch a step with an argument block of K operation slots (the first
-    // nops filled; blockIdx.y < nops never reads the others).
+    // nops filled; blockIdx.y < nops never reads the others).  `wave`: one-wave
+    // workgroups, one vector per lane.
     template <bool ADD, int K>
-    static void launch_step(const vrc::StepArgs& args, int nops, bool nt, bool u2, dim3 grid, hipStream_t st)
+    static void launch_step(const vrc::StepArgs& args, int nops, bool nt, bool u2, bool wave, dim3 grid,
+                            hipStream_t st)
     {
         vrc::StepArgsK<K> a = {};
         for (int i = 0; i < nops && i < K; i++) a.op[i] = args.op[i];
-        if (u2) {
+        if (wave) {
+            if (nt) hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true, K, 1, 64>), grid, dim3(64), 0, st, a);
+            else hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, false, K, 1, 64>), grid, dim3(64), 0, st, a);
+        } else if (u2) {
             if (nt) hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, true, K, 2>), grid, dim3(kBlock), 0, st, a);
             else hipLaunchKernelGGL((vrc::k_ring_step<T, ADD, false, K, 2>), grid, dim3(kBlock), 0, st, a);
         } else {

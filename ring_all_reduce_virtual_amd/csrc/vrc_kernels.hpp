@@ -4,8 +4,9 @@
 // count, grid-stride iteration over 16-byte vectors, and a scalar pass for
 // the elements before the first 16-byte boundary and after the last one.
 // Workgroups have 256 lanes (four wave64s), except in the all-reduce kernels
-// that read every rank at once (fused and single-launch ring), which the host
-// may launch with workgroups of one wave (template argument B = 64).  No MFMA:
+// that read every rank at once (fused and single-launch ring) and the ring
+// step, which the host may launch with workgroups of one wave (template
+// argument B = 64).  No MFMA:
 // the work is a sum, not a contraction.
 //
 // Geometry.  An operand region is `rows` rows of `width` elements with a row
@@ -42,7 +43,8 @@ __device__ __forceinline__ void scalar_slot(uint64_t k, const RowSplit& g, uint6
 // Ring step: one launch runs one reduce-scatter step (d = a + b) or one
 // all-gather step (d = a) for every rank at once; blockIdx.y is the rank's
 // operation.  Both operands of an add are loaded before the add, and with
-// U = 2 a lane keeps two vectors (four loads of an add) in flight.
+// U = 2 a lane keeps two vectors (four loads of an add) in flight.  B lanes
+// per workgroup (256, or one wave for the large adds of a few ranks).
 // ---------------------------------------------------------------------------
 struct StepOp {
     const char* a;  // element (0,0) of the first operand region
@@ -63,12 +65,12 @@ struct StepArgsK {
 };
 using StepArgs = StepArgsK<kMaxStepOps>;
 
-template <class T, bool ADD, bool NT, int K, int U = 1>
-__global__ __launch_bounds__(kBlock) void k_ring_step(StepArgsK<K> args)
+template <class T, bool ADD, bool NT, int K, int U = 1, int B = kBlock>
+__global__ __launch_bounds__(B) void k_ring_step(StepArgsK<K> args)
 {
     const StepOp& op = args.op[blockIdx.y];
-    const uint64_t tid = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    const uint64_t nthreads = (uint64_t)gridDim.x * kBlock;
+    const uint64_t tid = (uint64_t)blockIdx.x * B + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * B;
     constexpr uint64_t E = T::ESZ;
 
     const uint64_t nv = op.rows * op.g.nvb;

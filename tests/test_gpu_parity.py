@@ -293,11 +293,12 @@ def test_workload_reduce_scatter_fp16_n8_act(vrc, orc):
 # every step launch shape (vectors per lane, workgroups per CU), ragged sizes
 # ---------------------------------------------------------------------------
 SHAPE_CASES = [  # (n, count, dtype, modes): the shape each case's large steps take
-    (3, 50_331_653, "fp16", ("ring",)),               # <= 7 operations of >= 48 MiB: one vector, 4 per CU
+    (3, 50_331_653, "fp16", ("ring",)),               # <= 7 operations of >= 48 MiB: one vector; adds one-wave
     (7, 8_388_613, "fp32", ("ring",)),                # <= 7 small operations: two vectors, 16 per CU
     (9, 104_857_601, "fp32", ("ring",)),              # 8-11 operations of >= 128 MiB: two vectors, 8 per CU
     (16, 16_777_219, "fp16", ("ring", "hd")),         # >= 12 operations: two vectors, 16 per CU
-    (2, 268_435_459, "bf16", ("ring", "hd")),         # 2 operations of 768 MiB: one vector, 4 per CU
+    (2, 268_435_459, "bf16", ("ring", "hd")),         # 2 operations of 768 MiB: one vector; adds one-wave
+    (5, 41_943_047, "fp32", ("ring",)),               # 5 adds of 96 MiB, one-wave; ragged last chunk
 ]
 
 

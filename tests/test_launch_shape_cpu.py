@@ -145,17 +145,48 @@ def test_fused_all_gather_sixteen_per_cu():
     assert launches(ops) == [("fused_all_gather", min((nv + 255) // 256, CUS * 16 // n), n, 256, 1)]
 
 
-@pytest.mark.parametrize("n,count,dtype,per_cu,vectors", [
-    (8, 268435456, vrc.VRC_BF16, 8, 2),    # 8 operations of >= 128 MiB: two vectors, 8 per CU
-    (4, 536870912, vrc.VRC_BF16, 4, 1),    # <= 7 operations of >= 48 MiB: one vector, 4 per CU
-    (16, 134217728, vrc.VRC_BF16, 16, 2),  # >= 12 operations: two vectors, 16 per CU
+@pytest.mark.parametrize("n,count,dtype,add_shape,copy_shape", [
+    # 8 operations of >= 128 MiB: two vectors, 8 per CU
+    (8, 268435456, vrc.VRC_BF16, (8, 256, 2), (8, 256, 2)),
+    # <= 7 operations of >= 48 MiB: adds one-wave, 8 per CU; copies 256 lanes, 4 per CU; one vector
+    (4, 536870912, vrc.VRC_BF16, (8, 64, 1), (4, 256, 1)),
+    (7, 153391689, vrc.VRC_FP32, (8, 64, 1), (4, 256, 1)),
+    (2, 268435459, vrc.VRC_BF16, (8, 64, 1), (4, 256, 1)),
+    # >= 12 operations: two vectors, 16 per CU
+    (16, 134217728, vrc.VRC_BF16, (16, 256, 2), (16, 256, 2)),
 ])
-def test_ring_step_shapes(n, count, dtype, per_cu, vectors):
+def test_ring_step_shapes(n, count, dtype, add_shape, copy_shape):
     got = plan_ar(n, count, dtype, vrc.VRC_RING)
     assert len(got) == 2 * (n - 1)
     for kind, gx, gy, block, vec in got:
         assert kind in ("add", "copy")
-        assert (gx, gy, block, vec) == (CUS * per_cu // n, n, 256, vectors)
+        per_cu, want_block, want_vec = add_shape if kind == "add" else copy_shape
+        assert (gx, gy, block, vec) == (CUS * per_cu // n, n, want_block, want_vec), kind
+
+
+def test_ring_reduce_scatter_adds_with_a_scalar_operation_keep_256_lanes():
+    """5 x 819 MiB bf16 reduce-scatter: chunk offsets of 171,756,748 bytes put
+    chunks 1-3 of the inputs on other 16-byte offsets than the outputs, so
+    those operations run scalar and the adds keep 256-lane workgroups; a count
+    whose chunks are whole vectors takes the one-wave adds."""
+    n = 5
+    send, recv = wide(n)
+    for count, block in ((5 * 85878374, 256), (5 * 85878368, 64)):
+        ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_RING)
+        got = launches(ops)
+        assert len(got) == n - 1
+        for kind, gx, gy, b, vec in got:
+            assert (kind, b, vec) == ("add", block, 1)
+            assert gx == CUS * (8 if block == 64 else 4) // n
+
+
+def test_halving_doubling_steps_take_the_step_shapes():
+    """4 x 1 GiB bf16: the halving adds (4 operations of >= 48 MiB) run
+    one-wave workgroups, the doubling copies 256 lanes."""
+    got = plan_ar(4, 536870912, vrc.VRC_BF16, vrc.VRC_HD)
+    assert [k for k, *_ in got] == ["add", "add", "copy", "copy"]
+    for kind, gx, gy, block, vec in got:
+        assert (gy, block, vec) == ((4, 64, 1) if kind == "add" else (4, 256, 1))
 
 
 def test_ring_steps_launch_bound_below_64_mib():
@@ -166,20 +197,21 @@ def test_ring_steps_launch_bound_below_64_mib():
 
 
 def test_environment_overrides_reach_the_plan():
-    """VRC_FUSED_BLOCK / VRC_FUSED_BLOCKS_PER_CU / VRC_UNROLL and
-    VRC_CHAIN_BLOCK / VRC_CHAIN_BLOCKS_PER_CU replace the policy (read once
-    per process, so a child process checks them)."""
+    """VRC_FUSED_BLOCK / VRC_FUSED_BLOCKS_PER_CU / VRC_UNROLL,
+    VRC_CHAIN_BLOCK / VRC_CHAIN_BLOCKS_PER_CU and VRC_STEP_BLOCK replace the
+    policy (read once per process, so a child process checks them)."""
     code = (
         "import ring_all_reduce_virtual_amd as v\n"
         "s=[(1<<40)+r*(1<<32) for r in range(8)]; d=[(1<<42)+r*(1<<32) for r in range(8)]\n"
         "f,_=v.plan(v.COLL_ALLREDUCE,s,d,268435456,1,v.VRC_BF16,v.VRC_FUSED)\n"
         "c,_=v.plan(v.COLL_ALLREDUCE,s,d,268435456,1,v.VRC_BF16,v.VRC_RING_CHAINED)\n"
-        "print(f[0]['grid_x'],f[0]['block'],f[0]['vectors'],c[0]['grid_x'],c[0]['block'])\n")
+        "r,_=v.plan(v.COLL_ALLREDUCE,s[:4],d[:4],536870912,1,v.VRC_BF16,v.VRC_RING)\n"
+        "print(f[0]['grid_x'],f[0]['block'],f[0]['vectors'],c[0]['grid_x'],c[0]['block'],r[0]['block'])\n")
     env = dict(os.environ, VRC_FUSED_BLOCK="256", VRC_FUSED_BLOCKS_PER_CU="1", VRC_UNROLL="2",
-               VRC_CHAIN_BLOCK="256", VRC_CHAIN_BLOCKS_PER_CU="4", PYTHONPATH=ROOT)
+               VRC_CHAIN_BLOCK="256", VRC_CHAIN_BLOCKS_PER_CU="4", VRC_STEP_BLOCK="256", PYTHONPATH=ROOT)
     out = subprocess.run([sys.executable, "-c", code], env=env, check=True, capture_output=True, text=True,
                          cwd=ROOT).stdout.split()
-    assert list(map(int, out)) == [256, 256, 2, 1024, 256]
+    assert list(map(int, out)) == [256, 256, 2, 1024, 256, 256]
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 8, 9, 16])
