@@ -113,8 +113,31 @@ __global__ __launch_bounds__(B) void k_ring_step(StepArgsK<K> args)
         }
     }
 
+    // Scalar elements.  A region whose operands sit on different 16-byte
+    // offsets is all scalar, so a lane takes SU elements per iteration and
+    // issues all their loads before the adds and stores.
+    constexpr int SU = 8;
     const uint64_t ns = op.rows * (op.g.head + op.g.tail);
-    for (uint64_t k = tid; k < ns; k += nthreads) {
+    uint64_t k = tid;
+    for (; k + (SU - 1) * nthreads < ns; k += SU * nthreads) {
+        typename T::S x[SU], y[SU];
+        uint64_t od[SU];
+#pragma unroll
+        for (int u = 0; u < SU; u++) {
+            uint64_t row, col;
+            scalar_slot(k + u * nthreads, op.g, T::VEC, row, col);
+            x[u] = load_s<T>(op.a + (row * op.sa + col) * E);
+            if constexpr (ADD) y[u] = load_s<T>(op.b + (row * op.sb + col) * E);
+            od[u] = (row * op.sd + col) * E;
+        }
+        issue_loads_first();
+#pragma unroll
+        for (int u = 0; u < SU; u++) {
+            if constexpr (ADD) x[u] = add_s<T>(x[u], y[u]);
+            store_s<T>(op.d + od[u], x[u]);
+        }
+    }
+    for (; k < ns; k += nthreads) {
         uint64_t row, col;
         scalar_slot(k, op.g, T::VEC, row, col);
         typename T::S x = load_s<T>(op.a + (row * op.sa + col) * E);
