@@ -300,8 +300,31 @@ __global__ __launch_bounds__(kBlock) void k_fused_reduce_scatter(FusedRsArgs a)
         issue_loads_first();
         st16<NT>(c.d + row * c.s_dst * E + col, Fold::template vec<T, N>(in));
     }
+    // Scalar elements.  A chunk whose inputs and output sit on different
+    // 16-byte offsets is all scalar, so a lane takes SU elements per
+    // iteration (about 16 loads) and issues their loads first.
+    constexpr int SU = N >= 16 ? 1 : 16 / N;
     const uint64_t ns = c.rows * (c.g.head + c.g.tail);
-    for (uint64_t k = tid; k < ns; k += nthreads) {
+    uint64_t k = tid;
+    if constexpr (SU > 1) {
+        for (; k + (SU - 1) * nthreads < ns; k += SU * nthreads) {
+            typename T::S in[SU][N];
+            uint64_t od[SU];
+#pragma unroll
+            for (int u = 0; u < SU; u++) {
+                uint64_t row, col;
+                scalar_slot(k + u * nthreads, c.g, T::VEC, row, col);
+                const uint64_t so = (c.src_off + row * c.s_src + col) * E;
+#pragma unroll
+                for (int r = 0; r < N; r++) in[u][r] = load_s<T>(a.src[r] + so);
+                od[u] = (row * c.s_dst + col) * E;
+            }
+            issue_loads_first();
+#pragma unroll
+            for (int u = 0; u < SU; u++) store_s<T>(c.d + od[u], Fold::template scalar<T, N>(in[u]));
+        }
+    }
+    for (; k < ns; k += nthreads) {
         uint64_t row, col;
         scalar_slot(k, c.g, T::VEC, row, col);
         const uint64_t so = (c.src_off + row * c.s_src + col) * E;
