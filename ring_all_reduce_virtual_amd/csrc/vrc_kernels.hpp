@@ -694,7 +694,38 @@ __global__ __launch_bounds__(kBlock) void k_ring_chain_reduce_scatter(ChainArgs 
         chain_rs_block<N, MEM, VecIO<T, NT>>(in, (k.off + row * k.stride) * E + col, out + row * k.width * E + col);
     }
     const uint64_t ns = k.rows * (k.g.head + k.g.tail);
-    for (uint64_t j = tid; j < ns; j += nthreads) {
+    uint64_t j = tid;
+    if constexpr (!MEM) {
+        // A chunk whose inputs and output sit on different 16-byte offsets
+        // is all scalar: a lane takes SU elements per iteration (about 16
+        // loads) and issues their loads before the ring-order folds.
+        using IO = ScalarIO<T>;
+        constexpr int SU = N >= 16 ? 1 : 16 / N;
+        if constexpr (SU > 1) {
+            for (; j + (SU - 1) * nthreads < ns; j += SU * nthreads) {
+                typename T::S x[SU][N];
+                uint64_t od[SU];
+#pragma unroll
+                for (int u = 0; u < SU; u++) {
+                    uint64_t row, col;
+                    scalar_slot(j + u * nthreads, k.g, T::VEC, row, col);
+                    const uint64_t so = (k.off + row * k.stride + col) * E;
+#pragma unroll
+                    for (int t = 0; t < N; t++) x[u][t] = IO::ld_in(in[t] + so);
+                    od[u] = (row * k.width + col) * E;
+                }
+                issue_loads_first();
+#pragma unroll
+                for (int u = 0; u < SU; u++) {
+                    typename T::S p = x[u][0];
+#pragma unroll
+                    for (int t = 1; t < N; t++) p = IO::add(p, x[u][t]);
+                    IO::st_out(out + od[u], p);
+                }
+            }
+        }
+    }
+    for (; j < ns; j += nthreads) {
         uint64_t row, col;
         scalar_slot(j, k.g, T::VEC, row, col);
         chain_rs_block<N, MEM, ScalarIO<T>>(in, (k.off + row * k.stride + col) * E, out + (row * k.width + col) * E);
