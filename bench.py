@@ -18,7 +18,7 @@ same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--mode fused|ring|ring_chained|ring_order|hd|hd_order|select]
-       python bench.py --suite | --overlap | --probe-copy
+       python bench.py --suite | --offsets | --overlap | --probe-copy
 """
 from __future__ import annotations
 
@@ -251,6 +251,88 @@ def run_suite(steps: int, torch, vrc, workloads) -> int:
     return 0
 
 
+def interleaved_us(torch, calls: dict, steps: int, rounds: int = 4) -> dict:
+    """Median HIP-event time (us) of each named call, the calls interleaved
+    over `rounds` rounds in one process (the same buffers, the same DRAM
+    placement for every call of a pair)."""
+    ms = {k: [] for k in calls}
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(rounds):
+        for name, fn in calls.items():
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(max(1, steps // rounds))]
+            for e0, e1 in evs:
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            ms[name].extend(e0.elapsed_time(e1) for e0, e1 in evs)
+    return {k: sorted(v)[len(v) // 2] * 1e3 for k, v in ms.items()}
+
+
+def offset_views(torch, xs, offsets):
+    """Copies of `xs` placed `offsets[r]` elements into fresh buffers."""
+    out = []
+    for x, off in zip(xs, offsets):
+        buf = torch.empty(x.numel() + 64, dtype=x.dtype, device=x.device)
+        v = buf[off:off + x.numel()]
+        v.copy_(x.reshape(-1))
+        out.append(v)
+    return out
+
+
+def run_offsets(steps: int, torch, vrc, workloads) -> int:
+    """Operands on other offsets than their destination's 128-byte grid, each
+    timed beside its aligned twin in the same process (one JSON line each):
+
+    * the 8 x 512 MiB bf16 all-reduce with rank r's input r elements and its
+      output (3r mod 8) elements into fresh buffers, so no two operands share
+      an offset, against the aligned buffers, in every mode;
+    * a 5-rank bf16 reduce-scatter of about 819 MiB per rank whose chunk bytes
+      are odd multiples of 2 (inputs' chunks off the outputs' grid), against a
+      count whose chunks are whole 128-byte multiples."""
+    dev = "cuda:0"
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    xs = workloads.make_inputs(w, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    mx = offset_views(torch, xs, list(range(w.n)))
+    my = offset_views(torch, ys, [3 * r % 8 for r in range(w.n)])
+    for mode in vrc.MODES:
+        t = interleaved_us(torch, {
+            "aligned": lambda: vrc.vrc_allreduce(xs, recv=ys, mode=mode),
+            "offset": lambda: vrc.vrc_allreduce(mx, recv=my, mode=mode)}, steps)
+        rec = {"offsets": "allreduce_bf16_n8_512mib, rank r input +r, output +3r mod 8 elements", "mode": mode,
+               "aligned_us": round(t["aligned"], 1), "offset_us": round(t["offset"], 1),
+               "offset_over_aligned": round(t["offset"] / t["aligned"], 4)}
+        print(json.dumps(rec), flush=True)
+        log(f"offsets AR {mode:13s} aligned {t['aligned']:9.1f} us  offset {t['offset']:9.1f} us "
+            f" x{t['offset'] / t['aligned']:.3f}")
+    del xs, ys, mx, my
+    torch.cuda.empty_cache()
+    n = 5
+    whole = n * 85878336  # chunk bytes a multiple of 128
+    ragged = n * 85878375  # chunk bytes 171,756,750: chunks 1..4 of the inputs off the outputs' grid
+    xw = workloads.random_ranks(n, whole, "bf16", seed=61, device=dev, sigma=1e-2)
+    xr = workloads.random_ranks(n, ragged, "bf16", seed=62, device=dev, sigma=1e-2)
+    yw = vrc.vrc_reduce_scatter(xw)
+    yr = vrc.vrc_reduce_scatter(xr)
+    for mode in ("ring", "fused", "ring_chained", "ring_order"):
+        t = interleaved_us(torch, {
+            "aligned": lambda: vrc.vrc_reduce_scatter(xw, recv=yw, mode=mode),
+            "offset": lambda: vrc.vrc_reduce_scatter(xr, recv=yr, mode=mode)}, steps)
+        # per-element time, so the two counts compare directly
+        a_ns, o_ns = t["aligned"] / whole * 1e3, t["offset"] / ragged * 1e3
+        rec = {"offsets": f"reduce_scatter bf16 {n} ranks, count {ragged} (ragged chunks) vs {whole}",
+               "mode": mode, "aligned_us": round(t["aligned"], 1), "offset_us": round(t["offset"], 1),
+               "offset_over_aligned": round(o_ns / a_ns, 4)}
+        print(json.dumps(rec), flush=True)
+        log(f"offsets RS {mode:13s} aligned {t['aligned']:9.1f} us  ragged {t['offset']:9.1f} us  x{o_ns / a_ns:.3f}")
+    return 0
+
+
 def run_overlap(steps: int, mode: str, torch, vrc, workloads) -> int:
     """Overlap of the all-reduce with compute on two streams (the pages'
     compute/communication overlap: the collective runs on its own stream,
@@ -327,6 +409,8 @@ def main() -> int:
                     help="time the all-reduce alone, a matmul stream alone, and both on two streams")
     ap.add_argument("--suite", action="store_true",
                     help="measure every workload in every mode (one JSON line each) instead of the headline")
+    ap.add_argument("--offsets", action="store_true",
+                    help="time operands off their destination's grid beside their aligned twins")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB (known HBM traffic: 1 GiB read, 1 GiB "
                          "written per launch), for calibrating rocprofv3 byte counters")
@@ -348,6 +432,8 @@ def main() -> int:
         return 1
     if args.suite:
         return run_suite(args.steps, torch, vrc, workloads)
+    if args.offsets:
+        return run_offsets(args.steps, torch, vrc, workloads)
     if args.overlap:
         return run_overlap(args.steps, args.mode, torch, vrc, workloads)
     if args.probe_copy:

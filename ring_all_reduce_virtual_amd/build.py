@@ -10,7 +10,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvrc.so")
-SOURCES = [os.path.join(CSRC, "vrc_api.hip")]
+# One translation unit per element type holds that type's kernels; vrc_api.hip
+# holds the C ABI.  They compile in parallel.
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("vrc_type_bf16.hip", "vrc_type_f16.hip", "vrc_type_f32.hip", "vrc_type_i32.hip", "vrc_api.hip")]
+OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -19,7 +23,7 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
+    "-fvisibility=hidden",
     # Adds only, but never let the compiler contract or reassociate them.
     "-ffp-contract=off",
     "-fno-fast-math",
@@ -47,9 +51,31 @@ def build_c_check(verbose: bool = False) -> str:
     return C_CHECK_BIN
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source to an object (in parallel) and link libvrc.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
+    objs, pending = [], []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        pending.append(cmd)
+    running = []
+    failed = None
+    while pending or running:
+        while pending and len(running) < jobs:
+            cmd = pending.pop(0)
+            running.append((cmd, subprocess.Popen(cmd)))
+        cmd, proc = running.pop(0)
+        if proc.wait() != 0 and failed is None:
+            failed = cmd
+    if failed is not None:
+        raise subprocess.CalledProcessError(1, failed)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

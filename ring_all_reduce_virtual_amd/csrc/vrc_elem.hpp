@@ -15,6 +15,15 @@
 namespace vrc {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// The same 16 bytes at any address.  The HSA ABI runs the GPU in unaligned
+// access mode, so one global_load/store_dwordx4 serves an operand on any byte
+// offset (for this target the compiler emits that single instruction even for
+// a 16-byte memcpy from a char pointer).  The hardware reads and writes the
+// cache lines such a vector straddles, so misalignment costs bandwidth only
+// where a wave's 1 KiB run crosses a line or write block that another wave
+// also touches (measured on MI355X, 8 x 512 MiB fused bf16 all-reduce: inputs
+// on other offsets +8 %, outputs on other 64-byte offsets +22 %).
+typedef u32x4 u32x4_any __attribute__((aligned(1)));
 
 // Every buffer the library is given is device (global) memory.  Accessing it
 // through global address-space pointers gives global_load/global_store
@@ -24,12 +33,13 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <class X>
 using global_ptr = __attribute__((address_space(1))) X*;
 
-// 16-byte load/store, optionally with the non-temporal hint (streaming data
-// that is never re-read should not displace other lines from the caches).
+// 16-byte load/store at any element alignment, optionally with the
+// non-temporal hint (streaming data that is never re-read should not displace
+// other lines from the caches).
 template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const char* p)
 {
-    const auto g = (global_ptr<const u32x4>)p;
+    const auto g = (global_ptr<const u32x4_any>)p;
     if constexpr (NT) return __builtin_nontemporal_load(g);
     else return *g;
 }
@@ -37,7 +47,7 @@ __device__ __forceinline__ u32x4 ld16(const char* p)
 template <bool NT>
 __device__ __forceinline__ void st16(char* p, u32x4 v)
 {
-    const auto g = (global_ptr<u32x4>)p;
+    const auto g = (global_ptr<u32x4_any>)p;
     if constexpr (NT) __builtin_nontemporal_store(v, g);
     else *g = v;
 }

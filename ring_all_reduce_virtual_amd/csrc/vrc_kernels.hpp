@@ -11,10 +11,11 @@
 //
 // Geometry.  An operand region is `rows` rows of `width` elements with a row
 // stride in elements.  The host splits each row into `head` scalar elements
-// (up to the first 16-byte boundary), `nvb` 16-byte vectors and `tail`
-// scalar elements; when the operands of one region do not share the same
-// address offset modulo 16 (or a row stride is not a multiple of 16 bytes)
-// it sets head = width, nvb = tail = 0 and the region runs scalar.
+// (up to the destination's first 128-byte boundary), `nvb` 16-byte vectors
+// and `tail` scalar elements (less than one vector).  Operands on other
+// offsets than the destination still move in 16-byte vectors (unaligned
+// access), so only heads and tails run scalar: at most 127 + 15 bytes per
+// row.
 #pragma once
 
 #include "vrc_elem.hpp"
@@ -113,9 +114,9 @@ __global__ __launch_bounds__(B) void k_ring_step(StepArgsK<K> args)
         }
     }
 
-    // Scalar elements.  A region whose operands sit on different 16-byte
-    // offsets is all scalar, so a lane takes SU elements per iteration and
-    // issues all their loads before the adds and stores.
+    // Scalar elements: heads and tails, which make up whole regions of many
+    // narrow rows.  A lane takes SU elements per iteration and issues all
+    // their loads before the adds and stores.
     constexpr int SU = 8;
     const uint64_t ns = op.rows * (op.g.head + op.g.tail);
     uint64_t k = tid;
@@ -300,9 +301,9 @@ __global__ __launch_bounds__(kBlock) void k_fused_reduce_scatter(FusedRsArgs a)
         issue_loads_first();
         st16<NT>(c.d + row * c.s_dst * E + col, Fold::template vec<T, N>(in));
     }
-    // Scalar elements.  A chunk whose inputs and output sit on different
-    // 16-byte offsets is all scalar, so a lane takes SU elements per
-    // iteration (about 16 loads) and issues their loads first.
+    // Scalar elements (heads, tails; whole chunks of many narrow rows): a
+    // lane takes SU elements per iteration (about 16 loads) and issues their
+    // loads first.
     constexpr int SU = N >= 16 ? 1 : 16 / N;
     const uint64_t ns = c.rows * (c.g.head + c.g.tail);
     uint64_t k = tid;
@@ -536,8 +537,8 @@ __global__ __launch_bounds__(B) void k_ring_chain_allreduce(ChainArgs a)
         if (v < nvb) chain_block<N, MEM, VecIO<T, NT>>(in, out, body + v * 16);
     }
 
-    // Scalar head and tail elements (fewer than 2 * VEC per chunk): one wave
-    // per chunk, so the chunk stays uniform here too.
+    // Scalar head and tail elements (at most 127 + 15 bytes per chunk): one
+    // wave per chunk, so the chunk stays uniform here too.
     for (uint64_t cw = wave; cw < (uint64_t)N; cw += nwaves) {
         const int c = __builtin_amdgcn_readfirstlane((int)cw);
         const ChainChunk& k = a.ch[c];
@@ -696,9 +697,9 @@ __global__ __launch_bounds__(kBlock) void k_ring_chain_reduce_scatter(ChainArgs 
     const uint64_t ns = k.rows * (k.g.head + k.g.tail);
     uint64_t j = tid;
     if constexpr (!MEM) {
-        // A chunk whose inputs and output sit on different 16-byte offsets
-        // is all scalar: a lane takes SU elements per iteration (about 16
-        // loads) and issues their loads before the ring-order folds.
+        // Heads, tails and chunks of many narrow rows: a lane takes SU
+        // elements per iteration (about 16 loads) and issues their loads
+        // before the ring-order folds.
         using IO = ScalarIO<T>;
         constexpr int SU = N >= 16 ? 1 : 16 / N;
         if constexpr (SU > 1) {

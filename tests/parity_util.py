@@ -1,6 +1,9 @@
 """Helpers for comparing HIP outputs with the oracle (host-side plumbing)."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -83,3 +86,35 @@ def sample_indices(count: int, n: int, m: int, seed: int) -> np.ndarray:
         parts.append(np.arange(max(0, b - 9), min(count, b + 9)))
     idx = np.unique(np.concatenate(parts))
     return idx[(idx >= 0) & (idx < count)].astype(np.uint64)
+
+
+def oracle_every_element(at, hx, dtype: str, count: int, slice_elems: int = 1 << 22) -> np.ndarray:
+    """All `count` elements of an all-reduce result from one of the oracle's
+    per-element forms (`ring_allreduce_at`, `hd_allreduce_at`,
+    `fused_allreduce_at`), computed in slices on host threads: the oracle's C
+    code runs with the interpreter lock released, so the slices proceed in
+    parallel.  The forms are pinned against the full ring simulation by the
+    CPU tests."""
+    out = np.empty(count, dtype=hx[0].dtype)
+
+    def work(lo):
+        hi = min(count, lo + slice_elems)
+        out[lo:hi] = at(hx, dtype, np.arange(lo, hi, dtype=np.uint64))
+
+    with ThreadPoolExecutor(max_workers=max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        list(ex.map(work, range(0, count, slice_elems)))
+    return out
+
+
+def equal_to_expected(ys, want: torch.Tensor, what: str):
+    """Every rank's output bit for bit equal to `want` (on the device); on a
+    mismatch, name the first differing elements."""
+    wb = want.reshape(-1).view(torch.uint8)
+    esz = want.element_size()
+    for r, y in enumerate(ys):
+        yb = y.contiguous().reshape(-1).view(torch.uint8)
+        if not torch.equal(yb, wb):
+            diff = (yb.view(-1, esz) != wb.view(-1, esz)).any(dim=1).nonzero().reshape(-1)
+            first = diff[:8].tolist()
+            raise AssertionError(f"{what}: rank {r}: {diff.numel()} of {want.numel()} elements differ; "
+                                 f"first at {first}")

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity_util import assert_bitwise, host
+from tests.parity_util import assert_bitwise, equal_to_expected, host, oracle_every_element
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -118,6 +118,43 @@ def test_misaligned_views(vrc, orc, mode, dtype, offsets):
     for c in range(n):
         assert_bitwise(workloads.to_numpy(rs[c]), want_rs[c], f"misaligned rs {mode} {dtype} chunk {c}")
         assert_bitwise(workloads.to_numpy(ag[c]), want_ag[c], f"misaligned ag {mode} {dtype} rank {c}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_large_allreduce_on_mixed_offsets(vrc, orc, mode):
+    """8 ranks x (6 Mi + 5) bf16, about 96 MiB moved (the launch shapes of
+    large calls): rank r's input starts r elements and its output (3r mod 8)
+    elements into a fresh buffer, so no two operands share an offset.  Every
+    element of every rank against the oracle's per-element form."""
+    n, count = 8, 6 * (1 << 20) + 5
+    say(f"large mixed offsets {mode}: n={n} count={count}")
+    xs = workloads.random_ranks(n, count, "bf16", seed=4101, device=DEV, sigma=1e-2)
+    vx = _views(xs, list(range(n)), count)
+    vy = _views([torch.zeros_like(x) for x in xs], [3 * r % 8 for r in range(n)], count)
+    vrc.vrc_allreduce(vx, recv=vy, mode=mode)
+    torch.cuda.synchronize()
+    at = {"ring": orc.ring_allreduce_at, "hd": orc.hd_allreduce_at, "fused": orc.fused_allreduce_at}[
+        "ring" if mode in RING_FAMILY else "hd" if mode in HD_FAMILY else "fused"]
+    want = torch.from_numpy(oracle_every_element(at, host(xs), "bf16", count)).to(DEV)
+    equal_to_expected(vy, want, f"large mixed offsets {mode}")
+
+
+@pytest.mark.parametrize("mode,n", [("ring", 5), ("fused", 5), ("ring_chained", 5), ("ring_order", 5),
+                                    ("hd", 8), ("hd_order", 8)])
+def test_large_ragged_flat_reduce_scatter(vrc, orc, mode, n):
+    """A flat bf16 reduce-scatter whose chunk bytes are odd multiples of 2
+    (count = n * base + 3, base odd): chunk c of every input sits on another
+    16-byte offset than output c.  Above 64 MiB moved, so the flat kernels
+    run; every element of every chunk against the oracle's simulation."""
+    base = 3 * (1 << 21) + 3
+    count = n * base + 3
+    say(f"large ragged reduce-scatter {mode}: n={n} count={count}")
+    xs = workloads.random_ranks(n, count, "bf16", seed=4201 + n, device=DEV, sigma=1e-2)
+    ys = vrc.vrc_reduce_scatter(xs, mode=mode)
+    torch.cuda.synchronize()
+    want = oracle_rs(orc, host(xs), "bf16", mode)
+    for c, y in enumerate(ys):
+        assert_bitwise(workloads.to_numpy(y), want[c], f"large ragged rs {mode} chunk {c}")
 
 
 @pytest.mark.parametrize("mode", MODES)

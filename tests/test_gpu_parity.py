@@ -2,11 +2,12 @@
 
 Small cases span several 4 KiB lane tiles and a ragged tail and are compared
 element by element with the oracle's full simulation.  The named workloads
-run at full size in the launch configuration the benchmark times; where the
-oracle is too slow for every element (128 MiB and 512 MiB per rank) they are
-compared on sampled elements through the oracle's per-element forms, and on
-every element through properties (all ranks identical, the fp64 tolerance
-gate).
+run at full size in the launch configuration the benchmark times.  At 128 MiB
+and 512 MiB per rank the oracle's full simulation would take minutes, so every
+element of every rank is compared with the oracle's per-element forms (the
+ring, halving-doubling and rank-fold closed forms, pinned against the
+simulation on the CPU), computed on host threads; the fp64 tolerance gate
+runs on every element as well.
 """
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity_util import (assert_bitwise, host, ranks_identical, sample_indices,
+from tests.parity_util import (assert_bitwise, equal_to_expected, host, oracle_every_element, ranks_identical,
                                tolerance_gate_torch)
 
 pytestmark = pytest.mark.gpu
@@ -224,36 +225,42 @@ def gate_rtol(w, mode: str) -> float:
     return w.rtol
 
 
-def _sampled_allreduce(vrc, orc, w, modes, m):
+def _full_allreduce(vrc, orc, w, modes):
+    """Every mode on the full workload: every element of every rank bit for
+    bit against the oracle's per-element form of the mode's algorithm (one
+    expected array per algorithm family), plus the tolerance gate."""
     xs = workloads.make_inputs(w, DEV)
     hx = host(xs)
-    idx = sample_indices(w.count, w.n, m, seed=w.seed)
-    tidx = torch.from_numpy(idx.astype(np.int64)).to(DEV)
+    families = {}
     for mode in modes:
-        say(f"{w.name} {mode} ({idx.size} sampled elements)")
-        ys = vrc.vrc_allreduce(xs, mode=mode)
-        torch.cuda.synchronize()
-        ranks_identical(ys, f"{w.name} {mode}")
-        tolerance_gate_torch(ys, xs, gate_rtol(w, mode), f"{w.name} {mode}")
-        at = (orc.ring_allreduce_at if mode in RING_FAMILY else
-              orc.hd_allreduce_at if mode in HD_FAMILY else orc.fused_allreduce_at)
-        want = at(hx, w.dtype, idx)
-        for r in (0, w.n - 1):
-            got = workloads.to_numpy(ys[r].reshape(-1)[tidx])
-            assert_bitwise(got, want, f"{w.name} {mode} rank {r} sampled")
-        del ys
-        torch.cuda.empty_cache()
+        fam = "ring" if mode in RING_FAMILY else "hd" if mode in HD_FAMILY else "fused"
+        families.setdefault(fam, []).append(mode)
+    for fam, fam_modes in families.items():
+        at = {"ring": orc.ring_allreduce_at, "hd": orc.hd_allreduce_at, "fused": orc.fused_allreduce_at}[fam]
+        say(f"{w.name}: oracle {fam} form on all {w.count} elements")
+        want = torch.from_numpy(oracle_every_element(at, hx, w.dtype, w.count)).to(DEV)
+        for mode in fam_modes:
+            say(f"{w.name} {mode}: every element of every rank")
+            ys = vrc.vrc_allreduce(xs, mode=mode)
+            torch.cuda.synchronize()
+            equal_to_expected(ys, want, f"{w.name} {mode}")
+            tolerance_gate_torch(ys, xs, gate_rtol(w, mode), f"{w.name} {mode}")
+            del ys
+            torch.cuda.empty_cache()
+        del want
 
 
 def test_workload_allreduce_fp16_n8_128mib(vrc, orc):
     w = workloads.WORKLOADS["allreduce_fp16_n8_128mib"]
-    _sampled_allreduce(vrc, orc, w, MODES, m=1 << 20)
+    _full_allreduce(vrc, orc, w, MODES)
 
 
-def test_workload_allreduce_bf16_n8_512mib(vrc, orc):
+@pytest.mark.parametrize("family", ["fused", "ring", "hd"])
+def test_workload_allreduce_bf16_n8_512mib(vrc, orc, family):
+    # fused is the headline mode; the ring and halving-doubling families run too (not gated by the workload)
     w = workloads.WORKLOADS["allreduce_bf16_n8_512mib"]
-    # fused is the headline mode; the ring family runs too (not gated by the workload)
-    _sampled_allreduce(vrc, orc, w, MODES, m=1 << 20)
+    modes = {"fused": ("fused",), "ring": RING_FAMILY, "hd": HD_FAMILY}[family]
+    _full_allreduce(vrc, orc, w, modes)
 
 
 def test_workload_all_gather_fp16_n8_heads(vrc, orc):
@@ -307,17 +314,13 @@ def test_step_launch_shapes(vrc, orc, n, count, dtype, modes):
     say(f"step shapes n={n} count={count} {dtype} {modes}")
     xs = workloads.random_ranks(n, count, dtype, seed=500 + n, device=DEV)
     hx = host(xs)
-    idx = sample_indices(count, n, 1 << 18, seed=n)
-    tidx = torch.from_numpy(idx.astype(np.int64)).to(DEV)
     for mode in modes:
         ys = vrc.vrc_allreduce(xs, mode=mode)
         torch.cuda.synchronize()
-        ranks_identical(ys, f"{mode} n={n}")
-        want = (orc.ring_allreduce_at if mode in RING_FAMILY else orc.hd_allreduce_at)(hx, dtype, idx)
-        for r in (0, n - 1):
-            got = workloads.to_numpy(ys[r].reshape(-1)[tidx])
-            assert_bitwise(got, want, f"{mode} {dtype} n={n} count={count} rank {r} sampled")
-        del ys
+        at = orc.ring_allreduce_at if mode in RING_FAMILY else orc.hd_allreduce_at
+        want = torch.from_numpy(oracle_every_element(at, hx, dtype, count)).to(DEV)
+        equal_to_expected(ys, want, f"{mode} {dtype} n={n} count={count}")
+        del ys, want
         torch.cuda.empty_cache()
 
 

@@ -1,13 +1,12 @@
 """VRC_SELECT on the GPU: the plan names the algorithm the library picked
 (halving-doubling or ring, by the rule in include/vrc.h), and the result
 must be that algorithm's bits, checked against its oracle."""
-import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from tests.parity_util import assert_bitwise, host, ranks_identical, sample_indices
+from tests.parity_util import assert_bitwise, equal_to_expected, host, oracle_every_element, ranks_identical
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -72,12 +71,9 @@ def test_select_at_the_limit(vrc, orc, extra, alg):
     vrc.vrc_allreduce(xs, recv=ys, mode="select")
     torch.cuda.synchronize()
     ranks_identical(ys, f"select {alg}")
-    hx = host(xs)
-    idx = sample_indices(count, 8, 1 << 16, seed=5)
-    want = (orc.hd_allreduce_at if alg == "hd" else orc.ring_allreduce_at)(hx, "fp32", idx)
-    tidx = torch.from_numpy(idx.astype(np.int64)).to(DEV)
-    for r in (0, 7):
-        assert_bitwise(workloads.to_numpy(ys[r][tidx]), want, f"select at the limit ({alg}) rank {r}")
+    at = orc.hd_allreduce_at if alg == "hd" else orc.ring_allreduce_at
+    want = torch.from_numpy(oracle_every_element(at, host(xs), "fp32", count)).to(DEV)
+    equal_to_expected(ys, want, f"select at the limit ({alg})")
 
 
 def test_select_large_workload_runs_the_ring(vrc, orc):
@@ -88,11 +84,8 @@ def test_select_large_workload_runs_the_ring(vrc, orc):
     assert picked(vrc, vrc.COLL_ALLREDUCE, xs, ys, w.count, 1, "fp16") == "ring"
     vrc.vrc_allreduce(xs, recv=ys, mode="select")
     torch.cuda.synchronize()
-    idx = sample_indices(w.count, w.n, 1 << 16, seed=w.seed)
-    want = orc.ring_allreduce_at(host(xs), "fp16", idx)
-    tidx = torch.from_numpy(idx.astype(np.int64)).to(DEV)
-    for r in (0, w.n - 1):
-        assert_bitwise(workloads.to_numpy(ys[r][tidx]), want, f"select {w.name} rank {r}")
+    want = torch.from_numpy(oracle_every_element(orc.ring_allreduce_at, host(xs), "fp16", w.count)).to(DEV)
+    equal_to_expected(ys, want, f"select {w.name}")
 
 
 @pytest.mark.parametrize("n", [8, 6])

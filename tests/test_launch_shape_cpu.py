@@ -164,20 +164,19 @@ def test_ring_step_shapes(n, count, dtype, add_shape, copy_shape):
         assert (gx, gy, block, vec) == (CUS * per_cu // n, n, want_block, want_vec), kind
 
 
-def test_ring_reduce_scatter_adds_with_a_scalar_operation_keep_256_lanes():
+def test_ring_reduce_scatter_adds_on_other_offsets_run_one_wave():
     """5 x 819 MiB bf16 reduce-scatter: chunk offsets of 171,756,748 bytes put
-    chunks 1-3 of the inputs on other 16-byte offsets than the outputs, so
-    those operations run scalar and the adds keep 256-lane workgroups; a count
-    whose chunks are whole vectors takes the one-wave adds."""
+    chunks 1-3 of the inputs on other offsets than the outputs.  Those
+    operations still move 16-byte vectors (unaligned loads), so their adds take
+    the same one-wave shape as a count whose chunks are whole vectors."""
     n = 5
     send, recv = wide(n)
-    for count, block in ((5 * 85878374, 256), (5 * 85878368, 64)):
+    for count in (5 * 85878374, 5 * 85878368):
         ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_RING)
         got = launches(ops)
         assert len(got) == n - 1
         for kind, gx, gy, b, vec in got:
-            assert (kind, b, vec) == ("add", block, 1)
-            assert gx == CUS * (8 if block == 64 else 4) // n
+            assert (kind, gx, gy, b, vec) == ("add", CUS * 8 // n, n, 64, 1)
 
 
 def test_halving_doubling_steps_take_the_step_shapes():
@@ -237,19 +236,45 @@ def test_fused_reduce_scatter_flat_shape(n):
             assert launches(ops) == [(kind, CUS * bpc, 1, 64, 1)]
 
 
-def test_fused_reduce_scatter_keeps_the_chunk_grid_when_chunks_cannot_vectorize():
-    """Chunk offsets that leave inputs and outputs on different 16-byte
-    offsets, split dimensions, and calls below 64 MiB moved keep one grid row
-    per chunk with 256-lane workgroups."""
+def test_ragged_flat_reduce_scatter_takes_the_flat_walk():
+    """Chunk bytes that are not a multiple of 16 put the inputs' chunks on
+    other offsets than the outputs; the chunks still vectorize, so the flat
+    one-wave walk serves them like whole-vector chunks."""
     n = 8
     send, recv = wide(n)
-    ragged = 268435456 + n * 3 + 5  # chunk bytes not a multiple of 16
-    ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, ragged, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
-    (kind, gx, gy, block, vec), = launches(ops)
-    assert (kind, gy, block) == ("fused_reduce_scatter", n, 256)
-    ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, ragged, 1, vrc.VRC_BF16, vrc.VRC_RING_ORDER)
-    assert launches(ops)[0][0] == "ring_order_reduce_scatter" and launches(ops)[0][2:4] == (n, 256)
+    ragged = 268435456 + n * 3 + 5
+    for mode, kind, per_cu in ((vrc.VRC_FUSED, "fused_reduce_scatter", 4),
+                               (vrc.VRC_RING_ORDER, "ring_order_reduce_scatter", 4),
+                               (vrc.VRC_RING_CHAINED, "chain_reduce_scatter", 16),
+                               (vrc.VRC_HD_ORDER, "butterfly_reduce_scatter", 4)):
+        ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, ragged, 1, vrc.VRC_BF16, mode)
+        assert launches(ops) == [(kind, CUS * per_cu, 1, 64, 1)]
+
+
+def test_split_dimension_and_small_reduce_scatters_keep_the_chunk_grid():
+    """Split dimensions and calls below 64 MiB moved keep one grid row per
+    chunk with 256-lane workgroups."""
+    n = 8
+    send, recv = wide(n)
     ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, 268435456, 8, vrc.VRC_BF16, vrc.VRC_FUSED)
     assert launches(ops)[0][2:4] == (n, 256)
     ops, _ = vrc.plan(vrc.COLL_REDUCE_SCATTER, send, recv, 1 << 20, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
     assert launches(ops)[0][2:4] == (n, 256)
+
+
+@pytest.mark.parametrize("mode", sorted(vrc.MODES))
+def test_mixed_offsets_keep_the_full_grid(mode):
+    """8 x 512 MiB bf16 all-reduce with rank r's input and output 2r bytes
+    past a 256-byte boundary: every mode plans the launches of the aligned
+    call, each with at least one workgroup per CU (a region off its
+    destination's grid still runs 16-byte vectors)."""
+    n, count = 8, 268435456
+    send, recv = wide(n)
+    mixed_send = [a + 2 * r for r, a in enumerate(send)]
+    mixed_recv = [a + 2 * r for r, a in enumerate(recv)]
+    aligned, nl = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, vrc.VRC_BF16, vrc.MODES[mode])
+    mixed, nl2 = vrc.plan(vrc.COLL_ALLREDUCE, mixed_send, mixed_recv, count, 1, vrc.VRC_BF16, vrc.MODES[mode])
+    assert nl2 == nl
+    assert launches(mixed) == launches(aligned)
+    for kind, gx, gy, block, vec in launches(mixed):
+        assert gx * gy * block >= CUS * 64, kind
