@@ -28,7 +28,7 @@ DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
 NP_DTYPES = {"int32": np.int32, "fp32": np.float32, "fp16": np.float16, "bf16": np.uint16}
 
 OK, E_ARG, E_NOMEM, E_EMPTY, E_TAG, E_LEFTOVER = range(6)
-PHASE_RS, PHASE_AG, PHASE_HD_RS, PHASE_HD_AG = 0, 1, 2, 3
+PHASE_RS, PHASE_AG, PHASE_HD_RS, PHASE_HD_AG, PHASE_TREE_GATHER, PHASE_TREE_BCAST = 0, 1, 2, 3, 4, 5
 FAULT_NONE, FAULT_DROP, FAULT_DUP, FAULT_MISROUTE, FAULT_WRONG_CHUNK = range(5)
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra"]
@@ -106,6 +106,7 @@ class Oracle:
         L.orc_hd_reduce_scatter.argtypes = [i, i, u64, u64, vp, vp, C.POINTER(_Trace), C.POINTER(_Fault)]
         L.orc_hd_all_gather.argtypes = [i, i, u64, u64, vp, vp, C.POINTER(_Trace), C.POINTER(_Fault)]
         L.orc_hd_allreduce_at.argtypes = [i, i, u64, vp, vp, u64, vp]
+        L.orc_tree_all_gather.argtypes = [i, i, u64, u64, vp, vp, C.POINTER(_Trace), C.POINTER(_Fault)]
         L.orc_fused_allreduce.argtypes = [i, i, u64, vp, vp]
         L.orc_fused_reduce_scatter.argtypes = [i, i, u64, u64, vp, vp]
         L.orc_ring_allreduce_at.argtypes = [i, i, u64, vp, vp, u64, vp]
@@ -237,6 +238,22 @@ class Oracle:
                                        C.byref(tr) if trace else None, self._fault(fault))
         if rc:
             raise OracleError("hd_all_gather", rc)
+        return (ys, self._read_trace(tr, keep, n)) if trace else ys
+
+    # -- binomial tree ---------------------------------------------------------
+    def tree_all_gather(self, xs, dtype, outer=1, trace=False, fault=None):
+        """Binomial-tree all-gather: gather to rank 0, then broadcast from it
+        (2 ceil(log2 N) steps, any N)."""
+        xs = self._check_inputs(xs, dtype)
+        n, count = len(xs), xs[0].size
+        ys = [np.empty(n * count, dtype=xs[0].dtype) for _ in range(n)]
+        tr = keep = None
+        if trace:
+            tr, keep = self._make_trace(n, 2 * n + 8)
+        rc = self._L.orc_tree_all_gather(DTYPES[dtype], n, count, outer, _ptrs(xs), _ptrs(ys),
+                                         C.byref(tr) if trace else None, self._fault(fault))
+        if rc:
+            raise OracleError("tree_all_gather", rc)
         return (ys, self._read_trace(tr, keep, n)) if trace else ys
 
     def hd_allreduce_at(self, xs, dtype, idx):

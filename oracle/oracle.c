@@ -39,6 +39,18 @@
  *         keeps the half of its current block range that holds block r and
  *         adds the partner's copy of that half; the all-gather then doubles
  *         the owned range with distances 1, 2, ..., N/2.
+
+ *  [TREE] ai6s.net/6a102b5410ee7a33f2746c06.html, sections "分布式推理中的通信"
+ *         and "hcomm 在推理场景中的使用": the all-gather comes in a ring form
+ *         and a tree form, chosen by data size.  The tree is not defined
+ *         there; the oracle takes the textbook binomial tree (Thakur,
+ *         Rabenseifner and Gropp 2005, binomial gather and binomial
+ *         broadcast; all-gather = gather to rank 0, then broadcast from it):
+ *         gather with distances d = 1, 2, 4, ... (< N), rank r with
+ *         r mod 2d == d sending the slabs it holds, [r, min(r+d, N)), to rank
+ *         r - d; then broadcast with the same distances in reverse order,
+ *         rank r with r mod 2d == 0 sending all N slabs to rank r + d
+ *         (if r + d < N).  2*ceil(log2 N) steps for any N.
  *
  * Readings taken where the pages are silent or garbled:
  *  - The listing adds into the chunk it sends; the walkthrough says a card
@@ -74,7 +86,14 @@ enum {
     ORC_E_LEFTOVER = 5  /* messages left undelivered at the end */
 };
 
-enum { ORC_PHASE_RS = 0, ORC_PHASE_AG = 1, ORC_PHASE_HD_RS = 2, ORC_PHASE_HD_AG = 3 };
+enum {
+    ORC_PHASE_RS = 0,
+    ORC_PHASE_AG = 1,
+    ORC_PHASE_HD_RS = 2,
+    ORC_PHASE_HD_AG = 3,
+    ORC_PHASE_TREE_GATHER = 4,
+    ORC_PHASE_TREE_BCAST = 5
+};
 
 /* Test hook: plant one fault into the simulated transport. */
 enum {
@@ -1118,6 +1137,120 @@ int orc_hd_all_gather(int dt, int n, uint64_t count, uint64_t outer, const void*
         return ORC_E_NOMEM;
     }
     rc = phase_doubling(nt, buf, &g, lo, hi, log2i(n), 1);
+    if (!rc) rc = drain_check(nt);
+    if (!rc)
+        for (int r = 0; r < n; r++) memcpy(y[r], buf[r], out_elems * esz);
+    net_free(nt);
+    rank_state_free(buf, n);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Binomial-tree all-gather [TREE]                                     */
+/* ------------------------------------------------------------------ */
+
+/* Gather to rank 0.  hi[r]: rank r holds slabs [r, hi[r]) (its own slab to
+ * begin with).  At the step with distance d (1, 2, 4, ... while d < N) rank
+ * r with r mod 2d == d sends [r, hi[r]) to rank r - d, which copies the
+ * slabs into its buffer; ranks r with r mod 2d == 0 and r + d < N receive.
+ * After ceil(log2 N) steps rank 0 holds all N slabs. */
+static int phase_tree_gather(net* nt, unsigned char** buf, const geom* g, int* hi)
+{
+    int n = nt->n, step = 0;
+    for (int d = 1; d < n; d *= 2, step++) {
+        for (int r = 0; r < n; r++) {
+            if (r % (2 * d) != d) continue;
+            int lo = r, top = hi[r];
+            const orc_fault* f = nt->fault;
+            if (f && f->kind == ORC_FAULT_WRONG_CHUNK && f->phase == ORC_PHASE_TREE_GATHER && f->step == step &&
+                f->rank == r) {
+                lo -= d; /* the receiver's own slabs instead */
+                top -= d;
+            }
+            msg* m = range_msg(nt, r, ORC_PHASE_TREE_GATHER, step, lo, top, buf[r], g, 1);
+            if (!m) return ORC_E_NOMEM;
+            int rc = post_to(nt, m, r - d);
+            if (rc) return rc;
+        }
+        for (int r = 0; r < n; r++) {
+            if (r % (2 * d) != 0 || r + d >= n) continue;
+            int p = r + d;
+            msg* m;
+            int rc = receive_range(nt, r, p, ORC_PHASE_TREE_GATHER, step, p, hi[p], &m);
+            if (rc) return rc;
+            for (uint64_t k = 0; k < m->elems; k++)
+                memcpy(buf[r] + slab_range_elem(g, p, hi[p], k) * nt->esz, m->payload + k * nt->esz, nt->esz);
+            msg_free(m);
+            hi[r] = hi[p];
+        }
+    }
+    return ORC_OK;
+}
+
+/* Broadcast from rank 0 along the same tree in reverse: at the step with
+ * distance d (the largest power of two below N, then d/2, ..., 1) rank r
+ * with r mod 2d == 0 and r + d < N sends all N slabs to rank r + d, which
+ * copies them into its buffer. */
+static int phase_tree_bcast(net* nt, unsigned char** buf, const geom* g)
+{
+    int n = nt->n, step = 0, top = 1;
+    while (2 * top < n) top *= 2;
+    for (int d = top; n > 1 && d >= 1; d /= 2, step++) {
+        for (int r = 0; r < n; r++) {
+            if (r % (2 * d) != 0 || r + d >= n) continue;
+            int top_slab = n;
+            const orc_fault* f = nt->fault;
+            if (f && f->kind == ORC_FAULT_WRONG_CHUNK && f->phase == ORC_PHASE_TREE_BCAST && f->step == step &&
+                f->rank == r)
+                top_slab = n - 1; /* all but the last slab */
+            msg* m = range_msg(nt, r, ORC_PHASE_TREE_BCAST, step, 0, top_slab, buf[r], g, 1);
+            if (!m) return ORC_E_NOMEM;
+            int rc = post_to(nt, m, r + d);
+            if (rc) return rc;
+        }
+        for (int r = 0; r < n; r++) {
+            if (r % (2 * d) != d) continue;
+            msg* m;
+            int rc = receive_range(nt, r, r - d, ORC_PHASE_TREE_BCAST, step, 0, n, &m);
+            if (rc) return rc;
+            for (uint64_t k = 0; k < m->elems; k++)
+                memcpy(buf[r] + slab_range_elem(g, 0, n, k) * nt->esz, m->payload + k * nt->esz, nt->esz);
+            msg_free(m);
+        }
+    }
+    return ORC_OK;
+}
+
+/* Tree all-gather over the slabs of [outer, N*row] outputs: every rank
+ * starts with its own slab, the gather collects all slabs at rank 0, the
+ * broadcast hands rank 0's buffer to every rank.  Any N from 1 to 64. */
+int orc_tree_all_gather(int dt, int n, uint64_t count, uint64_t outer, const void* const* x, void* const* y,
+                        orc_trace* trace, const orc_fault* fault)
+{
+    int rc = check_dtype_n(dt, n);
+    if (rc) return rc;
+    if (n > 64) return ORC_E_ARG;
+    if (outer == 0 || count % outer != 0) return ORC_E_ARG;
+    geom g = {count, outer, count / outer, n};
+    size_t esz = elem_size(dt);
+    uint64_t out_elems = count * (uint64_t)n;
+    unsigned char** buf = rank_state_new(n, out_elems, esz);
+    if (!buf) return ORC_E_NOMEM;
+    int hi[64];
+    for (int r = 0; r < n; r++) {
+        memset(buf[r], 0, out_elems * esz);
+        for (uint64_t k = 0; k < count; k++)
+            memcpy(buf[r] + slab_range_elem(&g, r, r + 1, k) * esz, (const unsigned char*)x[r] + k * esz, esz);
+        hi[r] = r + 1;
+    }
+    net* nt = net_new(dt, n, trace, fault);
+    if (!nt) {
+        rank_state_free(buf, n);
+        return ORC_E_NOMEM;
+    }
+    rc = phase_tree_gather(nt, buf, &g, hi);
+    if (!rc && hi[0] != n) rc = ORC_E_TAG;
+    if (!rc) rc = phase_tree_bcast(nt, buf, &g);
     if (!rc) rc = drain_check(nt);
     if (!rc)
         for (int r = 0; r < n; r++) memcpy(y[r], buf[r], out_elems * esz);

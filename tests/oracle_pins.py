@@ -13,7 +13,9 @@ AssertionError (or an oracle error) when the oracle disagrees with:
   independent relay simulation in ``brute_ring``;
 * the IEEE 754 format definitions (exhaustive fp16/bf16 decode checks);
 * the standard error bound of recursive summation (Higham, Accuracy and
-  Stability of Numerical Algorithms, 2nd ed., eq. 4.4).
+  Stability of Numerical Algorithms, 2nd ed., eq. 4.4);
+* for halving-doubling and the binomial-tree all-gather, hand-derived
+  schedules of their textbook forms (Thakur, Rabenseifner and Gropp 2005).
 
 The same functions run against deliberately broken builds of the oracle in
 ``test_oracle_mutants.py``, to show that each plausible mistake is caught.
@@ -642,6 +644,79 @@ def pin_hd_rejects_non_power_of_two_and_detects_faults(orc):
                     assert e.code in (orc_mod.E_EMPTY, orc_mod.E_TAG, orc_mod.E_LEFTOVER), e
                 else:
                     raise AssertionError(f"hd fault {kind} phase {phase} step {step} not detected")
+
+
+# ---------------------------------------------------------------------------
+# binomial-tree all-gather (gather to rank 0, then broadcast from it), pinned
+# by hand-derived N = 4 and N = 5 schedules, concatenation (the all-gather's
+# result is unique), message and step counts, the traffic each slab's path
+# through the tree fixes, and fault detection
+# ---------------------------------------------------------------------------
+def _tree_golden(name):
+    want = []
+    for row in _read_rows(name):
+        ph, s, src, dst, lo, hi = row.split()
+        phase = orc_mod.PHASE_TREE_GATHER if ph == "gather" else orc_mod.PHASE_TREE_BCAST
+        want.append((phase, int(s), int(src), int(dst), int(lo), int(hi)))
+    return want
+
+
+def pin_tree_schedule_golden(orc):
+    for n, name in ((4, "tree_n4_schedule.txt"), (5, "tree_n5_schedule.txt")):
+        xs = [np.arange(6, dtype=np.int32) + 100 * r for r in range(n)]
+        _, tr = orc.tree_all_gather(xs, "int32", trace=True)
+        got = [(m[0], m[1], m[2], m[3], m[4], m[6]) for m in tr.messages]
+        assert sorted(got) == sorted(_tree_golden(name)), f"tree schedule n={n} differs:\n{got}"
+
+
+def pin_tree_all_gather_is_concatenation(orc):
+    rng = np.random.default_rng(41)
+    for dtype in DTYPES:
+        for n, outer, row in ((1, 1, 5), (2, 1, 7), (3, 2, 5), (4, 3, 5), (5, 1, 9), (6, 2, 4), (7, 1, 3),
+                              (8, 2, 16), (12, 1, 3), (16, 1, 3)):
+            xs = _ranks(rng, dtype, n, outer * row)
+            want = np.concatenate([x.reshape(outer, row) for x in xs], axis=1).reshape(-1)
+            for r, y in enumerate(orc.tree_all_gather(xs, dtype, outer=outer)):
+                _same_bits(y, want, f"tree ag {dtype} n={n} outer={outer} rank {r}")
+
+
+def pin_tree_traffic_and_steps(orc):
+    """Every rank but 0 sends once in the gather and receives once in the
+    broadcast; each phase takes ceil(log2 N) steps; slab j reaches rank 0 in
+    one hop per set bit of j (a hop clears the lowest one), so the gather
+    carries sum_j popcount(j) slabs, and the broadcast N slabs to each of the
+    N - 1 other ranks."""
+    for n in range(1, 17):
+        outer, row = 2, 3
+        xs = [np.arange(outer * row, dtype=np.int32) + 10 * r for r in range(n)]
+        _, tr = orc.tree_all_gather(xs, "int32", outer=outer, trace=True)
+        slab = outer * row
+        gather = [m for m in tr.messages if m[0] == orc_mod.PHASE_TREE_GATHER]
+        bcast = [m for m in tr.messages if m[0] == orc_mod.PHASE_TREE_BCAST]
+        assert len(gather) == n - 1 and len(bcast) == n - 1, n
+        assert sorted(m[2] for m in gather) == list(range(1, n)), n
+        assert sorted(m[3] for m in bcast) == list(range(1, n)), n
+        k = (n - 1).bit_length()
+        assert {m[1] for m in gather} == set(range(k)) and {m[1] for m in bcast} == set(range(k)), n
+        assert sum(m[5] for m in gather) == slab * sum(bin(j).count("1") for j in range(n)), n
+        assert sum(m[5] for m in bcast) == slab * n * (n - 1), n
+        assert tr.recv_elems[0] == slab * (n - 1), n
+
+
+def pin_tree_detects_faults(orc):
+    rng = np.random.default_rng(42)
+    for n, cases in ((8, ((orc_mod.PHASE_TREE_GATHER, 0, 5), (orc_mod.PHASE_TREE_GATHER, 2, 4),
+                          (orc_mod.PHASE_TREE_BCAST, 0, 0), (orc_mod.PHASE_TREE_BCAST, 2, 6))),
+                     (5, ((orc_mod.PHASE_TREE_GATHER, 2, 4), (orc_mod.PHASE_TREE_BCAST, 2, 2)))):
+        xs = _ranks(rng, "fp32", n, 6)
+        for kind in (orc_mod.FAULT_DROP, orc_mod.FAULT_DUP, orc_mod.FAULT_MISROUTE, orc_mod.FAULT_WRONG_CHUNK):
+            for phase, step, rank in cases:
+                try:
+                    orc.tree_all_gather(xs, "fp32", fault=orc_mod.Fault(kind, phase, step, rank=rank))
+                except orc_mod.OracleError as e:
+                    assert e.code in (orc_mod.E_EMPTY, orc_mod.E_TAG, orc_mod.E_LEFTOVER), e
+                else:
+                    raise AssertionError(f"tree fault {kind} phase {phase} step {step} rank {rank} not detected")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -68,6 +68,18 @@ MUTANTS = [
      "memcpy(mine, m->payload + k * nt->esz, nt->esz);"),
     ("hd_range_drops_remainder", "for (int b = lo; b < hi; b++) total += chunk_len(g, b);",
      "for (int b = lo; b < hi; b++) total += g->count / (uint64_t)g->n;"),
+    # binomial-tree all-gather
+    ("tree_gather_sends_own_slab_only", "int lo = r, top = hi[r];", "int lo = r, top = r + 1;"),
+    ("tree_gather_stops_at_floor_log2", "for (int d = 1; d < n; d *= 2, step++) {\n        for (int r = 0; r < n; r++) {\n"
+     "            if (r % (2 * d) != d) continue;",
+     "for (int d = 1; 2 * d <= n; d *= 2, step++) {\n        for (int r = 0; r < n; r++) {\n"
+     "            if (r % (2 * d) != d) continue;"),
+    ("tree_gather_lands_on_own_slab",
+     "memcpy(buf[r] + slab_range_elem(g, p, hi[p], k) * nt->esz, m->payload + k * nt->esz, nt->esz);",
+     "memcpy(buf[r] + slab_range_elem(g, r, r + hi[p] - p, k) * nt->esz, m->payload + k * nt->esz, nt->esz);"),
+    ("tree_bcast_skips_distance_one", "for (int d = top; n > 1 && d >= 1; d /= 2, step++) {",
+     "for (int d = top; n > 1 && d >= 2; d /= 2, step++) {"),
+    ("tree_bcast_top_rounds_up", "while (2 * top < n) top *= 2;", "while (top < n) top *= 2;"),
 ]
 
 
