@@ -18,7 +18,7 @@ same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--mode fused|ring|ring_chained|ring_order|hd|hd_order|select]
-       python bench.py --suite | --offsets | --overlap | --probe-copy
+       python bench.py --suite | --offsets | --ag-sweep | --overlap | --probe-copy
 """
 from __future__ import annotations
 
@@ -149,9 +149,18 @@ def selected(mode: str, n: int, size: int) -> str:
     return "hd" if n & (n - 1) == 0 and size <= (64 << 20) else "ring"
 
 
+def tree_slab_copies(n: int) -> int:
+    """Slab copies of the binomial-tree all-gather: every receiving rank's own
+    slab at the first gather step (ceil(N/2)), slab j once per set bit of j on
+    its way to rank 0, and all N slabs to each of the N - 1 other ranks."""
+    return (n + 1) // 2 + sum(bin(j).count("1") for j in range(n)) + n * (n - 1)
+
+
 def suite_bytes(w, mode: str) -> int:
     """Algorithmic bytes per call for a workload's collective and mode."""
     n, size = w.n, w.count * w.esize
+    if mode == "tree":
+        return 2 * tree_slab_copies(n) * size
     mode = selected(mode, n, size)
     fused_like = mode in ("fused", "ring_order", "hd_order")
     if w.collective == "reduce_scatter" and mode == "hd":
@@ -191,7 +200,7 @@ def run_suite(steps: int, torch, vrc, workloads) -> int:
         footprint = {"allreduce": 2 * w.n * size, "reduce_scatter": (w.n + 1) * size,
                      "all_gather": (w.n + w.n * w.n) * size}[w.collective]
         cached = footprint <= (512 << 20)
-        for mode in vrc.MODES:
+        for mode in (vrc.MODES if w.collective == "all_gather" else vrc.REDUCE_MODES):
             def call():
                 if w.collective == "allreduce":
                     vrc.vrc_allreduce(xs, recv=outs, mode=mode)
@@ -300,7 +309,7 @@ def run_offsets(steps: int, torch, vrc, workloads) -> int:
     ys = [torch.empty_like(x) for x in xs]
     mx = offset_views(torch, xs, list(range(w.n)))
     my = offset_views(torch, ys, [3 * r % 8 for r in range(w.n)])
-    for mode in vrc.MODES:
+    for mode in vrc.REDUCE_MODES:
         t = interleaved_us(torch, {
             "aligned": lambda: vrc.vrc_allreduce(xs, recv=ys, mode=mode),
             "offset": lambda: vrc.vrc_allreduce(mx, recv=my, mode=mode)}, steps)
@@ -330,6 +339,51 @@ def run_offsets(steps: int, torch, vrc, workloads) -> int:
                "offset_over_aligned": round(o_ns / a_ns, 4)}
         print(json.dumps(rec), flush=True)
         log(f"offsets RS {mode:13s} aligned {t['aligned']:9.1f} us  ragged {t['offset']:9.1f} us  x{o_ns / a_ns:.3f}")
+    return 0
+
+
+def run_ag_sweep(steps: int, torch, vrc, workloads) -> int:
+    """The all-gather algorithms side by side: ring relay, recursive doubling
+    (halving-doubling's all-gather, powers of two only), binomial tree and the
+    fused broadcast, for several rank counts and per-rank sizes (fp16, flat),
+    interleaved in one process; a 1 GiB write before each call evicts the
+    Infinity Cache for calls whose buffers fit in it.  One JSON line per
+    (ranks, size)."""
+    dev = "cuda:0"
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for n in (4, 6, 8, 12, 16):
+        for per_rank in (4 << 10, 64 << 10, 1 << 20, 8 << 20, 32 << 20, 128 << 20):
+            if n * n * per_rank > (8 << 30):
+                continue
+            count = per_rank // 2
+            xs = workloads.random_ranks(n, count, "fp16", seed=90 + n, device=dev)
+            ys = vrc.vrc_all_gather(xs)
+            modes = ["ring", "tree", "fused", "select"] + (["hd"] if n & (n - 1) == 0 else [])
+            cached = (n + n * n) * per_rank <= (512 << 20)
+            ms = {m: [] for m in modes}
+            for m in modes:
+                vrc.vrc_all_gather(xs, recv=ys, mode=m)
+            torch.cuda.synchronize()
+            for _ in range(4):
+                for m in modes:
+                    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                           for _ in range(max(1, steps // 4))]
+                    for e0, e1 in evs:
+                        if cached:
+                            flush.zero_()
+                        e0.record()
+                        vrc.vrc_all_gather(xs, recv=ys, mode=m)
+                        e1.record()
+                    torch.cuda.synchronize()
+                    ms[m].extend(e0.elapsed_time(e1) for e0, e1 in evs)
+            us = {m: round(sorted(v)[len(v) // 2] * 1e3, 2) for m, v in ms.items()}
+            rec = {"ag_sweep": {"n_ranks": n, "bytes_per_rank": per_rank, "us_median": us,
+                                "label": "effective" if cached else "hbm"}}
+            print(json.dumps(rec), flush=True)
+            log(f"all-gather n={n:2d} {per_rank >> 10:7d} KiB/rank: " +
+                "  ".join(f"{m} {t:9.1f}" for m, t in us.items()))
+            del xs, ys
+            torch.cuda.empty_cache()
     return 0
 
 
@@ -411,6 +465,8 @@ def main() -> int:
                     help="measure every workload in every mode (one JSON line each) instead of the headline")
     ap.add_argument("--offsets", action="store_true",
                     help="time operands off their destination's grid beside their aligned twins")
+    ap.add_argument("--ag-sweep", action="store_true",
+                    help="time the all-gather algorithms (ring, recursive doubling, tree, fused) by size")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB (known HBM traffic: 1 GiB read, 1 GiB "
                          "written per launch), for calibrating rocprofv3 byte counters")
@@ -434,6 +490,8 @@ def main() -> int:
         return run_suite(args.steps, torch, vrc, workloads)
     if args.offsets:
         return run_offsets(args.steps, torch, vrc, workloads)
+    if args.ag_sweep:
+        return run_ag_sweep(args.steps, torch, vrc, workloads)
     if args.overlap:
         return run_overlap(args.steps, args.mode, torch, vrc, workloads)
     if args.probe_copy:
@@ -477,7 +535,7 @@ def main() -> int:
              "alg_bytes_per_step": nbytes, "kernel_source_sha256_16": kernel_source_hash(),
              "inputs": {"seed": w.seed, "sha256_16_of_first_bytes": fp_bytes, "per_rank": fingerprints}}
     if not args.no_extra:
-        for other in vrc.MODES:
+        for other in vrc.REDUCE_MODES:
             if other == args.mode:
                 continue
 

@@ -32,6 +32,9 @@
  *           AllGather(send_buf, recv_buf, count, comm).
  *   [OVERLAP] www.bjdmk.com.cn/news/5966809/, section 4 (compute/comm
  *           overlap): collectives are enqueued on a stream.
+ *   [TREE]  ai6s.net/6a102b5410ee7a33f2746c06.html, "分布式推理中的通信":
+ *           the all-gather has a ring form and a tree form, chosen by data
+ *           size (the tree itself is not defined there).
  *
  * Chunking.  A buffer of `count` elements has chunks c = 0..N-1: with
  * base = count / N, chunk c is [c*base, (c+1)*base) for c < N-1 and the last
@@ -61,9 +64,13 @@
  *               Work is enqueued asynchronously; the call returns before it
  *               finishes.  Errors raised by running kernels surface at the
  *               caller's next synchronisation, not here.
- *   Alignment   Any element-aligned pointer works.  16-byte vector loads and
- *               stores are used where every operand of a chunk shares the
- *               same address offset modulo 16; otherwise a scalar path runs.
+ *   Alignment   Any element-aligned pointer works, and every operand moves
+ *               in 16-byte vectors whatever its offset.  A region's vectors
+ *               start where its destination crosses a 128-byte boundary (the
+ *               elements before it and the last partial vector run scalar);
+ *               operands on other offsets cost some bandwidth (about 8 % for
+ *               inputs; outputs on differing offsets, up to about 30 % for the
+ *               single-launch all-reduce modes).
  *   Errors      Argument errors return before anything is enqueued.
  *   Threads     Calls are re-entrant and thread-safe; calls that overlap on
  *               the same buffers race like any two kernels would.
@@ -81,7 +88,7 @@
 extern "C" {
 #endif
 
-#define VRC_VERSION 101 /* 1.0.1: vrc_op_desc reports the launch geometry */
+#define VRC_VERSION 102 /* 1.0.2: VRC_TREE all-gather */
 #define VRC_MAX_RANKS 16
 
 struct ihipStream_t;
@@ -134,6 +141,17 @@ typedef enum { VRC_SUM = 0 } vrc_op_t;
  *                     halving-doubling's log2 N steps on MI355X (8 ranks:
  *                     halving-doubling 8 % faster at 16 MiB, the ring 3 %
  *                     faster at 128 MiB per rank). */
+/* Binomial tree [TREE], all-gather only (vrc_allreduce and
+ * vrc_reduce_scatter return VRC_ERR_UNSUPPORTED for it): the textbook
+ * binomial gather to rank 0 followed by the binomial broadcast from rank 0
+ * (Thakur, Rabenseifner and Gropp, "Optimization of Collective Communication
+ * Operations in MPICH", IJHPCA 2005).  Gather step with distance d = 1, 2,
+ * 4, ... (< nranks): rank r with r mod 2d == d hands the slabs it holds,
+ * [r, min(r+d, nranks)), to rank r-d.  Broadcast steps with the distances in
+ * reverse: rank r with r mod 2d == 0 copies its whole output to rank r+d.
+ *   VRC_TREE          one launch per step: 2 ceil(log2 nranks) launches, any
+ *                     nranks.  The bytes are the concatenation, as in every
+ *                     all-gather mode. */
 #define VRC_SELECT_HD_MAX_BYTES (64ull << 20)
 typedef enum {
     VRC_RING = 0,
@@ -142,7 +160,8 @@ typedef enum {
     VRC_RING_ORDER = 3,
     VRC_HD = 4,
     VRC_HD_ORDER = 5,
-    VRC_SELECT = 6
+    VRC_SELECT = 6,
+    VRC_TREE = 7
 } vrc_mode_t;
 
 typedef enum {
@@ -196,6 +215,8 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
  *   VRC_RING relays slabs around the ring (nranks-1 launches: rank r copies
  *   slab (r-1-s) from rank r-1 at step s, and its own slab in step 0).
  *   VRC_FUSED reads each input once and writes it to all outputs.
+ *   VRC_TREE gathers the slabs to rank 0 and broadcasts them along a
+ *   binomial tree (2 ceil(log2 nranks) launches).
  *   recv buffers must not overlap each other or any send buffer.
  */
 vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nranks, size_t count,

@@ -17,7 +17,9 @@ and per all-gather step), ``"fused"`` the single-launch N-way kernel,
 one launch per step and ``"hd_order"`` halving-doubling in one launch (both
 need a power-of-two rank count and return the same bits); ``"select"`` picks
 ``"hd"`` for power-of-two rank counts with at most 64 MiB per rank and
-``"ring"`` otherwise, and returns the bits of the one it picks.
+``"ring"`` otherwise, and returns the bits of the one it picks.  ``"tree"``
+is the binomial-tree all-gather (gather to rank 0, broadcast from it; the
+all-gather only).
 """
 from __future__ import annotations
 
@@ -29,13 +31,15 @@ LIB_PATH = os.path.join(PKG, "libvrc.so")
 
 VRC_INT32, VRC_FP32, VRC_FP16, VRC_BF16 = 0, 1, 2, 3
 VRC_SUM = 0
-VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER, VRC_SELECT = 0, 1, 2, 3, 4, 5, 6
+VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER, VRC_SELECT, VRC_TREE = range(8)
 SELECT_HD_MAX_BYTES = 64 << 20  # VRC_SELECT_HD_MAX_BYTES of include/vrc.h
 VRC_OK, VRC_ERR_INVALID_ARG, VRC_ERR_UNSUPPORTED, VRC_ERR_ALIAS, VRC_ERR_HIP = range(5)
 MAX_RANKS = 16
 
 MODES = {"ring": VRC_RING, "fused": VRC_FUSED, "ring_chained": VRC_RING_CHAINED, "ring_order": VRC_RING_ORDER,
-         "hd": VRC_HD, "hd_order": VRC_HD_ORDER, "select": VRC_SELECT}
+         "hd": VRC_HD, "hd_order": VRC_HD_ORDER, "select": VRC_SELECT, "tree": VRC_TREE}
+GATHER_ONLY_MODES = ("tree",)  # the all-reduce and reduce-scatter return VRC_ERR_UNSUPPORTED for these
+REDUCE_MODES = {k: v for k, v in MODES.items() if k not in GATHER_ONLY_MODES}
 RING_MODES = ("ring", "ring_chained", "ring_order")  # same bits as the per-step ring
 HD_MODES = ("hd", "hd_order")  # halving-doubling; nranks must be a power of two
 
@@ -49,7 +53,7 @@ class VrcError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 101  # VRC_VERSION of include/vrc.h that these mirrors follow
+ABI_VERSION = 102  # VRC_VERSION of include/vrc.h that these mirrors follow
 
 
 class OpDesc(C.Structure):
@@ -344,6 +348,7 @@ __all__ = [
     "vrc_allreduce", "vrc_reduce_scatter", "vrc_all_gather", "reduce_scatter_shape", "chunk_range",
     "version", "raw_allreduce", "raw_reduce_scatter", "raw_all_gather", "lib", "VrcError",
     "VRC_INT32", "VRC_FP32", "VRC_FP16", "VRC_BF16", "VRC_SUM", "VRC_RING", "VRC_FUSED", "VRC_RING_CHAINED",
-    "VRC_RING_ORDER", "VRC_HD", "VRC_HD_ORDER", "MODES", "RING_MODES", "HD_MODES", "VRC_OK",
+    "VRC_RING_ORDER", "VRC_HD", "VRC_HD_ORDER", "VRC_SELECT", "VRC_TREE", "MODES", "REDUCE_MODES",
+    "GATHER_ONLY_MODES", "RING_MODES", "HD_MODES", "VRC_OK",
     "VRC_ERR_INVALID_ARG", "VRC_ERR_UNSUPPORTED", "VRC_ERR_ALIAS", "VRC_ERR_HIP", "MAX_RANKS",
 ]

@@ -125,7 +125,7 @@ vrc_status_t run(Coll coll, vrc_mode_t mode, vrc_dtype_t dt, const void* const* 
 bool mode_ok(vrc_mode_t m)
 {
     return m == VRC_RING || m == VRC_FUSED || m == VRC_RING_CHAINED || m == VRC_RING_ORDER || m == VRC_HD ||
-           m == VRC_HD_ORDER || m == VRC_SELECT;
+           m == VRC_HD_ORDER || m == VRC_SELECT || m == VRC_TREE;
 }
 
 // VRC_SELECT: halving-doubling for power-of-two rank counts and inputs of at
@@ -179,7 +179,7 @@ vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nrank
 {
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
-    if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
+    if (op != VRC_SUM || !mode_ok(mode) || mode == VRC_TREE) return VRC_ERR_UNSUPPORTED;
     const uint64_t bytes = (uint64_t)count * (uint64_t)esize(dtype);
     mode = resolve_mode(mode, nranks, bytes);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
@@ -197,7 +197,7 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
 {
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
-    if (op != VRC_SUM || !mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
+    if (op != VRC_SUM || !mode_ok(mode) || mode == VRC_TREE) return VRC_ERR_UNSUPPORTED;
     const int E = esize(dtype);
     mode = resolve_mode(mode, nranks, (uint64_t)count * E);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;

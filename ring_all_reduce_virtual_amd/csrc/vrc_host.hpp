@@ -99,7 +99,7 @@ inline const Tuning& tuning()
 {
     static const Tuning t = {env_int("VRC_FUSED_BLOCKS_PER_CU", 0, 1, 64),
                              env_int("VRC_STEP_BLOCKS_PER_CU", 0, 1, 64),
-                             env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 0, 1, 2),
+                             env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 0, 1, 8),
                              env_int("VRC_STEP_NT", -1, 0, 2), env_int("VRC_STEP_UNROLL", 0, 1, 2),
                              env_int("VRC_FUSED_BLOCK", 0, 64, 256), env_int("VRC_CHAIN_BLOCK", 0, 64, 256),
                              env_int("VRC_STEP_BLOCK", 0, 64, 256)};
@@ -125,37 +125,70 @@ inline int fused_blocks_per_cu(uint64_t bytes_moved, int n)
 // keeps in flight.
 //
 // From 64 MiB moved the kernel runs one-wave workgroups.  Workgroups are
-// handed to the 8 XCDs in turn, so consecutive 1 KiB tiles of every buffer
-// are served by different XCDs; with 256-lane workgroups each XCD owned 4 KiB
-// runs.  The grid keeps about 32 KiB of loads in flight per CU (workgroups per
-// CU x ranks x vectors per rank <= 32, at most 8 workgroups): more
-// outstanding requests made the mixed read/write stream slower, not faster.
-// Two vectors per rank at 3 and 4 ranks, one otherwise.  Measured on MI355X,
-// all shapes compared in one process on the same buffers (GB/s, old shape:
-// 256 lanes, two vectors, 1-2 per CU at these sizes -> this policy):
-//   8 x 512 MiB bf16 5,454 -> 5,648;  8 x 64 MiB 5,460 -> 5,902;
-//   16 x 256 MiB 5,025 -> 5,522;      4 x 128 MiB 5,428 -> 5,978;
-//   2 x 2 GiB 5,180 -> 5,576;         8 x 16 MiB (cache flushed) 4,505 -> 5,314.
+// handed to the 8 XCDs in turn, so consecutive wave tiles of every buffer go
+// to different XCDs.  A wave takes U consecutive 1 KiB tiles per iteration
+// (all U * N loads in flight, then the U folds and U * N stores back to
+// back).  The grid keeps 16-48 KiB of loads in flight per CU (workgroups per
+// CU x ranks x U): more outstanding requests made the mixed read/write stream
+// slower, not faster.  Shapes measured on MI355X, bf16, 8 GiB moved, all
+// shapes in one process on the same buffers, interleaved over four rounds,
+// three runs (time relative to the previous policy, U vectors one grid stride
+// apart at 3-4 ranks and U = 1 otherwise, at the largest power of two <= 8
+// per CU with workgroups x N x U <= 32):
+//   2 ranks: U 8, 2 per CU 0.91-0.92 (U 4 or 2 at 4 per CU 0.92-0.93);
+//   3 ranks: U 4, 2 per CU 0.97-0.98;   4 ranks: U 8, 1 per CU 0.92;
+//   5 ranks: U 2, 2 per CU 0.97-0.98;   8 ranks: U 1 at 2 or 4 per CU within
+//   2 % (4 kept), every U > 1 2-4 % slower;  12 and 16 ranks: U 1, 2 per CU
+//   (U 2 or 4 per CU 1-7 % slower at 16).
+// Outputs that do not all share the vector grid (write_ref) split a 64-byte
+// write block at each tile edge; with consecutive tiles a wave fills those
+// blocks itself, back to back, and the cache merges them.  Those calls take
+// the largest U <= 8 with U x N <= 32 at 64 / (U x N) per CU.  8 ranks with
+// inputs and outputs on offsets 2r bytes (ms; aligned U 1 at 4 per CU:
+// 1.532): rank fold U 4 at 2 per CU 1.781, U 2 at 2 per CU 1.798, U 4 at 1
+// per CU 1.814, U 1 at 4 per CU 2.017; the butterfly fold 1.770, 1.819, 2.743
+// and 2.021 (with one wave per CU it turns ALU-bound).
 // Below 64 MiB moved a call is launch-bound and keeps 256-lane workgroups,
-// 8 per CU, two vectors per rank.
+// 8 per CU, two vectors per rank one grid stride apart.
 struct FusedShape {
     int block;
     int blocks_per_cu;
     int unroll;
 };
 
-inline FusedShape fused_ar_shape(uint64_t bytes_moved, int n)
+inline FusedShape fused_ar_shape(uint64_t bytes_moved, int n, bool outputs_share_grid)
 {
     FusedShape s = {kBlock, 8, 2};
     if (bytes_moved >= 64 * kMiB) {
         s.block = 64;
-        s.unroll = (n == 3 || n == 4) ? 2 : 1;
-        s.blocks_per_cu = 8;
-        while (s.blocks_per_cu > 1 && s.blocks_per_cu * n * s.unroll > 32) s.blocks_per_cu /= 2;
+        if (!outputs_share_grid) {
+            s.unroll = 8;
+            while (s.unroll > 1 && s.unroll * n > 32) s.unroll /= 2;
+            s.blocks_per_cu = 1;
+            while (2 * s.blocks_per_cu * s.unroll * n <= 64) s.blocks_per_cu *= 2;
+        } else if (n == 2) {
+            s = {64, 2, 8};
+        } else if (n == 3) {
+            s = {64, 2, 4};
+        } else if (n == 4) {
+            s = {64, 1, 8};
+        } else if (n <= 7) {
+            s = {64, 2, 2};
+        } else if (n == 8) {
+            s = {64, 4, 1};
+        } else {
+            s = {64, 2, 1};
+        }
     }
     if (tuning().fused_blocks_per_cu) s.blocks_per_cu = tuning().fused_blocks_per_cu;
     if (tuning().fused_block) s.block = tuning().fused_block == 64 ? 64 : kBlock;
     if (tuning().unroll) s.unroll = tuning().unroll;
+    // One-wave kernels exist for U = 1, 2, 4 and 8 with U x N <= 32 (a lane's
+    // loads stay in registers); 256-lane ones for U = 1 and 2.
+    const int umax = s.block == 64 ? 8 : 2;
+    int u = 1;
+    while (2 * u <= s.unroll && 2 * u <= umax && (s.block != 64 || 2 * u * n <= 32)) u *= 2;
+    s.unroll = u;
     return s;
 }
 

@@ -151,10 +151,14 @@ __global__ __launch_bounds__(B) void k_ring_step(StepArgsK<K> args)
 // Fused all-reduce: every lane reads element block i of all N inputs, folds
 // them in rank order in the accumulator, rounds once and writes the result
 // to all N outputs.  Reads precede writes within a lane, so in-place calls
-// are safe.  U independent vectors per lane per iteration keep U*N 16-byte
-// loads in flight.  B lanes per workgroup: with B = 64 consecutive 1 KiB
-// wave tiles belong to consecutive workgroups, which the hardware hands to
-// different XCDs in turn.
+// are safe.  U vectors per lane per iteration keep U*N 16-byte loads in
+// flight.
+//  B = 64 (one-wave workgroups): a wave takes U consecutive 1 KiB tiles per
+//  iteration and stores them back to back, so a 64-byte write block that an
+//  output off the vector grid splits between two of its tiles is filled by
+//  one wave at once, and the cache merges it; workgroups go to the XCDs in
+//  turn, U KiB each.
+//  B = 256: the U vectors of a lane are one grid stride apart.
 // ---------------------------------------------------------------------------
 struct FusedArArgs {
     const char* src[kMaxRanks];
@@ -218,15 +222,11 @@ struct Butterfly {
     }
 };
 
-template <class T, int N, int U, bool NT, class Fold = RankFold, int B = kBlock>
-__global__ __launch_bounds__(B) void k_fused_allreduce(FusedArArgs a)
+// The fused all-reduce's vectors, U per lane one grid stride apart.
+template <class T, int N, int U, bool NT, class Fold>
+__device__ __forceinline__ void fused_strided(const FusedArArgs& a, uint64_t tid, uint64_t nthreads, uint64_t body,
+                                              uint64_t nv)
 {
-    const uint64_t tid = (uint64_t)blockIdx.x * B + threadIdx.x;
-    const uint64_t nthreads = (uint64_t)gridDim.x * B;
-    constexpr uint64_t E = T::ESZ;
-    const uint64_t body = a.g.head * E;
-    const uint64_t nv = a.g.nvb;
-
     uint64_t v = tid;
     if constexpr (U > 1) {
         for (; v + (U - 1) * nthreads < nv; v += U * nthreads) {
@@ -252,6 +252,53 @@ __global__ __launch_bounds__(B) void k_fused_allreduce(FusedArArgs a)
         const u32x4 s = Fold::template vec<T, N>(in);
 #pragma unroll
         for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, s);
+    }
+}
+
+template <class T, int N, int U, bool NT, class Fold = RankFold, int B = kBlock>
+__global__ __launch_bounds__(B) void k_fused_allreduce(FusedArArgs a)
+{
+    const uint64_t tid = (uint64_t)blockIdx.x * B + threadIdx.x;
+    const uint64_t nthreads = (uint64_t)gridDim.x * B;
+    constexpr uint64_t E = T::ESZ;
+    const uint64_t body = a.g.head * E;
+    const uint64_t nv = a.g.nvb;
+
+    if constexpr (B == 64) {
+        // Groups of U whole wave tiles, with no bounds test inside: across a
+        // branch the compiler cannot count the outstanding accesses, and it
+        // waits for every one of them (a tile's stores included) before the
+        // next tile's fold.  The tiles after the last whole group, the last one
+        // partial, go one per wave.
+        constexpr uint64_t W = 64;
+        const uint64_t lane = threadIdx.x;
+        const uint64_t groups = nv / W / U;
+        for (uint64_t g = blockIdx.x; g < groups; g += gridDim.x) {
+            const uint64_t v0 = g * U * W + lane;
+            u32x4 in[U][N];
+#pragma unroll
+            for (int u = 0; u < U; u++)
+#pragma unroll
+                for (int r = 0; r < N; r++) in[u][r] = ld16<NT>(a.src[r] + body + (v0 + u * W) * 16);
+            issue_loads_first();
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const u32x4 s = Fold::template vec<T, N>(in[u]);
+#pragma unroll
+                for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + (v0 + u * W) * 16, s);
+            }
+        }
+        for (uint64_t v = (groups * U + blockIdx.x) * W + lane; v < nv; v += (uint64_t)gridDim.x * W) {
+            u32x4 in[N];
+#pragma unroll
+            for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
+            issue_loads_first();
+            const u32x4 s = Fold::template vec<T, N>(in);
+#pragma unroll
+            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, s);
+        }
+    } else {
+        fused_strided<T, N, U, NT, Fold>(a, tid, nthreads, body, nv);
     }
 
     const uint64_t ns = a.g.head + a.g.tail;

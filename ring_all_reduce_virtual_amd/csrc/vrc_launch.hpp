@@ -234,8 +234,15 @@ struct Launch {
     template <int N, class Fold>
     static void launch_fused_ar_n(const vrc::FusedArArgs& a, dim3 grid, FusedShape sh, hipStream_t st)
     {
+        // One-wave workgroups take U consecutive tiles; U * N <= 32 (fused_ar_shape clamps it) keeps a
+        // lane's loads in registers, and no other U is instantiated.
+        constexpr int U8 = 8 * N <= 32 ? 8 : 1, U4 = 4 * N <= 32 ? 4 : 1;
         if (sh.block == 64) {
-            if (sh.unroll == 2)
+            if (sh.unroll == 8)
+                hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, U8, true, Fold, 64>), grid, dim3(64), 0, st, a);
+            else if (sh.unroll == 4)
+                hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, U4, true, Fold, 64>), grid, dim3(64), 0, st, a);
+            else if (sh.unroll == 2)
                 hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 2, true, Fold, 64>), grid, dim3(64), 0, st, a);
             else
                 hipLaunchKernelGGL((vrc::k_fused_allreduce<T, N, 1, true, Fold, 64>), grid, dim3(64), 0, st, a);
@@ -264,9 +271,13 @@ struct Launch {
             a.dst[r] = nullptr;
         }
         a.count = count;
-        a.g = split_rows(write_ref(out, n), count, E);
+        const uintptr_t ref = write_ref(out, n);
+        a.g = split_rows(ref, count, E);
+        bool share = true;  // every output on the vector grid
+        for (int r = 0; r < n; r++)
+            if (out[r] % kGridAlign != ref % kGridAlign) share = false;
         const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
-        const FusedShape sh = fused_ar_shape(2 * (uint64_t)n * count * E, n);
+        const FusedShape sh = fused_ar_shape(2 * (uint64_t)n * count * E, n, share);
         const dim3 grid(grid_x(cus, work, 1, sh.blocks_per_cu, sh.block));
         if (g_plan)
             return plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_ALLREDUCE
@@ -557,6 +568,54 @@ struct Launch {
         return VRC_OK;
     }
 
+    // ---- binomial-tree all-gather -----------------------------------------
+    // Gather to rank 0, then broadcast from it (the textbook binomial tree;
+    // Thakur, Rabenseifner and Gropp 2005).  Gather distance d = 1, 2, 4, ...
+    // (< N): rank r with r mod 2d == 0 copies the slabs rank r + d holds,
+    // [r + d, hi[r + d]), into the same columns of its output.  The d = 1
+    // launch also places every receiving rank's own slab and reads the
+    // sending ranks' slabs straight from their inputs.  Broadcast distances run
+    // in reverse: rank r with r mod 2d == 0 copies its whole output to rank
+    // r + d.  2 ceil(log2 N) launches; a launch writes only ranks that none of
+    // its operations reads.
+    static vrc_status_t tree_all_gather(const char* const* x, char* const* y, int n, uint64_t count,
+                                        uint64_t outer, int cus, hipStream_t st)
+    {
+        const uint64_t row = count / outer, sy = (uint64_t)n * row;
+        if (n == 1) return copy(x[0], y[0], 1, count, 0, 0, cus, st);
+        int hi[kMaxRanks];
+        for (int r = 0; r < n; r++) hi[r] = r + 1;
+        vrc::StepArgs args;
+        for (int d = 1; d < n; d *= 2) {
+            int nops = 0;
+            uint64_t work = 0;
+            for (int r = 0; r < n; r += 2 * d) {
+                if (d == 1) args.op[nops++] = make_op(x[r], nullptr, y[r] + (uint64_t)r * row * E, outer, row, row, 0, sy);
+                if (r + d < n) {
+                    const int p = r + d;
+                    const uint64_t off = (uint64_t)p * row * E, width = (uint64_t)(hi[p] - p) * row;
+                    args.op[nops++] = d == 1 ? make_op(x[p], nullptr, y[r] + off, outer, row, row, 0, sy)
+                                             : make_op(y[p] + off, nullptr, y[r] + off, outer, width, sy, 0, sy);
+                    hi[r] = hi[p];
+                }
+            }
+            for (int i = 0; i < nops; i++)
+                if (op_work(args.op[i]) > work) work = op_work(args.op[i]);
+            vrc_status_t rc = step<false>(args, nops, work, cus, st);
+            if (rc) return rc;
+        }
+        int top = 1;
+        while (2 * top < n) top *= 2;
+        for (int d = top; d >= 1; d /= 2) {
+            int nops = 0;
+            for (int r = 0; r + d < n; r += 2 * d)
+                args.op[nops++] = make_op(y[r], nullptr, y[r + d], 1, (uint64_t)n * count, 0, 0, 0);
+            vrc_status_t rc = step<false>(args, nops, op_work(args.op[0]), cus, st);
+            if (rc) return rc;
+        }
+        return VRC_OK;
+    }
+
     // ---- single-launch ring (chained per element) ------------------------
     template <bool MEM>
     static vrc_status_t chain_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
@@ -710,6 +769,7 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
             return n == 2 ? L::fused_allreduce(x, y, n, count, cus, st)
                           : L::template fused_allreduce<vrc::Butterfly>(x, y, n, count, cus, st);
         case VRC_SELECT: break;  // resolved to VRC_HD or VRC_RING by the entry point
+        case VRC_TREE: break;    // all-gather only
         }
         break;
     case Coll::RS:
@@ -722,7 +782,8 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
         case VRC_HD_ORDER:
             return n == 2 ? L::fused_reduce_scatter(x, y, n, count, outer, cus, st)
                           : L::template fused_reduce_scatter<vrc::Butterfly>(x, y, n, count, outer, cus, st);
-        case VRC_SELECT: break;
+        case VRC_SELECT:
+        case VRC_TREE: break;
         }
         break;
     case Coll::AG:
@@ -733,6 +794,7 @@ vrc_status_t run_typed(Coll coll, vrc_mode_t mode, const char* const* x, char* c
         case VRC_HD_ORDER: return L::fused_all_gather(x, y, n, count, outer, cus, st);
         case VRC_RING_CHAINED: return L::chain_all_gather(x, y, n, count, outer, cus, st);
         case VRC_HD: return L::hd_all_gather(x, y, n, count, outer, cus, st);
+        case VRC_TREE: return L::tree_all_gather(x, y, n, count, outer, cus, st);
         case VRC_SELECT: break;
         }
         break;

@@ -53,14 +53,27 @@ static int run_dtype(vrc_dtype_t dt, size_t count)
         CHECK_HIP(hipMalloc(&ag[r], count * esz * N));
         CHECK_HIP(hipMemcpy(x[r], host, count * esz, hipMemcpyHostToDevice));
     }
-    const vrc_mode_t modes[] = {VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER, VRC_SELECT};
+    const vrc_mode_t modes[] = {VRC_RING, VRC_FUSED, VRC_RING_CHAINED, VRC_RING_ORDER, VRC_HD, VRC_HD_ORDER, VRC_SELECT,
+                                VRC_TREE};
     for (size_t m = 0; m < sizeof(modes) / sizeof(modes[0]); m++) {
-        vrc_status_t st = vrc_allreduce((const void* const*)x, y, N, count, dt, VRC_SUM, modes[m], NULL);
+        /* The tree is an all-gather algorithm: the reduce collectives refuse it
+         * (and run fused here, so the checks below still apply to them). */
+        vrc_mode_t reduce_mode = modes[m];
+        if (modes[m] == VRC_TREE) {
+            if (vrc_allreduce((const void* const*)x, y, N, count, dt, VRC_SUM, VRC_TREE, NULL) != VRC_ERR_UNSUPPORTED ||
+                vrc_reduce_scatter((const void* const*)x, rs, N, count, 1, dt, VRC_SUM, VRC_TREE, NULL) !=
+                    VRC_ERR_UNSUPPORTED) {
+                fprintf(stderr, "VRC_TREE accepted by a reduce collective\n");
+                return 1;
+            }
+            reduce_mode = VRC_FUSED;
+        }
+        vrc_status_t st = vrc_allreduce((const void* const*)x, y, N, count, dt, VRC_SUM, reduce_mode, NULL);
         if (st != VRC_OK) {
             fprintf(stderr, "vrc_allreduce mode %d: %s\n", (int)modes[m], vrc_status_string(st));
             return 1;
         }
-        st = vrc_reduce_scatter((const void* const*)x, rs, N, count, 1, dt, VRC_SUM, modes[m], NULL);
+        st = vrc_reduce_scatter((const void* const*)x, rs, N, count, 1, dt, VRC_SUM, reduce_mode, NULL);
         if (st != VRC_OK) {
             fprintf(stderr, "vrc_reduce_scatter mode %d: %s\n", (int)modes[m], vrc_status_string(st));
             return 1;

@@ -32,7 +32,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert vrc.version() == 101 == vrc.ABI_VERSION
+    header = open(os.path.join(ROOT, "include", "vrc.h")).read()
+    declared = int(re.search(r"#define VRC_VERSION (\d+)", header).group(1))
+    assert vrc.version() == declared == vrc.ABI_VERSION == 102
     for st in range(5):
         assert vrc.lib().vrc_status_string(st).decode().startswith("VRC_")
     assert b"unknown" in vrc.lib().vrc_status_string(99)

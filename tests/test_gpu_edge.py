@@ -157,6 +157,31 @@ def test_large_ragged_flat_reduce_scatter(vrc, orc, mode, n):
         assert_bitwise(workloads.to_numpy(y), want[c], f"large ragged rs {mode} chunk {c}")
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 7, 9, 16])
+@pytest.mark.parametrize("count", [0, 1, 3, 4099])
+def test_tree_all_gather_edges(vrc, orc, n, count):
+    """The binomial-tree all-gather at any rank count (powers of two or not),
+    empty and tiny inputs, inputs and outputs on different element offsets."""
+    say(f"tree all-gather n={n} count={count}")
+    xs = workloads.random_ranks(n, count, "fp16", seed=430 + n, device=DEV)
+    vx = _views(xs, [r % 5 for r in range(n)], count)
+    vy = _views([torch.zeros(n * count, dtype=xs[0].dtype, device=DEV) for _ in range(n)],
+                [(2 * r + 1) % 7 for r in range(n)], n * count)
+    vrc.vrc_all_gather(vx, recv=vy, mode="tree")
+    torch.cuda.synchronize()
+    want = orc.tree_all_gather(host(xs), "fp16") if count else [np.zeros(0, np.float16)] * n
+    for r in range(n):
+        assert_bitwise(workloads.to_numpy(vy[r]), want[r], f"tree n={n} count={count} rank {r}")
+
+
+def test_tree_refuses_the_reduce_collectives(vrc):
+    xs = workloads.random_ranks(4, 64, "fp32", seed=431, device=DEV)
+    for call in (lambda: vrc.vrc_allreduce(xs, mode="tree"), lambda: vrc.vrc_reduce_scatter(xs, mode="tree")):
+        with pytest.raises(vrc.VrcError) as e:
+            call()
+        assert e.value.status == vrc.VRC_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_single_rank_is_identity(vrc, mode, dtype):
@@ -374,7 +399,7 @@ def test_reduce_scatter_chunks_past_2_to_31_elements(vrc, orc, mode):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("mode", MODES + ("tree",))
 def test_all_gather_output_past_2_to_32_elements(vrc, orc, mode):
     """64-bit indexing in the all-gather: 2 ranks of 2^31 + 8 bf16 elements,
     so every output holds 2^32 + 16 elements (8 GiB) and slab 1 starts past

@@ -93,3 +93,30 @@ def test_captured_reduce_scatter_and_all_gather(vrc, mode):
         for c in range(n):
             assert_bitwise(workloads.to_numpy(rs[c]), want[c], f"replay {rep} rs {mode} chunk {c}")
             assert_bitwise(workloads.to_numpy(ag[c]), gathered[c], f"replay {rep} ag {mode} rank {c}")
+
+
+@pytest.mark.parametrize("n", [5, 8])
+def test_captured_tree_all_gather(vrc, n):
+    """The binomial-tree all-gather (2 ceil(log2 N) launches) captured once
+    and replayed on fresh inputs."""
+    print(f"graph tree all-gather n={n}", flush=True)
+    orc = oracle.get()
+    xs = workloads.random_ranks(n, (3, 4097), "bf16", seed=520 + n, device=DEV)
+    ag = vrc.vrc_all_gather(xs, dim=-1, mode="tree")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        vrc.vrc_all_gather(xs, recv=ag, dim=-1, mode="tree")
+    torch.cuda.synchronize()
+    for rep in range(3):
+        fresh = workloads.random_ranks(n, (3, 4097), "bf16", seed=720 + rep, device=DEV)
+        for x, f in zip(xs, fresh):
+            x.copy_(f)
+        for y in ag:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = orc.tree_all_gather(host(fresh), "bf16", outer=3)
+        for r in range(n):
+            assert_bitwise(workloads.to_numpy(ag[r]), want[r], f"replay {rep} tree rank {r}")

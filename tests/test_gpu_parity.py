@@ -24,6 +24,7 @@ DTYPES = ("int32", "fp32", "fp16", "bf16")
 MODES = ("ring", "fused", "ring_chained", "ring_order", "hd", "hd_order")
 RING_FAMILY = ("ring", "ring_chained", "ring_order")  # all return the per-step ring's bits
 HD_FAMILY = ("hd", "hd_order")  # halving-doubling: power-of-two rank counts only
+AG_MODES = MODES + ("tree",)  # the binomial tree is an all-gather mode only
 
 
 def pow2(n):
@@ -129,7 +130,17 @@ AG_CASES = [  # (n, shape, dim)
 ]
 
 
-@pytest.mark.parametrize("mode", MODES)
+def want_ag(orc, hx, dtype, mode, outer=1):
+    """The all-gather of the mode's own step-literal oracle (every algorithm
+    gives the concatenation; each is checked against its own simulation)."""
+    if mode in HD_FAMILY:
+        return orc.hd_all_gather(hx, dtype, outer=outer)
+    if mode == "tree":
+        return orc.tree_all_gather(hx, dtype, outer=outer)
+    return orc.ring_all_gather(hx, dtype, outer=outer)
+
+
+@pytest.mark.parametrize("mode", AG_MODES)
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("n,shape,dim", AG_CASES)
 def test_all_gather_small(vrc, orc, mode, dtype, n, shape, dim):
@@ -140,7 +151,7 @@ def test_all_gather_small(vrc, orc, mode, dtype, n, shape, dim):
     ys = vrc.vrc_all_gather(xs, dim=dim, mode=mode)
     torch.cuda.synchronize()
     outer = int(np.prod(shape[:dim % len(shape)])) if len(shape) > 1 else 1
-    want = (orc.hd_all_gather if mode in HD_FAMILY else orc.ring_all_gather)(host(xs), dtype, outer=outer)
+    want = want_ag(orc, host(xs), dtype, mode, outer)
     ref = torch.cat(xs, dim=dim)
     for r, y in enumerate(ys):
         assert tuple(y.shape) == tuple(ref.shape)
@@ -268,7 +279,8 @@ def test_workload_all_gather_fp16_n8_heads(vrc, orc):
     xs = workloads.make_inputs(w, DEV)
     want = orc.ring_all_gather(host(xs), "fp16", outer=1)
     assert all(np.array_equal(a, b) for a, b in zip(want, orc.hd_all_gather(host(xs), "fp16", outer=1)))
-    for mode in MODES:
+    assert all(np.array_equal(a, b) for a, b in zip(want, orc.tree_all_gather(host(xs), "fp16", outer=1)))
+    for mode in AG_MODES:
         say(f"{w.name} {mode}")
         ys = vrc.vrc_all_gather(xs, dim=w.dim, mode=mode)
         torch.cuda.synchronize()
@@ -337,11 +349,17 @@ def test_fused_launch_shapes(vrc, orc, n):
     say(f"fused shapes n={n} count={count} {dtype}")
     base = workloads.random_ranks(n, count + 1, dtype, seed=700 + n, device=DEV, sigma=1e-2)
     modes = ("fused", "hd_order") if pow2(n) else ("fused",)
-    for offset in (0, 1):  # offset 1: every buffer starts one element past a 16-byte boundary
-        xs = [b[offset:offset + count] for b in base]
+    # offset 1: every buffer starts one element past a 16-byte boundary; "mixed": rank r's output r
+    # elements into its own buffer, so the outputs do not share one vector grid (its own launch shape)
+    for offset in (0, 1, "mixed"):
+        xs = [b[1:1 + count] if offset == "mixed" else b[offset:offset + count] for b in base]
         hx = host(xs)
         for mode in modes:
-            ys = vrc.vrc_allreduce(xs, mode=mode)
+            if offset == "mixed":
+                ys = [torch.empty(count + 16, dtype=xs[0].dtype, device=DEV)[r % 16:r % 16 + count] for r in range(n)]
+                vrc.vrc_allreduce(xs, recv=ys, mode=mode)
+            else:
+                ys = vrc.vrc_allreduce(xs, mode=mode)
             torch.cuda.synchronize()
             ranks_identical(ys, f"{mode} n={n} offset={offset}")
             want = want_ar(orc, hx, dtype, mode)
@@ -352,13 +370,12 @@ def test_fused_launch_shapes(vrc, orc, n):
 
 # ---------------------------------------------------------------------------
 # fused and single-launch ring reduce-scatter over flat chunks from 64 MiB moved:
-# one-wave tiles over all chunks (every chunk 16-byte compatible), else one
-# grid row per chunk
+# one-wave tiles over all chunks, whatever the offsets of inputs and outputs
 # ---------------------------------------------------------------------------
 RS_FLAT_LAYOUTS = {
     "aligned": (0, 0),         # inputs and outputs on 16-byte boundaries: vector body, ragged tail
     "both_offset": (1, 1),     # inputs and outputs one element past a boundary: scalar heads
-    "inputs_offset": (1, 0),   # offsets differ between inputs and outputs: the per-chunk grid
+    "inputs_offset": (1, 0),   # inputs off the outputs' grid: unaligned vector loads
 }
 
 

@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 from tests.parity_util import assert_bitwise, host
-from tests.test_gpu_parity import DTYPES, HD_FAMILY, MODES, want_ar, want_rs
+from tests.test_gpu_parity import AG_MODES, DTYPES, HD_FAMILY, MODES, want_ag, want_ar, want_rs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -45,10 +45,10 @@ def orc():
     return oracle.get()
 
 
-def draw(kind: int, k: int):
+def draw(kind: int, k: int, modes=MODES):
     rng = case_rng(7919 * kind + k)
     dtype = str(rng.choice(DTYPES))
-    mode = str(rng.choice(MODES))
+    mode = str(rng.choice(modes))
     n = int(2 ** rng.integers(0, 5)) if mode in HD_FAMILY else int(rng.integers(1, 17))
     return rng, dtype, mode, n
 
@@ -130,7 +130,7 @@ def test_random_reduce_scatter(vrc, orc, k):
 
 @pytest.mark.parametrize("k", range(CASES))
 def test_random_all_gather(vrc, orc, k):
-    rng, dtype, mode, n = draw(3, k)
+    rng, dtype, mode, n = draw(3, k, AG_MODES)
     nd = int(rng.integers(1, 4))
     shape = tuple(int(rng.integers(1, 9)) for _ in range(nd - 1)) + (log_uniform(rng, 800) + 1,)
     dim = int(rng.integers(0, nd))
@@ -143,7 +143,7 @@ def test_random_all_gather(vrc, orc, k):
     hx = host(xs)
     vrc.vrc_all_gather(xs, recv=ys, dim=dim, mode=mode)
     torch.cuda.synchronize()
-    want = orc.ring_all_gather(hx, dtype, outer=outer)
+    want = want_ag(orc, hx, dtype, mode, outer)
     for r, y in enumerate(host(ys)):
         assert_bitwise(y, want[r], f"case {k} {mode} {dtype} n={n} shape={shape} dim={dim} rank {r}")
 

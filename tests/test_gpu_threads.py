@@ -22,10 +22,10 @@ def vrc():
 
 
 def test_concurrent_callers_on_their_own_streams(vrc):
-    print(f"threads: 4 callers x {len(vrc.MODES)} modes", flush=True)
+    print(f"threads: 4 callers x {len(vrc.REDUCE_MODES)} modes", flush=True)
     orc = oracle.get()
     n, count = 8, 200003
-    modes = list(vrc.MODES)
+    modes = list(vrc.REDUCE_MODES)
     inputs = [workloads.random_ranks(n, count, "bf16", seed=900 + t, device=DEV) for t in range(4)]
     outs = [{m: [torch.empty_like(x) for x in inputs[t]] for m in modes} for t in range(4)]
     torch.cuda.synchronize()

@@ -78,20 +78,38 @@ def test_op_desc_layout_matches_the_header():
     assert vrc.OpDesc.grid_x.offset == off_grid and vrc.OpDesc.vectors.offset == off_vec
 
 
+FUSED_SHAPES = {2: (2, 8), 3: (2, 4), 4: (1, 8), 5: (2, 2), 6: (2, 2), 7: (2, 2), 8: (4, 1)}  # n: (per CU, U)
+
+
 @pytest.mark.parametrize("n", list(range(2, 17)))
-def test_fused_allreduce_one_wave_budget(n):
-    """8 GiB moved: one-wave workgroups, two vectors per rank at 3-4 ranks,
-    workgroups per CU from the 32-loads budget (8 at 2 ranks, 4 at 3-8,
-    2 at 9-16)."""
+def test_fused_allreduce_one_wave_shapes(n):
+    """8 GiB moved: one-wave workgroups taking U consecutive tiles, by rank
+    count: U 8 at 2 per CU (2 ranks), U 4 at 2 (3), U 8 at 1 (4), U 2 at 2
+    (5-7), U 1 at 4 (8) and at 2 (9-16)."""
     count = (4 << 30) // n // 2 // 64 * 64
-    vectors = 2 if n in (3, 4) else 1
-    bpc = budget_blocks_per_cu(n, vectors)
-    assert bpc == (8 if n == 2 else 4 if n <= 8 else 2)
+    bpc, vectors = FUSED_SHAPES.get(n, (2, 1))
+    assert vectors * n <= 32
     got = plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_FUSED)
     assert got == [("fused_allreduce", CUS * bpc, 1, 64, vectors)]
     if n & (n - 1) == 0 and n > 2:  # halving-doubling in one launch: the same kernel with the butterfly fold
         assert plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_HD_ORDER) == [("butterfly_allreduce", CUS * bpc, 1, 64,
                                                                       vectors)]
+
+
+@pytest.mark.parametrize("n", list(range(2, 17)))
+def test_fused_allreduce_outputs_off_one_grid(n):
+    """Outputs on different offsets modulo 128 bytes: the largest U <= 8 with
+    U x N <= 32 consecutive tiles per wave, at 64 / (U x N) workgroups per CU."""
+    count = (4 << 30) // n // 2 // 64 * 64
+    send, recv = wide(n)
+    recv = [a + 2 * r for r, a in enumerate(recv)]
+    u = 8
+    while u * n > 32:
+        u //= 2
+    bpc = 64 // (u * n)
+    bpc = 1 << (bpc.bit_length() - 1)
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
+    assert launches(ops) == [("fused_allreduce", CUS * bpc, 1, 64, u)]
 
 
 def test_headline_shape():
@@ -262,7 +280,7 @@ def test_split_dimension_and_small_reduce_scatters_keep_the_chunk_grid():
     assert launches(ops)[0][2:4] == (n, 256)
 
 
-@pytest.mark.parametrize("mode", sorted(vrc.MODES))
+@pytest.mark.parametrize("mode", sorted(vrc.REDUCE_MODES))
 def test_mixed_offsets_keep_the_full_grid(mode):
     """8 x 512 MiB bf16 all-reduce with rank r's input and output 2r bytes
     past a 256-byte boundary: every mode plans the launches of the aligned
@@ -275,6 +293,10 @@ def test_mixed_offsets_keep_the_full_grid(mode):
     aligned, nl = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, vrc.VRC_BF16, vrc.MODES[mode])
     mixed, nl2 = vrc.plan(vrc.COLL_ALLREDUCE, mixed_send, mixed_recv, count, 1, vrc.VRC_BF16, vrc.MODES[mode])
     assert nl2 == nl
-    assert launches(mixed) == launches(aligned)
+    if mode in ("fused", "hd_order"):
+        # the fused kernel takes its shape for outputs off one grid (test above)
+        assert [k[0] for k in launches(mixed)] == [k[0] for k in launches(aligned)]
+    else:
+        assert launches(mixed) == launches(aligned)
     for kind, gx, gy, block, vec in launches(mixed):
         assert gx * gy * block >= CUS * 64, kind

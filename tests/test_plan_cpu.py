@@ -1,7 +1,7 @@
 """The library's own launch plans, checked on the CPU (vrc_plan launches
-nothing): the ring and halving-doubling schedules against the hand-derived
-N = 4 fixtures, the chunk partition, the algorithmic bytes of each mode, and
-that no two operations of one launch race."""
+nothing): the ring, halving-doubling and binomial-tree schedules against the
+hand-derived fixtures, the chunk partition, the algorithmic bytes of each
+mode, and that no two operations of one launch race."""
 import os
 
 import pytest
@@ -196,6 +196,74 @@ def test_no_races_in_reduce_scatter_and_all_gather_plans(mode, n, outer, row):
     for coll in (vrc.COLL_REDUCE_SCATTER, vrc.COLL_ALL_GATHER):
         ops, _ = vrc.plan(coll, send, recv, outer * row, outer, vrc.VRC_FP32, mode)
         assert not races(ops)
+
+
+@pytest.mark.parametrize("n,name", [(4, "tree_n4_schedule.txt"), (5, "tree_n5_schedule.txt")])
+def test_tree_all_gather_plan_matches_the_textbook_schedule(n, name):
+    """The tree all-gather's copies, read as messages (source rank, receiving
+    rank, slab range), are the hand-derived gather and broadcast schedules;
+    the first gather launch also places each receiving rank's own slab."""
+    count = 6
+    send, recv = buffers(n)
+    ops, launches = vrc.plan(vrc.COLL_ALL_GATHER, send, recv, count, 1, vrc.VRC_FP32, vrc.VRC_TREE)
+    k = (n - 1).bit_length()
+    assert launches == 2 * k
+    got, own = [], []
+    for op in ops:
+        assert op["kind"] == "copy"
+        dst, doff = owner(op["d"], recv)
+        if op["launch"] < k:
+            phase, step = "gather", op["launch"]
+            lo, hi = doff // (count * E), doff // (count * E) + op["width"] // count
+            if op["a"] in send:
+                src = send.index(op["a"])
+                if src == dst:
+                    own.append(dst)
+                    continue
+            else:
+                src, aoff = owner(op["a"], recv)
+                assert aoff == doff
+        else:
+            phase, step = "bcast", op["launch"] - k
+            src, aoff = owner(op["a"], recv)
+            assert aoff == doff == 0 and op["width"] == n * count
+            lo, hi = 0, n
+        got.append((phase, str(step), str(src), str(dst), str(lo), str(hi)))
+    assert sorted(got) == sorted(tuple(r) for r in rows(name))
+    assert own == list(range(0, n, 2))
+
+
+def tree_slab_copies(n):
+    return (n + 1) // 2 + sum(bin(j).count("1") for j in range(n)) + n * (n - 1)
+
+
+@pytest.mark.parametrize("n", list(range(1, 17)))
+def test_tree_plan_moves_the_tree_bytes(n):
+    """Each copy reads and writes its slabs once: ceil(N/2) own slabs, slab j
+    once per set bit of j in the gather, N slabs to each of the N - 1 other
+    ranks in the broadcast."""
+    outer, row = 2, 5
+    send, recv = buffers(n)
+    ops, launches = vrc.plan(vrc.COLL_ALL_GATHER, send, recv, outer * row, outer, vrc.VRC_FP32, vrc.VRC_TREE)
+    moved = sum(o["rows"] * o["width"] * E * 2 for o in ops)
+    assert moved == 2 * tree_slab_copies(n) * outer * row * E
+    assert launches == (2 * (n - 1).bit_length() if n > 1 else 1)
+
+
+@pytest.mark.parametrize("n", list(range(2, 17)))
+@pytest.mark.parametrize("outer,row", [(1, 7), (3, 8)])
+def test_no_races_in_tree_all_gather_plans(n, outer, row):
+    send, recv = buffers(n)
+    ops, _ = vrc.plan(vrc.COLL_ALL_GATHER, send, recv, outer * row, outer, vrc.VRC_FP32, vrc.VRC_TREE)
+    assert not races(ops)
+
+
+def test_tree_is_an_all_gather_mode_only():
+    send, recv = buffers(4)
+    for coll in (vrc.COLL_ALLREDUCE, vrc.COLL_REDUCE_SCATTER):
+        with pytest.raises(vrc.VrcError) as e:
+            vrc.plan(coll, send, recv, 100, 1, vrc.VRC_FP32, vrc.VRC_TREE)
+        assert e.value.status == vrc.VRC_ERR_UNSUPPORTED
 
 
 def test_plan_validates_like_the_call():
