@@ -18,7 +18,7 @@ same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--mode fused|ring|ring_chained|ring_order|hd|hd_order|select]
-       python bench.py --suite | --offsets | --ag-sweep | --overlap | --probe-copy
+       python bench.py --suite | --offsets | --ag-sweep | --overlap [--buckets] | --probe-copy
 """
 from __future__ import annotations
 
@@ -142,11 +142,16 @@ def cpu_baseline(xs, w, mode: str):
     }
 
 
-def selected(mode: str, n: int, size: int) -> str:
+def selected(mode: str, n: int, size: int, collective: str = "allreduce") -> str:
     """The algorithm VRC_SELECT runs (the rule stated in include/vrc.h)."""
     if mode != "select":
         return mode
-    return "hd" if n & (n - 1) == 0 and size <= (64 << 20) else "ring"
+    if n & (n - 1) == 0 and size <= (64 << 20):
+        return "hd"
+    saved = (n - 1) - 2 * (n - 1).bit_length()
+    if collective == "all_gather" and n & (n - 1) and saved > 0 and size <= saved * (128 << 10):
+        return "tree"
+    return "ring"
 
 
 def tree_slab_copies(n: int) -> int:
@@ -159,9 +164,9 @@ def tree_slab_copies(n: int) -> int:
 def suite_bytes(w, mode: str) -> int:
     """Algorithmic bytes per call for a workload's collective and mode."""
     n, size = w.n, w.count * w.esize
+    mode = selected(mode, n, size, w.collective)
     if mode == "tree":
         return 2 * tree_slab_copies(n) * size
-    mode = selected(mode, n, size)
     fused_like = mode in ("fused", "ring_order", "hd_order")
     if w.collective == "reduce_scatter" and mode == "hd":
         fused_like = True  # the stand-alone halving-doubling reduce-scatter runs as one butterfly launch
@@ -351,8 +356,8 @@ def run_ag_sweep(steps: int, torch, vrc, workloads) -> int:
     (ranks, size)."""
     dev = "cuda:0"
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    for n in (4, 6, 8, 12, 16):
-        for per_rank in (4 << 10, 64 << 10, 1 << 20, 8 << 20, 32 << 20, 128 << 20):
+    for n in (4, 6, 8, 10, 12, 14, 16):
+        for per_rank in (4 << 10, 64 << 10, 256 << 10, 512 << 10, 1 << 20, 8 << 20, 32 << 20, 128 << 20):
             if n * n * per_rank > (8 << 30):
                 continue
             count = per_rank // 2
@@ -449,6 +454,95 @@ def run_overlap(steps: int, mode: str, torch, vrc, workloads) -> int:
     return 0
 
 
+def run_overlap_buckets(steps: int, mode: str, torch, vrc, workloads, only=None) -> int:
+    """The pages' recipe for hiding the all-reduce behind the computation that
+    produces its input (www.bjdmk.com.cn/news/5966809/, sections 4.2-4.3): the
+    compute stream writes the gradients bucket by bucket and records an event
+    per bucket; the communication stream waits on each event and all-reduces
+    that bucket (vrc_allreduce_bucketed).  The producer of bucket k is one GEMM
+    per rank, [rows_k, K] x [K, 4096] in bf16, written straight into that
+    rank's bucket: K = 512 makes all buckets together take about as long as
+    the all-reduce (the GEMMs write as many bytes as the all-reduce reads),
+    K = 4096 makes them compute-bound, like a weight gradient summed over many
+    tokens.  For each bucket size: the GEMMs alone, the bucketed all-reduce
+    alone (no waits), and both; `exposed_ms` = both - GEMMs alone is the
+    communication the overlap failed to hide.  Totals: the 8 x 512 MiB bf16
+    gradients (buckets from 1 MiB per rank), and 8 x 16 MiB (buckets from
+    64 KiB, K = 512).  One JSON line per case."""
+    dev = "cuda:0"
+    n, cols = 8, 4096
+    g = torch.Generator(device=dev).manual_seed(11)
+    s_comp, s_comm = torch.cuda.Stream(), torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+
+    def timed(launch, reps):
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            s_comp.wait_event(e0)
+            s_comm.wait_event(e0)
+            launch()
+            cur.wait_event(s_comp.record_event())
+            cur.wait_event(s_comm.record_event())
+            e1.record(cur)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        return ms[len(ms) // 2]
+
+    series = ((512 << 20, 512, (1 << 20, 4 << 20, 16 << 20, 64 << 20, 256 << 20, 512 << 20)),
+              (512 << 20, 4096, (4 << 20, 16 << 20, 64 << 20, 128 << 20, 256 << 20, 512 << 20)),
+              (16 << 20, 512, (64 << 10, 256 << 10, 1 << 20, 4 << 20, 16 << 20)))
+    if only is not None:  # one case: (K, bucket MiB per rank) on the 8 x 512 MiB gradients
+        series = ((512 << 20, only[0], (only[1] << 20,)),)
+    for per_rank, k_dim, buckets in series:
+        count = per_rank // 2
+        rows = count // cols
+        grads = [torch.empty(rows, cols, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+        outs = [torch.empty_like(x) for x in grads]
+        a = torch.randn(rows, k_dim, generator=g, device=dev).to(torch.bfloat16)
+        wt = torch.randn(k_dim, cols, generator=g, device=dev).to(torch.bfloat16)
+        flat_g = [x.view(-1) for x in grads]
+        flat_o = [x.view(-1) for x in outs]
+        for bucket_bytes in buckets:
+            b_rows = bucket_bytes // 2 // cols
+            nb = rows // b_rows
+            events = [torch.cuda.Event() for _ in range(nb)]
+
+            def produce(record):
+                with torch.cuda.stream(s_comp):
+                    for k in range(nb):
+                        for x in grads:
+                            torch.matmul(a[k * b_rows:(k + 1) * b_rows], wt, out=x[k * b_rows:(k + 1) * b_rows])
+                        if record:
+                            events[k].record(s_comp)
+
+            def reduce(ready):
+                vrc.vrc_allreduce_bucketed(flat_g, recv=flat_o, bucket=b_rows * cols, mode=mode,
+                                           ready=events if ready else None, stream=s_comm)
+
+            produce(True)
+            reduce(True)
+            torch.cuda.synchronize()
+            reps = max(3, min(steps, 10))
+            t_comp = timed(lambda: produce(False), reps)
+            t_ar = timed(lambda: reduce(False), reps)
+            t_both = timed(lambda: (produce(True), reduce(True)), reps)
+            rec = {"overlap_buckets": {
+                "mode": mode, "n_ranks": n, "bytes_per_rank": per_rank, "bucket_bytes_per_rank": bucket_bytes,
+                "buckets": nb, "gemm": [b_rows, k_dim, cols], "compute_ms": round(t_comp, 4),
+                "allreduce_ms": round(t_ar, 4), "both_ms": round(t_both, 4), "serial_ms": round(t_comp + t_ar, 4),
+                "exposed_ms": round(t_both - t_comp, 4),
+                "hidden_fraction_of_allreduce": round((t_comp + t_ar - t_both) / t_ar, 3)}}
+            print(json.dumps(rec), flush=True)
+            log(f"K={k_dim:4d} {per_rank >> 20:4d} MiB/rank in {bucket_bytes >> 10:7d} KiB: compute {t_comp:8.3f} ms  "
+                f"all-reduce {t_ar:8.3f}  both {t_both:8.3f}  exposed {t_both - t_comp:8.3f} ms")
+        del grads, outs, a, wt, flat_g, flat_o
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,6 +555,11 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true", help="skip the extra ring-mode timing")
     ap.add_argument("--overlap", action="store_true",
                     help="time the all-reduce alone, a matmul stream alone, and both on two streams")
+    ap.add_argument("--buckets", action="store_true",
+                    help="with --overlap: the bucketed all-reduce behind the GEMMs that produce each bucket, "
+                         "swept over bucket sizes")
+    ap.add_argument("--bucket-case", default=None,
+                    help="with --overlap --buckets: one case only, 'K,MiB' (GEMM depth, bucket MiB per rank)")
     ap.add_argument("--suite", action="store_true",
                     help="measure every workload in every mode (one JSON line each) instead of the headline")
     ap.add_argument("--offsets", action="store_true",
@@ -492,6 +591,9 @@ def main() -> int:
         return run_offsets(args.steps, torch, vrc, workloads)
     if args.ag_sweep:
         return run_ag_sweep(args.steps, torch, vrc, workloads)
+    if args.overlap and args.buckets:
+        only = tuple(int(v) for v in args.bucket_case.split(",")) if args.bucket_case else None
+        return run_overlap_buckets(args.steps, args.mode, torch, vrc, workloads, only)
     if args.overlap:
         return run_overlap(args.steps, args.mode, torch, vrc, workloads)
     if args.probe_copy:

@@ -88,11 +88,13 @@
 extern "C" {
 #endif
 
-#define VRC_VERSION 102 /* 1.0.2: VRC_TREE all-gather */
+#define VRC_VERSION 103 /* 1.0.3: vrc_allreduce_bucketed */
 #define VRC_MAX_RANKS 16
 
 struct ihipStream_t;
 typedef struct ihipStream_t* vrc_stream_t; /* the same type as hipStream_t */
+struct ihipEvent_t;
+typedef struct ihipEvent_t* vrc_event_t;   /* the same type as hipEvent_t */
 
 typedef enum { VRC_INT32 = 0, VRC_FP32 = 1, VRC_FP16 = 2, VRC_BF16 = 3 } vrc_dtype_t;
 typedef enum { VRC_SUM = 0 } vrc_op_t;
@@ -133,14 +135,20 @@ typedef enum { VRC_SUM = 0 } vrc_op_t;
  *                     vrc_plan reports it) as the fused kernel.
  * Size-based selection between the two step-by-step algorithms [TP]:
  *   VRC_SELECT        VRC_HD when nranks is a power of two and each rank's
- *                     input holds at most VRC_SELECT_HD_MAX_BYTES, else
+ *                     input holds at most VRC_SELECT_HD_MAX_BYTES.  For the
+ *                     all-gather at other rank counts, VRC_TREE while it
+ *                     saves launches, L = (nranks-1) - 2 ceil(log2 nranks) >
+ *                     0, and each rank's input holds at most
+ *                     L * VRC_SELECT_TREE_BYTES_PER_SAVED_LAUNCH.  Else
  *                     VRC_RING.  The bits are those of the algorithm chosen
  *                     (vrc_plan shows which: 2 log2 N or 2(N-1) launches for
- *                     the all-reduce).  Any nranks is accepted.  The limit
- *                     is where the ring's fewer, larger launches overtake
- *                     halving-doubling's log2 N steps on MI355X (8 ranks:
+ *                     the all-reduce).  Any nranks is accepted.  The limits
+ *                     are where the ring's fewer, larger launches overtake
+ *                     the log-depth algorithms on MI355X (8 ranks:
  *                     halving-doubling 8 % faster at 16 MiB, the ring 3 %
- *                     faster at 128 MiB per rank). */
+ *                     faster at 128 MiB per rank; the tree all-gather 13-35 %
+ *                     faster than the ring at 10-14 ranks and 64 KiB, within
+ *                     5 % either way at 128-512 KiB, slower from 1 MiB). */
 /* Binomial tree [TREE], all-gather only (vrc_allreduce and
  * vrc_reduce_scatter return VRC_ERR_UNSUPPORTED for it): the textbook
  * binomial gather to rank 0 followed by the binomial broadcast from rank 0
@@ -153,6 +161,7 @@ typedef enum { VRC_SUM = 0 } vrc_op_t;
  *                     nranks.  The bytes are the concatenation, as in every
  *                     all-gather mode. */
 #define VRC_SELECT_HD_MAX_BYTES (64ull << 20)
+#define VRC_SELECT_TREE_BYTES_PER_SAVED_LAUNCH (128ull << 10)
 typedef enum {
     VRC_RING = 0,
     VRC_FUSED = 1,
@@ -185,6 +194,34 @@ typedef enum {
  */
 vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
                            vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, vrc_stream_t stream);
+
+/*
+ * Bucketed all-reduce, overlapped with the computation that produces its
+ * input [OVERLAP] (www.bjdmk.com.cn/news/5966809/, sections 4.2 and 4.3:
+ * the compute stream records an event when a chunk of the tensor is ready,
+ * the communication stream waits on that event and all-reduces the chunk
+ * while the next chunk is computed).
+ *   Every rank's buffer is cut into buckets of `bucket` elements (the last
+ *   one holds the rest): bucket k is elements [k*bucket, min((k+1)*bucket,
+ *   count)).  For k = 0, 1, ... the call enqueues on `stream` a wait on
+ *   ready[k] (when `ready` is not NULL) and then the all-reduce of bucket k
+ *   alone, exactly as vrc_allreduce would run it on those slices, and
+ *   VRC_SELECT picks per bucket.  VRC_FUSED and the halving-doubling modes
+ *   fold every element the same way whatever the partition, so they give
+ *   the bits of the unbucketed call; the ring modes fold chunk c of each
+ *   bucket from rank c, so theirs are the bits of each bucket's own ring.
+ *   ready     NULL, or `nready` == number of buckets events (hipEvent_t)
+ *             recorded by the caller on the stream that produces the data;
+ *             NULL with nready == 0 runs the buckets back to back.
+ *   The buffers, in-place rule, modes and errors are those of
+ *   vrc_allreduce over the whole buffers (VRC_TREE is refused); bucket == 0,
+ *   a NULL event or a wrong nready returns VRC_ERR_INVALID_ARG before
+ *   anything is enqueued.  A HIP failure at bucket k returns VRC_ERR_HIP
+ *   with buckets 0..k-1 already enqueued.  count == 0 enqueues nothing.
+ */
+vrc_status_t vrc_allreduce_bucketed(const void* const* send, void* const* recv, int nranks, size_t count,
+                                    vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, size_t bucket,
+                                    const vrc_event_t* ready, int nready, vrc_stream_t stream);
 
 /*
  * Reduce-scatter (sum) [RS][REM][TP].
@@ -225,7 +262,8 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
 /*
  * Launch plan, host only: what a call would enqueue, without touching the
  * GPU.  vrc_plan takes the arguments of the collective named by `coll`
- * (`outer` is ignored for the all-reduce) and fills `ops` with one entry
+ * (`outer` is ignored for the all-reduce and is the bucket size for
+ * VRC_COLL_ALLREDUCE_BUCKETED, planned without events) and fills `ops` with one entry
  * per operation, in launch order.  Ring and halving-doubling steps give one
  * entry per rank operation of the step (VRC_OP_ADD: d = a + b, VRC_OP_COPY:
  * d = a, over `rows` rows of `width` elements with the given row strides in
@@ -237,7 +275,12 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
  * returned.  Used by the tests to check the schedules on the CPU, and for
  * debugging.
  */
-typedef enum { VRC_COLL_ALLREDUCE = 0, VRC_COLL_REDUCE_SCATTER = 1, VRC_COLL_ALL_GATHER = 2 } vrc_coll_t;
+typedef enum {
+    VRC_COLL_ALLREDUCE = 0,
+    VRC_COLL_REDUCE_SCATTER = 1,
+    VRC_COLL_ALL_GATHER = 2,
+    VRC_COLL_ALLREDUCE_BUCKETED = 3 /* `outer` carries the bucket size in elements; no events */
+} vrc_coll_t;
 
 typedef enum {
     VRC_OP_ADD = 0,

@@ -53,7 +53,7 @@ class VrcError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 102  # VRC_VERSION of include/vrc.h that these mirrors follow
+ABI_VERSION = 103  # VRC_VERSION of include/vrc.h that these mirrors follow
 
 
 class OpDesc(C.Structure):
@@ -64,7 +64,7 @@ class OpDesc(C.Structure):
                 ("vectors", C.c_uint)]
 
 
-COLL_ALLREDUCE, COLL_REDUCE_SCATTER, COLL_ALL_GATHER = 0, 1, 2
+COLL_ALLREDUCE, COLL_REDUCE_SCATTER, COLL_ALL_GATHER, COLL_ALLREDUCE_BUCKETED = 0, 1, 2, 3
 OP_KINDS = {0: "add", 1: "copy", 2: "fused_allreduce", 3: "fused_reduce_scatter", 4: "fused_all_gather",
             5: "chain_allreduce", 6: "chain_reduce_scatter", 7: "chain_all_gather", 8: "ring_order_allreduce",
             9: "ring_order_reduce_scatter", 10: "butterfly_allreduce", 11: "butterfly_reduce_scatter"}
@@ -93,6 +93,8 @@ def _load():
     L.vrc_reduce_scatter.restype = i
     L.vrc_all_gather.argtypes = [ptrs, ptrs, i, sz, sz, i, i, vp]
     L.vrc_all_gather.restype = i
+    L.vrc_allreduce_bucketed.argtypes = [ptrs, ptrs, i, sz, i, i, i, sz, ptrs, i, vp]
+    L.vrc_allreduce_bucketed.restype = i
     L.vrc_plan.argtypes = [i, ptrs, ptrs, i, sz, sz, i, i, C.POINTER(OpDesc), i, C.POINTER(i), C.POINTER(i)]
     L.vrc_plan.restype = i
     L.vrc_chunk_range.argtypes = [sz, i, i, C.POINTER(sz), C.POINTER(sz)]
@@ -142,6 +144,13 @@ def raw_reduce_scatter(send, recv, count, outer, dtype, mode, stream=0, op=VRC_S
 def raw_all_gather(send, recv, count, outer, dtype, mode, stream=0) -> int:
     return _lib.vrc_all_gather(_ptr_array(send), _ptr_array(recv), len(send), count, outer, dtype, mode,
                                stream or None)
+
+
+def raw_allreduce_bucketed(send, recv, count, dtype, mode, bucket, ready=(), stream=0, op=VRC_SUM) -> int:
+    """`ready`: raw hipEvent_t handles, one per bucket, or empty for none."""
+    events = _ptr_array(list(ready)) if ready else None
+    return _lib.vrc_allreduce_bucketed(_ptr_array(send), _ptr_array(recv), len(send), count, dtype, op, mode, bucket,
+                                       events, len(ready), stream or None)
 
 
 def plan(coll: int, send, recv, count: int, outer: int, dtype: int, mode: int):
@@ -267,6 +276,41 @@ def vrc_allreduce(send, recv=None, mode: str = "fused", stream=None):
     return recv
 
 
+def bucket_count(count: int, bucket: int) -> int:
+    """Number of buckets vrc_allreduce_bucketed cuts `count` elements into."""
+    return 0 if count == 0 else (count - 1) // bucket + 1
+
+
+def vrc_allreduce_bucketed(send, recv=None, bucket: int = 1 << 20, mode: str = "fused", ready=None, stream=None):
+    """The all-reduce of `send` bucket by bucket (`bucket` elements per rank
+    each, the last one smaller): bucket k's launches wait on ``ready[k]`` (a
+    recorded torch.cuda.Event, e.g. marking that the compute stream has
+    written bucket k of every rank), so the all-reduce of early buckets
+    overlaps the computation of later ones."""
+    torch = _torch()
+    _check_ranks(send, "vrc_allreduce_bucketed")
+    if recv is None:
+        recv = [torch.empty_like(t) for t in send]
+    _check_ranks(recv, "vrc_allreduce_bucketed")
+    if len(recv) != len(send) or recv[0].shape != send[0].shape or recv[0].dtype != send[0].dtype:
+        raise ValueError("vrc_allreduce_bucketed: recv must match send")
+    _same_device(send, recv, "vrc_allreduce_bucketed")
+    if bucket < 1:
+        raise ValueError("vrc_allreduce_bucketed: bucket must be at least one element")
+    handles = []
+    if ready is not None:
+        if len(ready) != bucket_count(send[0].numel(), bucket):
+            raise ValueError("vrc_allreduce_bucketed: one event per bucket")
+        handles = [e.cuda_event for e in ready]
+        if not all(handles):
+            raise ValueError("vrc_allreduce_bucketed: every event must have been recorded")
+    st = raw_allreduce_bucketed([t.data_ptr() for t in send], [t.data_ptr() for t in recv], send[0].numel(),
+                                _dtype_code(send[0]), _mode(mode), bucket, handles, _stream(stream, send[0].device))
+    if st != VRC_OK:
+        raise VrcError(st, "vrc_allreduce_bucketed")
+    return recv
+
+
 def reduce_scatter_shape(shape, nranks: int, dim: int = 0):
     """Output shape of rank c for the reduce-scatter of `shape` along `dim`.
 
@@ -336,6 +380,23 @@ def vrc_all_gather(send, recv=None, dim: int = 0, mode: str = "fused", stream=No
     return recv
 
 
+def all_reduce(tensors, mode: str = "fused", out=None, stream=None):
+    """all_reduce(list of per-rank tensors, mode, out=None): ``vrc_allreduce``
+    under the name of the tensor-parallel interface (``tp.all_reduce``)."""
+    return vrc_allreduce(tensors, recv=out, mode=mode, stream=stream)
+
+
+def reduce_scatter(tensors, dim: int = 0, mode: str = "fused", out=None, stream=None):
+    """reduce_scatter(list of per-rank tensors, dim, mode): ``vrc_reduce_scatter``."""
+    return vrc_reduce_scatter(tensors, recv=out, dim=dim, mode=mode, stream=stream)
+
+
+def all_gather(tensors, dim: int = 0, mode: str = "fused", out=None, stream=None):
+    """all_gather(list of per-rank tensors, dim, mode): ``vrc_all_gather``
+    under the name of the tensor-parallel interface (``tp.all_gather``)."""
+    return vrc_all_gather(tensors, recv=out, dim=dim, mode=mode, stream=stream)
+
+
 def _prod(shape) -> int:
     p = 1
     for k in shape:
@@ -345,7 +406,9 @@ def _prod(shape) -> int:
 
 __all__ = [
     "plan", "OpDesc", "OP_KINDS", "COLL_ALLREDUCE", "COLL_REDUCE_SCATTER", "COLL_ALL_GATHER",
-    "vrc_allreduce", "vrc_reduce_scatter", "vrc_all_gather", "reduce_scatter_shape", "chunk_range",
+    "COLL_ALLREDUCE_BUCKETED", "vrc_allreduce", "vrc_reduce_scatter", "vrc_all_gather", "vrc_allreduce_bucketed",
+    "all_reduce", "reduce_scatter", "all_gather", "bucket_count", "raw_allreduce_bucketed",
+    "reduce_scatter_shape", "chunk_range",
     "version", "raw_allreduce", "raw_reduce_scatter", "raw_all_gather", "lib", "VrcError",
     "VRC_INT32", "VRC_FP32", "VRC_FP16", "VRC_BF16", "VRC_SUM", "VRC_RING", "VRC_FUSED", "VRC_RING_CHAINED",
     "VRC_RING_ORDER", "VRC_HD", "VRC_HD_ORDER", "VRC_SELECT", "VRC_TREE", "MODES", "REDUCE_MODES",

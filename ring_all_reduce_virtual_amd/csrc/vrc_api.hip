@@ -130,12 +130,22 @@ bool mode_ok(vrc_mode_t m)
 
 // VRC_SELECT: halving-doubling for power-of-two rank counts and inputs of at
 // most VRC_SELECT_HD_MAX_BYTES per rank (log2 N steps win while launches
-// dominate), else the ring.
-vrc_mode_t resolve_mode(vrc_mode_t m, int n, uint64_t bytes_per_rank)
+// dominate).  For the all-gather at other rank counts, the binomial tree
+// while it saves launches ((N-1) - 2 ceil(log2 N) of them) and each rank's
+// input is at most VRC_SELECT_TREE_BYTES_PER_SAVED_LAUNCH per launch saved
+// (it copies more slabs than the ring).  Else the ring.
+vrc_mode_t resolve_mode(vrc_mode_t m, int n, uint64_t bytes_per_rank, Coll coll)
 {
     if (m != VRC_SELECT) return m;
     const bool pow2 = (n & (n - 1)) == 0;
-    return pow2 && bytes_per_rank <= VRC_SELECT_HD_MAX_BYTES ? VRC_HD : VRC_RING;
+    if (pow2 && bytes_per_rank <= VRC_SELECT_HD_MAX_BYTES) return VRC_HD;
+    if (coll == Coll::AG && !pow2) {
+        int lg = 0;
+        while ((1 << lg) < n) lg++;
+        const int saved = (n - 1) - 2 * lg;
+        if (saved > 0 && bytes_per_rank <= (uint64_t)saved * VRC_SELECT_TREE_BYTES_PER_SAVED_LAUNCH) return VRC_TREE;
+    }
+    return VRC_RING;
 }
 
 // Halving-doubling pairs rank r with r XOR d, so it needs a power of two.
@@ -166,6 +176,9 @@ vrc_status_t vrc_plan(vrc_coll_t coll, const void* const* send, void* const* rec
         rc = vrc_reduce_scatter(send, recv, nranks, count, outer, dtype, VRC_SUM, mode, nullptr);
         break;
     case VRC_COLL_ALL_GATHER: rc = vrc_all_gather(send, recv, nranks, count, outer, dtype, mode, nullptr); break;
+    case VRC_COLL_ALLREDUCE_BUCKETED:
+        rc = vrc_allreduce_bucketed(send, recv, nranks, count, dtype, VRC_SUM, mode, outer, nullptr, 0, nullptr);
+        break;
     }
     g_plan = nullptr;
     *n_ops = plan.n;
@@ -181,7 +194,7 @@ vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nrank
     if (rc) return rc;
     if (op != VRC_SUM || !mode_ok(mode) || mode == VRC_TREE) return VRC_ERR_UNSUPPORTED;
     const uint64_t bytes = (uint64_t)count * (uint64_t)esize(dtype);
-    mode = resolve_mode(mode, nranks, bytes);
+    mode = resolve_mode(mode, nranks, bytes, Coll::AR);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     uint64_t rb[kMaxRanks];
     for (int r = 0; r < nranks; r++) rb[r] = bytes;
@@ -189,6 +202,43 @@ vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nrank
     if (rc) return rc;
     if (count == 0) return VRC_OK;
     return run(Coll::AR, mode, dtype, send, recv, nranks, count, 1, (hipStream_t)stream);
+}
+
+vrc_status_t vrc_allreduce_bucketed(const void* const* send, void* const* recv, int nranks, size_t count,
+                                    vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, size_t bucket,
+                                    const vrc_event_t* ready, int nready, vrc_stream_t stream)
+{
+    vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
+    if (rc) return rc;
+    if (op != VRC_SUM || !mode_ok(mode) || mode == VRC_TREE) return VRC_ERR_UNSUPPORTED;
+    if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
+    if (bucket == 0) return VRC_ERR_INVALID_ARG;
+    const uint64_t nb = count == 0 ? 0 : (count - 1) / bucket + 1;
+    if (ready ? (nready < 0 || (uint64_t)nready != nb) : nready != 0) return VRC_ERR_INVALID_ARG;
+    if (ready)
+        for (uint64_t k = 0; k < nb; k++)
+            if (!ready[k]) return VRC_ERR_INVALID_ARG;
+    const int E = esize(dtype);
+    uint64_t rb[kMaxRanks];
+    for (int r = 0; r < nranks; r++) rb[r] = (uint64_t)count * E;
+    rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, true);
+    if (rc) return rc;
+    const void* xs[kMaxRanks];
+    void* ys[kMaxRanks];
+    for (uint64_t k = 0; k < nb; k++) {
+        const uint64_t off = k * bucket, len = count - off < bucket ? count - off : bucket;
+        if (ready && !g_plan) {
+            const hipError_t e = hipStreamWaitEvent((hipStream_t)stream, (hipEvent_t)ready[k], 0);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        for (int r = 0; r < nranks; r++) {
+            xs[r] = static_cast<const char*>(send[r]) + off * E;
+            ys[r] = static_cast<char*>(recv[r]) + off * E;
+        }
+        rc = run(Coll::AR, resolve_mode(mode, nranks, len * E, Coll::AR), dtype, xs, ys, nranks, len, 1, (hipStream_t)stream);
+        if (rc) return rc;
+    }
+    return VRC_OK;
 }
 
 vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int nranks, size_t count,
@@ -199,7 +249,7 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
     if (rc) return rc;
     if (op != VRC_SUM || !mode_ok(mode) || mode == VRC_TREE) return VRC_ERR_UNSUPPORTED;
     const int E = esize(dtype);
-    mode = resolve_mode(mode, nranks, (uint64_t)count * E);
+    mode = resolve_mode(mode, nranks, (uint64_t)count * E, Coll::RS);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     if (outer > 1 && (count / outer) % (uint64_t)nranks != 0) return VRC_ERR_INVALID_ARG;
@@ -226,7 +276,7 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
     if (rc) return rc;
     if (!mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
     const int E = esize(dtype);
-    mode = resolve_mode(mode, nranks, (uint64_t)count * E);
+    mode = resolve_mode(mode, nranks, (uint64_t)count * E, Coll::AG);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     uint64_t rb[kMaxRanks];

@@ -27,17 +27,17 @@ def orc():
 
 
 def picked(vrc, coll, xs, ys, count, outer, dtype):
-    """'hd' or 'ring', from the launch plan of the same call."""
+    """'hd', 'ring' or 'tree', from the launch plan of the same call."""
     send = [x.data_ptr() for x in xs]
     recv = [y.data_ptr() for y in ys]
     got = vrc.plan(coll, send, recv, count, outer, CODES[dtype], vrc.VRC_SELECT)
-    for name, code in (("hd", vrc.VRC_HD), ("ring", vrc.VRC_RING)):
+    for name, code in (("hd", vrc.VRC_HD), ("ring", vrc.VRC_RING), ("tree", vrc.VRC_TREE)):
         try:
             if vrc.plan(coll, send, recv, count, outer, CODES[dtype], code) == got:
                 return name
-        except vrc.VrcError:  # halving-doubling refuses rank counts that are not powers of two
-            pass
-    raise AssertionError("VRC_SELECT planned neither halving-doubling nor the ring")
+        except vrc.VrcError:  # halving-doubling refuses rank counts that are not powers of two, the
+            pass              # reduce collectives the tree
+    raise AssertionError("VRC_SELECT planned none of halving-doubling, the ring and the tree")
 
 
 def expected_algorithm(n, nbytes):
@@ -104,3 +104,20 @@ def test_select_halves(vrc, orc, n):
     for c in range(n):
         assert_bitwise(workloads.to_numpy(rs[c]), want[c], f"select rs n={n} ({alg}) chunk {c}")
         assert_bitwise(workloads.to_numpy(ag[c]), gathered[c], f"select ag n={n} rank {c}")
+
+
+@pytest.mark.parametrize("n,count,alg", [(12, 1000, "tree"), (14, 300000, "tree"), (12, 300000, "ring"),
+                                         (10, 70000, "ring")])
+def test_select_all_gather_tree(vrc, orc, n, count, alg):
+    """The all-gather at rank counts that are not powers of two takes the
+    binomial tree while it saves launches and the input is small (at most
+    128 KiB per launch saved); its bits are the tree oracle's."""
+    print(f"select all-gather n={n} count={count} ({alg})", flush=True)
+    xs = workloads.random_ranks(n, count, "fp16", seed=95 + n, device=DEV)
+    ys = [torch.empty(n * count, dtype=xs[0].dtype, device=DEV) for _ in range(n)]
+    assert picked(vrc, vrc.COLL_ALL_GATHER, xs, ys, count, 1, "fp16") == alg
+    vrc.vrc_all_gather(xs, recv=ys, mode="select")
+    torch.cuda.synchronize()
+    want = (orc.tree_all_gather if alg == "tree" else orc.ring_all_gather)(host(xs), "fp16")
+    for r in range(n):
+        assert_bitwise(workloads.to_numpy(ys[r]), want[r], f"select all-gather n={n} ({alg}) rank {r}")

@@ -266,6 +266,81 @@ def test_tree_is_an_all_gather_mode_only():
         assert e.value.status == vrc.VRC_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("mode,per_bucket", [(vrc.VRC_FUSED, 1), (vrc.VRC_RING, 14), (vrc.VRC_HD, 6),
+                                               (vrc.VRC_RING_ORDER, 1)])
+@pytest.mark.parametrize("count,bucket", [(1000, 300), (1000, 1000), (1000, 4096), (999, 111)])
+def test_bucketed_plan_runs_each_bucket_on_its_slice(mode, per_bucket, count, bucket):
+    """One all-reduce per bucket, in bucket order, each touching only its
+    bucket's slice of every rank buffer; the ring and halving-doubling ones
+    partition the bucket as a buffer of its own."""
+    n = 8
+    send, recv = buffers(n)
+    ops, launches = vrc.plan(vrc.COLL_ALLREDUCE_BUCKETED, send, recv, count, bucket, vrc.VRC_FP32, mode)
+    nb = vrc.bucket_count(count, bucket)
+    assert launches == nb * per_bucket
+    for k in range(nb):
+        lo, hi = k * bucket * E, min(count, (k + 1) * bucket) * E
+        want, _ = vrc.plan(vrc.COLL_ALLREDUCE, [a + lo for a in send], [a + lo for a in recv], (hi - lo) // E, 1,
+                           vrc.VRC_FP32, mode)
+        got = [dict(o, launch=o["launch"] - k * per_bucket) for o in ops if k * per_bucket <= o["launch"] <
+               (k + 1) * per_bucket]
+        assert got == want
+        for o in got:
+            for key in ("a", "b", "d"):
+                if o[key]:
+                    rank, off = owner(o[key], send if o[key] < RECV_BASE else recv)
+                    assert lo <= off < hi
+
+
+def test_bucketed_plan_selects_per_bucket():
+    """VRC_SELECT resolves each bucket by its own size: 8 ranks, 80 MiB fp32
+    per rank in 40 MiB buckets take halving-doubling (6 launches each);
+    the same buffers in one bucket take the ring (14)."""
+    n, count = 8, 20 << 20
+    send, recv = wide_buffers(n)
+    _, halves = vrc.plan(vrc.COLL_ALLREDUCE_BUCKETED, send, recv, count, count // 2, vrc.VRC_FP32, vrc.VRC_SELECT)
+    _, whole = vrc.plan(vrc.COLL_ALLREDUCE_BUCKETED, send, recv, count, count, vrc.VRC_FP32, vrc.VRC_SELECT)
+    assert (halves, whole) == (12, 14)
+
+
+def test_bucketed_plan_validates():
+    send, recv = buffers(4)
+    for bucket, mode, status in ((0, vrc.VRC_FUSED, vrc.VRC_ERR_INVALID_ARG),
+                                 (10, vrc.VRC_TREE, vrc.VRC_ERR_UNSUPPORTED)):
+        with pytest.raises(vrc.VrcError) as e:
+            vrc.plan(vrc.COLL_ALLREDUCE_BUCKETED, send, recv, 100, bucket, vrc.VRC_FP32, mode)
+        assert e.value.status == status
+    send3, recv3 = buffers(3)
+    with pytest.raises(vrc.VrcError) as e:
+        vrc.plan(vrc.COLL_ALLREDUCE_BUCKETED, send3, recv3, 100, 10, vrc.VRC_FP32, vrc.VRC_HD)
+    assert e.value.status == vrc.VRC_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("n,count,want", [
+    (12, 1000, "tree"),                        # saves 11 - 8 = 3 launches
+    (12, 3 * (128 << 10) // 2, "tree"),        # exactly 3 x 128 KiB of fp16 per rank
+    (12, 3 * (128 << 10) // 2 + 1, "ring"),
+    (10, (128 << 10) // 2, "tree"),            # saves one launch: up to 128 KiB
+    (10, (128 << 10) // 2 + 1, "ring"),
+    (15, 6 * (128 << 10) // 2, "tree"),
+    (9, 100, "ring"), (7, 100, "ring"), (6, 100, "ring"), (3, 100, "ring"),  # no launch saved
+    (8, 100, "hd"), (16, 5000, "hd"),          # powers of two: halving-doubling
+])
+def test_select_all_gather_follows_the_tree_rule(n, count, want):
+    """VRC_SELECT for the all-gather: the binomial tree at rank counts that
+    are not powers of two while it saves L = (N-1) - 2 ceil(log2 N) launches
+    and each rank's input holds at most L x 128 KiB; the reduce collectives
+    never take the tree."""
+    send, recv = wide_buffers(n)
+    mode = {"tree": vrc.VRC_TREE, "ring": vrc.VRC_RING, "hd": vrc.VRC_HD}[want]
+    got = vrc.plan(vrc.COLL_ALL_GATHER, send, recv, count, 1, vrc.VRC_FP16, vrc.VRC_SELECT)
+    assert got == vrc.plan(vrc.COLL_ALL_GATHER, send, recv, count, 1, vrc.VRC_FP16, mode)
+    if want == "tree":
+        for coll in (vrc.COLL_ALLREDUCE, vrc.COLL_REDUCE_SCATTER):
+            assert vrc.plan(coll, send, recv, count, 1, vrc.VRC_FP16, vrc.VRC_SELECT) == \
+                vrc.plan(coll, send, recv, count, 1, vrc.VRC_FP16, vrc.VRC_RING)
+
+
 def test_plan_validates_like_the_call():
     send, recv = buffers(3)
     with pytest.raises(vrc.VrcError):
