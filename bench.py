@@ -543,6 +543,40 @@ def run_overlap_buckets(steps: int, mode: str, torch, vrc, workloads, only=None)
     return 0
 
 
+def run_profile_case(case: str, steps: int, torch, vrc, workloads) -> int:
+    """`steps` calls of one workload in one mode, each after an untimed 1 GiB
+    write (the suite's cache flush), for rocprofv3 counter passes: the kernel
+    of interest is every dispatch whose name it bears.  `case` is
+    WORKLOAD[@COUNT]:MODE (COUNT overrides the per-rank element count, as the
+    sweep sizes of a workload)."""
+    dev = "cuda:0"
+    name, mode = case.split(":")
+    count = None
+    if "@" in name:
+        name, count = name.split("@")
+    w = workloads.WORKLOADS[name]
+    if count is not None:
+        w = w.with_count(int(count))
+    xs = workloads.make_inputs(w, dev)
+    if w.collective == "allreduce":
+        outs = [torch.empty_like(x) for x in xs]
+        call = lambda: vrc.vrc_allreduce(xs, recv=outs, mode=mode)  # noqa: E731
+    elif w.collective == "reduce_scatter":
+        outs = vrc.vrc_reduce_scatter(xs, dim=w.dim)
+        call = lambda: vrc.vrc_reduce_scatter(xs, recv=outs, dim=w.dim, mode=mode)  # noqa: E731
+    else:
+        outs = vrc.vrc_all_gather(xs, dim=w.dim)
+        call = lambda: vrc.vrc_all_gather(xs, recv=outs, dim=w.dim, mode=mode)  # noqa: E731
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        flush.zero_()
+        call()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_case": case, "calls": steps, "alg_bytes_per_call": suite_bytes(w, mode)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -566,6 +600,8 @@ def main() -> int:
                     help="time operands off their destination's grid beside their aligned twins")
     ap.add_argument("--ag-sweep", action="store_true",
                     help="time the all-gather algorithms (ring, recursive doubling, tree, fused) by size")
+    ap.add_argument("--profile-case", default=None,
+                    help="WORKLOAD[@COUNT]:MODE -- run only this collective `--steps` times (for counter passes)")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB (known HBM traffic: 1 GiB read, 1 GiB "
                          "written per launch), for calibrating rocprofv3 byte counters")
@@ -591,6 +627,8 @@ def main() -> int:
         return run_offsets(args.steps, torch, vrc, workloads)
     if args.ag_sweep:
         return run_ag_sweep(args.steps, torch, vrc, workloads)
+    if args.profile_case:
+        return run_profile_case(args.profile_case, args.steps, torch, vrc, workloads)
     if args.overlap and args.buckets:
         only = tuple(int(v) for v in args.bucket_case.split(",")) if args.bucket_case else None
         return run_overlap_buckets(args.steps, args.mode, torch, vrc, workloads, only)

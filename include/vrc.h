@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define VRC_VERSION 103 /* 1.0.3: vrc_allreduce_bucketed */
+#define VRC_VERSION 104 /* 1.0.4: realigned fused all-reduce launches in vrc_plan */
 #define VRC_MAX_RANKS 16
 
 struct ihipStream_t;
@@ -294,7 +294,10 @@ typedef enum {
     VRC_OP_RING_ORDER_ALLREDUCE = 8, /* VRC_RING_ORDER */
     VRC_OP_RING_ORDER_REDUCE_SCATTER = 9,
     VRC_OP_BUTTERFLY_ALLREDUCE = 10, /* VRC_HD_ORDER */
-    VRC_OP_BUTTERFLY_REDUCE_SCATTER = 11
+    VRC_OP_BUTTERFLY_REDUCE_SCATTER = 11,
+    VRC_OP_FUSED_ALLREDUCE_REALIGNED = 12,   /* VRC_FUSED, outputs on different 128-byte offsets */
+    VRC_OP_BUTTERFLY_ALLREDUCE_REALIGNED = 13, /* VRC_HD_ORDER, outputs on different 128-byte offsets */
+    VRC_OP_RING_ORDER_ALLREDUCE_REALIGNED = 14 /* VRC_RING_ORDER, outputs on different 128-byte offsets */
 } vrc_op_kind_t;
 
 typedef struct {

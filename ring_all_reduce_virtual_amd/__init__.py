@@ -53,7 +53,7 @@ class VrcError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 103  # VRC_VERSION of include/vrc.h that these mirrors follow
+ABI_VERSION = 104  # VRC_VERSION of include/vrc.h that these mirrors follow
 
 
 class OpDesc(C.Structure):
@@ -67,7 +67,9 @@ class OpDesc(C.Structure):
 COLL_ALLREDUCE, COLL_REDUCE_SCATTER, COLL_ALL_GATHER, COLL_ALLREDUCE_BUCKETED = 0, 1, 2, 3
 OP_KINDS = {0: "add", 1: "copy", 2: "fused_allreduce", 3: "fused_reduce_scatter", 4: "fused_all_gather",
             5: "chain_allreduce", 6: "chain_reduce_scatter", 7: "chain_all_gather", 8: "ring_order_allreduce",
-            9: "ring_order_reduce_scatter", 10: "butterfly_allreduce", 11: "butterfly_reduce_scatter"}
+            9: "ring_order_reduce_scatter", 10: "butterfly_allreduce", 11: "butterfly_reduce_scatter",
+            12: "fused_allreduce_realigned", 13: "butterfly_allreduce_realigned",
+            14: "ring_order_allreduce_realigned"}
 
 
 def _load():

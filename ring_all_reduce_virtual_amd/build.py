@@ -51,6 +51,21 @@ def build_c_check(verbose: bool = False) -> str:
     return C_CHECK_BIN
 
 
+CVT_CHECK_SRC = os.path.join(ROOT, "tests", "c", "bf16_cvt_check.hip")
+CVT_CHECK_BIN = os.path.join(ROOT, "tests", "c", "bf16_cvt_check")
+
+
+def build_cvt_check(verbose: bool = False) -> str:
+    """Build the exhaustive check of the bf16 conversion the kernels use
+    (tests/c/bf16_cvt_check.hip), with the library's compiler flags."""
+    flags = [f for f in FLAGS if f not in ("-fPIC", "-fvisibility=hidden")]
+    cmd = [HIPCC, *flags, "-o", CVT_CHECK_BIN, CVT_CHECK_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return CVT_CHECK_BIN
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
     """Compile every source to an object (in parallel) and link libvrc.so."""
     os.makedirs(OBJDIR, exist_ok=True)
@@ -86,4 +101,5 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
 if __name__ == "__main__":
     build(verbose=True)
     build_c_check(verbose=True)
+    build_cvt_check(verbose=True)
     sys.exit(0)

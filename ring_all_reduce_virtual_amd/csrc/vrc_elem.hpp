@@ -52,6 +52,15 @@ __device__ __forceinline__ void st16(char* p, u32x4 v)
     else *g = v;
 }
 
+// Bytes 4Q + s .. 4Q + s + 15 (s < 4) of the eight dwords w, as one vector:
+// dword i is funnelled from w[Q + i] and w[Q + i + 1] by v_alignbyte.
+template <int Q>
+__device__ __forceinline__ u32x4 funnel(const unsigned* w, uint32_t s)
+{
+    return u32x4{__builtin_amdgcn_alignbyte(w[Q + 1], w[Q], s), __builtin_amdgcn_alignbyte(w[Q + 2], w[Q + 1], s),
+                 __builtin_amdgcn_alignbyte(w[Q + 3], w[Q + 2], s), __builtin_amdgcn_alignbyte(w[Q + 4], w[Q + 3], s)};
+}
+
 // Compiler barrier.  A load after it is issued even when this lane has just
 // stored the value it reads (the compiler would otherwise reuse the stored
 // register): the memory-faithful ring chains read every partial back from
@@ -129,14 +138,18 @@ struct BF16 {
     static constexpr int ESZ = 2, VEC = 8;
     // bfloat16 is the upper half of an IEEE binary32.
     __device__ static A widen(S s) { return __uint_as_float((uint32_t)s << 16); }
-    // Round to nearest even on the 16 discarded bits; NaN stays a quiet NaN.
-    // Both results are computed and one selected, so no lane branches.
-    __device__ static S narrow(A a)
+    // Round to nearest even on the 16 discarded bits; a NaN keeps its sign
+    // and upper payload bits and becomes quiet (bit 6 of the half set).  The
+    // target's conversion (v_cvt_pk_bf16_f32, two values per instruction)
+    // does exactly that in this library's floating-point mode (denormals
+    // kept): tests/c/bf16_cvt_check.hip compares it with the bit-level
+    // rounding on all 2^32 inputs.
+    __device__ static S narrow(A a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
+    __device__ static uint32_t narrow2(A lo, A hi)
     {
-        const uint32_t u = __float_as_uint(a);
-        const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-        const uint32_t quiet_nan = (u >> 16) | 0x40u;
-        return (S)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded);
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
     }
     __device__ static A add(A a, A b) { return a + b; }
     __device__ static void unpack(u32x4 v, A* a)
@@ -150,10 +163,7 @@ struct BF16 {
     }
     __device__ static u32x4 pack(const A* a)
     {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) w[i] = (uint32_t)narrow(a[2 * i]) | ((uint32_t)narrow(a[2 * i + 1]) << 16);
-        return u32x4{w[0], w[1], w[2], w[3]};
+        return u32x4{narrow2(a[0], a[1]), narrow2(a[2], a[3]), narrow2(a[4], a[5]), narrow2(a[6], a[7])};
     }
 };
 

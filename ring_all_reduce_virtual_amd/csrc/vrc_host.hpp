@@ -93,6 +93,7 @@ struct Tuning {
     int fused_block;          // 0: size policy; else lanes per fused all-reduce workgroup (64 or 256)
     int chain_block;          // 0: policy; else lanes per single-launch ring all-reduce workgroup (64 or 256)
     int step_block;           // 0: size policy; else lanes per step workgroup (64, with one vector per lane, or 256)
+    int realign;              // 1: outputs on different 128-byte offsets take the realigned fused kernel; 0: never
 };
 
 inline const Tuning& tuning()
@@ -102,7 +103,7 @@ inline const Tuning& tuning()
                              env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 0, 1, 8),
                              env_int("VRC_STEP_NT", -1, 0, 2), env_int("VRC_STEP_UNROLL", 0, 1, 2),
                              env_int("VRC_FUSED_BLOCK", 0, 64, 256), env_int("VRC_CHAIN_BLOCK", 0, 64, 256),
-                             env_int("VRC_STEP_BLOCK", 0, 64, 256)};
+                             env_int("VRC_STEP_BLOCK", 0, 64, 256), env_int("VRC_REALIGN", 1, 0, 1)};
     return t;
 }
 
@@ -190,6 +191,21 @@ inline FusedShape fused_ar_shape(uint64_t bytes_moved, int n, bool outputs_share
     while (2 * u <= s.unroll && 2 * u <= umax && (s.block != 64 || 2 * u * n <= 32)) u *= 2;
     s.unroll = u;
     return s;
+}
+
+// Vectors per rank per lane of the realigned fused all-reduce, one kernel
+// per rank count: the largest U <= 8 with U x N <= 32, at least 2 (a group
+// of U tiles re-reads 128 bytes of the next group, 1/(8U) of its reads).
+constexpr int realign_unroll(int n) { return 8 * n <= 32 ? 8 : (4 * n <= 32 ? 4 : 2); }
+
+// Workgroups per CU of the realigned fused all-reduce: 64 / (U x N) rounded
+// down to a power of two, at least 1.
+inline int realign_blocks_per_cu(int n)
+{
+    if (tuning().fused_blocks_per_cu) return tuning().fused_blocks_per_cu;
+    int b = 1;
+    while (2 * b * realign_unroll(n) * n <= 64) b *= 2;
+    return b;
 }
 
 // Launch shape of a ring or halving-doubling step of `nops` per-rank

@@ -314,6 +314,119 @@ __global__ __launch_bounds__(B) void k_fused_allreduce(FusedArArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Fused all-reduce for outputs on different 128-byte offsets (one-wave
+// workgroups, no output overlapping an input).  The loads follow one
+// reference grid; output r is stored `shift[r]` bytes later, on its own
+// 128-byte grid, so every store of the main loop fills whole write blocks
+// whatever the output offsets.  A wave folds U tiles of the reference grid
+// plus the 128 bytes after them into LDS, then reads each output's 16 bytes
+// per lane back at that output's shift.  The 128 bytes are read again by the
+// next group's wave (1/(8U) more input reads).
+//
+// Stores outside the groups (the 128 bytes before every output's first
+// boundary, the vectors after the last group, the scalar head and tail) go
+// to every output at the reference offsets.  Where they overlap a group's
+// stores both write the same sum, and no input is overwritten: inputs and
+// outputs are disjoint.
+// ---------------------------------------------------------------------------
+struct FusedRealignArgs {
+    const char* src[kMaxRanks];
+    char* dst[kMaxRanks];
+    uint32_t shift[kMaxRanks];  // bytes from the body start to output r's next 128-byte boundary, < 128
+    uint64_t groups;            // groups of U tiles whose next 128 bytes lie in the body
+    RowSplit g;
+};
+
+// Lane `lane`'s 16 bytes of U tiles of one output, d bytes past the sums
+// staged in LDS (d < 128, (d / 4) % 4 == Q).
+template <int Q, int U>
+__device__ __forceinline__ void shifted(u32x4* out, const u32x4* sum, uint64_t lane, uint32_t d)
+{
+    const uint64_t k0 = lane + d / 16;  // + u * 64 + 1 <= U * 64 + 7
+    const uint32_t s = d % 4;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const u32x4 lo = sum[u * 64 + k0], hi = sum[u * 64 + k0 + 1];
+        const unsigned w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        out[u] = funnel<Q>(w, s);
+    }
+}
+
+template <class T, int N, int U, bool NT, class Fold>
+__global__ __launch_bounds__(64) void k_fused_allreduce_realigned(FusedRealignArgs a)
+{
+    constexpr uint64_t W = 64;
+    constexpr uint64_t E = T::ESZ;
+    constexpr uint64_t X = 8;  // 16-byte vectors past a group: 128 bytes
+    __shared__ u32x4 sum[U * W + X];
+    const uint64_t lane = threadIdx.x;
+    const uint64_t body = a.g.head * E;
+
+    for (uint64_t g = blockIdx.x; g < a.groups; g += gridDim.x) {
+        const uint64_t v0 = g * U * W;
+        u32x4 in[U + 1][N];
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int r = 0; r < N; r++) in[u][r] = ld16<NT>(a.src[r] + body + (v0 + u * W + lane) * 16);
+#pragma unroll
+        for (int r = 0; r < N; r++) in[U][r] = ld16<NT>(a.src[r] + body + (v0 + U * W + (lane % X)) * 16);
+        issue_loads_first();
+#pragma unroll
+        for (int u = 0; u < U; u++) sum[u * W + lane] = Fold::template vec<T, N>(in[u]);
+        const u32x4 next = Fold::template vec<T, N>(in[U]);
+        if (lane < X) sum[U * W + lane] = next;
+        __syncthreads();
+        // Every output's vectors first, then all U * N stores back to back: a
+        // register that still feeds a store in flight is not overwritten
+        // before that store completes, so the stores must not share registers.
+        u32x4 out[N][U];
+#pragma unroll
+        for (int r = 0; r < N; r++) {
+            const uint32_t d = a.shift[r];
+            switch ((d / 4) % 4) {  // the same for every lane: one scalar branch per output
+            case 0: shifted<0, U>(out[r], sum, lane, d); break;
+            case 1: shifted<1, U>(out[r], sum, lane, d); break;
+            case 2: shifted<2, U>(out[r], sum, lane, d); break;
+            default: shifted<3, U>(out[r], sum, lane, d); break;
+            }
+        }
+        issue_loads_first();
+#pragma unroll
+        for (int r = 0; r < N; r++)
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                st16<NT>(a.dst[r] + body + (v0 + u * W + lane) * 16 + a.shift[r], out[r][u]);
+        __syncthreads();
+    }
+
+    // The first X vectors and those after the last group, at the reference
+    // offsets (groups >= 1, so the two ranges are disjoint).
+    const uint64_t rest0 = a.groups * U * W;
+    const uint64_t nrest = X + (a.g.nvb - rest0);
+    for (uint64_t k = (uint64_t)blockIdx.x * W + lane; k < nrest; k += (uint64_t)gridDim.x * W) {
+        const uint64_t v = k < X ? k : rest0 + (k - X);
+        u32x4 in[N];
+#pragma unroll
+        for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
+        const u32x4 s = Fold::template vec<T, N>(in);
+#pragma unroll
+        for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, s);
+    }
+
+    const uint64_t ns = a.g.head + a.g.tail;
+    for (uint64_t k = (uint64_t)blockIdx.x * W + lane; k < ns; k += (uint64_t)gridDim.x * W) {
+        const uint64_t i = (k < a.g.head) ? k : a.g.head + a.g.nvb * T::VEC + (k - a.g.head);
+        typename T::S in[N];
+#pragma unroll
+        for (int r = 0; r < N; r++) in[r] = load_s<T>(a.src[r] + i * E);
+        const typename T::S s = Fold::template scalar<T, N>(in);
+#pragma unroll
+        for (int r = 0; r < N; r++) store_s<T>(a.dst[r] + i * E, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fused reduce-scatter: blockIdx.y = chunk c.  Output c is the rank-order
 // fold of chunk c over all N inputs, rounded once.
 // ---------------------------------------------------------------------------
@@ -595,6 +708,125 @@ __global__ __launch_bounds__(B) void k_ring_chain_allreduce(ChainArgs a)
         for (uint64_t j = lane; j < ns; j += W) {
             const uint64_t col = (j < k.g.head) ? j : k.g.head + k.g.nvb * T::VEC + (j - k.g.head);
             chain_block<N, MEM, ScalarIO<T>>(in, out, (k.off + col) * E);
+        }
+    }
+}
+
+// Ring-order all-reduce for outputs on different 128-byte offsets (one-wave
+// workgroups, no output in place): the realigned stores of the fused
+// kernel, chunk by chunk.  A group of U tiles lies inside one chunk, whose
+// rank rotation it takes, with the 128 bytes after it; chunk c's groups are
+// [group0[c], group0[c+1]).  The vectors of a chunk outside its groups (the
+// first X and those after its last group, or all of them in a chunk too
+// small for a group) form rest tiles [rest0[c], rest0[c+1]), stored at the
+// reference offsets like the tile kernel's.
+struct RingOrderRealignArgs {
+    const char* src[kMaxRanks];
+    char* dst[kMaxRanks];
+    ChainChunk ch[kMaxRanks];
+    uint64_t group0[kMaxRanks + 1];
+    uint64_t rest0[kMaxRanks + 1];       // in tiles of 64 vectors
+    uint8_t shift[kMaxRanks][kMaxRanks];  // [c][r]: bytes from chunk c's body to output r's next 128-byte boundary
+};
+
+template <class T, int N, int U, bool NT>
+__global__ __launch_bounds__(64) void k_ring_order_allreduce_realigned(RingOrderRealignArgs a)
+{
+    constexpr uint64_t W = 64;
+    constexpr uint64_t E = T::ESZ;
+    constexpr uint64_t X = 8;
+    __shared__ u32x4 sum[U * W + X];
+    const uint64_t lane = threadIdx.x;
+    const char* in[N];
+    char* out[N];
+    uint32_t sh[N];
+
+    // The chunk's rank rotation, offsets and shifts are reloaded only when a
+    // wave's next group lies in another chunk.
+    int cur = -1;
+    uint64_t body = 0, first = 0;
+    for (uint64_t g = blockIdx.x; g < a.group0[N]; g += gridDim.x) {
+        const int c = __builtin_amdgcn_readfirstlane(range_of<N>(g, a.group0));
+        if (c != cur) {
+            cur = c;
+            body = (a.ch[c].off + a.ch[c].g.head) * E;
+            first = a.group0[c];
+#pragma unroll
+            for (int t = 0; t < N; t++) {
+                in[t] = a.src[(c + t) % N];
+                sh[t] = a.shift[c][t];
+            }
+        }
+        const uint64_t v0 = (g - first) * U * W;
+        u32x4 x[U + 1][N];
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int t = 0; t < N; t++) x[u][t] = ld16<NT>(in[t] + body + (v0 + u * W + lane) * 16);
+#pragma unroll
+        for (int t = 0; t < N; t++) x[U][t] = ld16<NT>(in[t] + body + (v0 + U * W + (lane % X)) * 16);
+        issue_loads_first();
+        // The ring's order: rank c's value, then ranks c+1, ..., c+N-1, each
+        // partial rounded to the storage type.
+#pragma unroll
+        for (int u = 0; u <= U; u++) {
+            u32x4 p = x[u][0];
+#pragma unroll
+            for (int t = 1; t < N; t++) p = add_v<T>(p, x[u][t]);
+            if (u < U) sum[u * W + lane] = p;
+            else if (lane < X) sum[U * W + lane] = p;
+        }
+        __syncthreads();
+        u32x4 o[N][U];
+#pragma unroll
+        for (int r = 0; r < N; r++) {
+            const uint32_t d = sh[r];
+            switch ((d / 4) % 4) {
+            case 0: shifted<0, U>(o[r], sum, lane, d); break;
+            case 1: shifted<1, U>(o[r], sum, lane, d); break;
+            case 2: shifted<2, U>(o[r], sum, lane, d); break;
+            default: shifted<3, U>(o[r], sum, lane, d); break;
+            }
+        }
+        issue_loads_first();
+#pragma unroll
+        for (int r = 0; r < N; r++)
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                st16<NT>(a.dst[r] + body + (v0 + u * W + lane) * 16 + sh[r], o[r][u]);
+        __syncthreads();
+    }
+
+    for (uint64_t t = blockIdx.x; t < a.rest0[N]; t += gridDim.x) {
+        const int c = __builtin_amdgcn_readfirstlane(range_of<N>(t, a.rest0));
+        const ChainChunk& k = a.ch[c];
+        const uint64_t groups = a.group0[c + 1] - a.group0[c];
+        const uint64_t nrest = groups ? X + (k.g.nvb - groups * U * W) : k.g.nvb;
+        const uint64_t kk = (t - a.rest0[c]) * W + lane;
+        if (kk >= nrest) continue;
+        const uint64_t v = (groups == 0 || kk < X) ? kk : groups * U * W + (kk - X);
+#pragma unroll
+        for (int q = 0; q < N; q++) {
+            in[q] = a.src[(c + q) % N];
+            out[q] = a.dst[(c + q) % N];
+        }
+        chain_block<N, false, VecIO<T, NT>>(in, out, (k.off + k.g.head) * E + v * 16);
+    }
+
+    // Scalar head and tail elements: one wave per chunk.
+    for (uint64_t cw = blockIdx.x; cw < (uint64_t)N; cw += gridDim.x) {
+        const int c = __builtin_amdgcn_readfirstlane((int)cw);
+        const ChainChunk& k = a.ch[c];
+        const uint64_t ns = k.g.head + k.g.tail;
+        if (lane >= ns) continue;
+#pragma unroll
+        for (int q = 0; q < N; q++) {
+            in[q] = a.src[(c + q) % N];
+            out[q] = a.dst[(c + q) % N];
+        }
+        for (uint64_t j = lane; j < ns; j += W) {
+            const uint64_t col = (j < k.g.head) ? j : k.g.head + k.g.nvb * T::VEC + (j - k.g.head);
+            chain_block<N, false, ScalarIO<T>>(in, out, (k.off + col) * E);
         }
     }
 }

@@ -254,6 +254,52 @@ struct Launch {
         }
     }
 
+    // The fused all-reduce with each output stored on its own 128-byte grid
+    // (groups >= 1 groups of realign_unroll(n) tiles, no output in place).
+    template <class Fold>
+    static vrc_status_t fused_allreduce_realigned(const vrc::FusedArArgs& f, int n, uint64_t count, uint64_t groups,
+                                                  int cus, hipStream_t st)
+    {
+        constexpr bool butterfly = std::is_same<Fold, vrc::Butterfly>::value;
+        vrc::FusedRealignArgs a = {};
+        for (int r = 0; r < kMaxRanks; r++) {
+            a.src[r] = f.src[r];
+            a.dst[r] = f.dst[r];
+        }
+        a.g = f.g;
+        a.groups = groups;
+        const uintptr_t body = f.g.head * E;
+        for (int r = 0; r < n; r++)
+            a.shift[r] = (uint32_t)((kGridAlign - ((uintptr_t)f.dst[r] + body) % kGridAlign) % kGridAlign);
+        const int U = realign_unroll(n);
+        const dim3 grid(grid_x(cus, groups * 64, 1, realign_blocks_per_cu(n), 64));
+        if (g_plan)
+            return plan_single(butterfly ? VRC_OP_BUTTERFLY_ALLREDUCE_REALIGNED : VRC_OP_FUSED_ALLREDUCE_REALIGNED,
+                               count, grid, 64, U);
+#define VRC_REALIGNED(K)                                                                                           \
+    hipLaunchKernelGGL((vrc::k_fused_allreduce_realigned<T, K, realign_unroll(K), true, Fold>), grid, dim3(64), 0, \
+                       st, a)
+        if constexpr (butterfly) {
+            switch (n) {
+            case 2: VRC_REALIGNED(2); break;
+            case 4: VRC_REALIGNED(4); break;
+            case 8: VRC_REALIGNED(8); break;
+            case 16: VRC_REALIGNED(16); break;
+            default: return VRC_ERR_INVALID_ARG;
+            }
+        } else {
+            switch (n) {
+#define VRC_CASE(K) \
+    case K: VRC_REALIGNED(K); break;
+                VRC_FOR_N(VRC_CASE)
+#undef VRC_CASE
+            default: return VRC_ERR_INVALID_ARG;
+            }
+        }
+#undef VRC_REALIGNED
+        return check_launch();
+    }
+
     template <class Fold = vrc::RankFold>
     static vrc_status_t fused_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
                                         hipStream_t st)
@@ -278,6 +324,16 @@ struct Launch {
             if (out[r] % kGridAlign != ref % kGridAlign) share = false;
         const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
         const FusedShape sh = fused_ar_shape(2 * (uint64_t)n * count * E, n, share);
+        if (!share && sh.block == 64 && tuning().realign) {
+            // Outputs on different 128-byte offsets: store each on its own
+            // grid, unless an output is its input (the realigned stores run
+            // up to 127 bytes ahead of the reads).
+            bool in_place = false;
+            for (int r = 0; r < n; r++) in_place = in_place || x[r] == y[r];
+            const uint64_t gv = (uint64_t)realign_unroll(n) * 64;
+            const uint64_t groups = a.g.nvb >= gv + 8 ? (a.g.nvb - 8) / gv : 0;
+            if (!in_place && groups > 0) return fused_allreduce_realigned<Fold>(a, n, count, groups, cus, st);
+        }
         const dim3 grid(grid_x(cus, work, 1, sh.blocks_per_cu, sh.block));
         if (g_plan)
             return plan_single(std::is_same<Fold, vrc::Butterfly>::value ? VRC_OP_BUTTERFLY_ALLREDUCE
@@ -637,6 +693,18 @@ struct Launch {
             a.ch[c] = {off, 1, len, 0, split_rows(write_ref(out, n), len, E)};
             a.tile0[c + 1] = a.tile0[c] + (a.ch[c].g.nvb + 63) / 64;
         }
+        if (!MEM && tuning().realign && chain_ar_shape(MEM, n).block == 64) {
+            // Outputs on different 128-byte offsets, none in place: every
+            // output stored on its own grid (the chunks start at the same
+            // element of every buffer, so one test covers all chunks).
+            bool share = true, in_place = false;
+            for (int r = 0; r < n; r++) {
+                share = share && (uintptr_t)y[r] % kGridAlign == (uintptr_t)y[0] % kGridAlign;
+                in_place = in_place || x[r] == y[r];
+            }
+            if (!share && !in_place && 2 * (uint64_t)n * count * E >= 64 * kMiB)
+                return ring_order_realigned(a, n, count, cus, st);
+        }
         // At least one wave per chunk for the scalar head/tail pass.
         const uint64_t lanes = a.tile0[n] * 64, scalar_lanes = (uint64_t)n * 64;
         const uint64_t work = lanes > scalar_lanes ? lanes : scalar_lanes;
@@ -651,6 +719,51 @@ struct Launch {
             hipLaunchKernelGGL((vrc::k_ring_chain_allreduce<T, K, MEM, true, 64>), grid, dim3(64), 0, st, a); \
         else                                                                                             \
             hipLaunchKernelGGL((vrc::k_ring_chain_allreduce<T, K, MEM, true>), grid, dim3(kBlock), 0, st, a); \
+        break;
+            VRC_FOR_N(VRC_CASE)
+#undef VRC_CASE
+        default: return VRC_ERR_INVALID_ARG;
+        }
+        return check_launch();
+    }
+
+    // The ring-order all-reduce with every output stored on its own 128-byte
+    // grid; `c` holds the chunk geometry of the tile kernel.
+    static vrc_status_t ring_order_realigned(const vrc::ChainArgs& c, int n, uint64_t count, int cus, hipStream_t st)
+    {
+        const int U = realign_unroll(n);
+        const uint64_t gv = (uint64_t)U * 64;
+        vrc::RingOrderRealignArgs a = {};
+        for (int r = 0; r < kMaxRanks; r++) {
+            a.src[r] = c.src[r];
+            a.dst[r] = c.dst[r];
+            a.ch[r] = c.ch[r];
+        }
+        a.group0[0] = 0;
+        a.rest0[0] = 0;
+        for (int k = 0; k < n; k++) {
+            const uint64_t nvb = c.ch[k].g.nvb;
+            const uint64_t groups = nvb >= gv + 8 ? (nvb - 8) / gv : 0;
+            const uint64_t rest = groups ? 8 + (nvb - groups * gv) : nvb;
+            a.group0[k + 1] = a.group0[k] + groups;
+            a.rest0[k + 1] = a.rest0[k] + (rest + 63) / 64;
+            const uintptr_t body = (c.ch[k].off + c.ch[k].g.head) * E;
+            for (int r = 0; r < n; r++)
+                a.shift[k][r] = (uint8_t)((kGridAlign - ((uintptr_t)c.dst[r] + body) % kGridAlign) % kGridAlign);
+        }
+        for (int k = n; k < kMaxRanks; k++) {
+            a.group0[k + 1] = a.group0[n];
+            a.rest0[k + 1] = a.rest0[n];
+        }
+        uint64_t work = a.group0[n] > a.rest0[n] ? a.group0[n] : a.rest0[n];
+        if (work < (uint64_t)n) work = n;  // one wave per chunk for the scalar pass
+        const dim3 grid(grid_x(cus, work * 64, 1, realign_blocks_per_cu(n), 64));
+        if (g_plan) return plan_single(VRC_OP_RING_ORDER_ALLREDUCE_REALIGNED, count, grid, 64, U);
+        switch (n) {
+#define VRC_CASE(K)                                                                                              \
+    case K:                                                                                                      \
+        hipLaunchKernelGGL((vrc::k_ring_order_allreduce_realigned<T, K, realign_unroll(K), true>), grid, dim3(64), \
+                           0, st, a);                                                                            \
         break;
             VRC_FOR_N(VRC_CASE)
 #undef VRC_CASE

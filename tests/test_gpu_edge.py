@@ -139,6 +139,58 @@ def test_large_allreduce_on_mixed_offsets(vrc, orc, mode):
     equal_to_expected(vy, want, f"large mixed offsets {mode}")
 
 
+@pytest.mark.parametrize("n,dtype,mode,count", [
+    (2, "fp32", "fused", 4 * (1 << 20) + 37),
+    (3, "fp16", "fused", 6 * (1 << 20) + 11),
+    (4, "fp16", "hd_order", 4 * (1 << 20) + 1),
+    (5, "int32", "fused", 2 * (1 << 20) + 3),
+    (8, "bf16", "hd_order", 2 * (1 << 20) + 77),
+    (8, "bf16", "fused", 2 * (1 << 20) + 4096 + 13),
+    (13, "fp32", "fused", (1 << 20) + 5),
+    (16, "bf16", "fused", (1 << 20) + 9),
+    (16, "fp32", "hd_order", (1 << 19) + 1),
+    (3, "int32", "ring_order", 3 * (1 << 20) + 7),
+    (5, "fp16", "ring_order", 4 * (1 << 20) + 5),
+    (8, "bf16", "ring_order", 2 * (1 << 20) + 77),
+    (16, "fp32", "ring_order", (1 << 19) + 1)])
+def test_realigned_fused_allreduce(vrc, orc, n, dtype, mode, count):
+    """Outputs on n different offsets modulo 128 bytes (every byte shift the
+    realigned stores funnel, 2-byte ones included; the ring order per chunk,
+    with the chunk's own rank rotation), inputs on their own
+    offsets, a count that leaves a partial group and a scalar tail, at least
+    64 MiB moved so the realigned kernel runs (vrc_plan says which).  Every
+    element of every output against the oracle."""
+    esz = {"fp32": 4, "int32": 4, "fp16": 2, "bf16": 2}[dtype]
+    per_line = 128 // esz
+    in_off = [r % 3 for r in range(n)]
+    out_off = [(19 * r + 5) % per_line for r in range(n)]
+    say(f"realigned fused all-reduce {mode}: n={n} {dtype} count={count} out offsets {out_off}")
+    xs = workloads.random_ranks(n, count, dtype, seed=4301 + n, device=DEV, sigma=1e-2)
+
+    def views(src, offsets):
+        out = []
+        for x, off in zip(src, offsets):
+            buf = torch.zeros(count + per_line, dtype=x.dtype, device=DEV)
+            v = buf[off:off + count]
+            v.copy_(x)
+            out.append(v)
+        return out
+
+    vx = views(xs, in_off)
+    vy = views([torch.zeros_like(x) for x in xs], out_off)
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, [v.data_ptr() for v in vx], [v.data_ptr() for v in vy], count, 1,
+                      {"int32": vrc.VRC_INT32, "fp32": vrc.VRC_FP32, "fp16": vrc.VRC_FP16, "bf16": vrc.VRC_BF16}[dtype],
+                      vrc.MODES[mode])
+    want_kind = {"hd_order": "butterfly", "ring_order": "ring_order", "fused": "fused"}[mode] + "_allreduce_realigned"
+    assert [o["kind"] for o in ops] == [want_kind]
+    vrc.vrc_allreduce(vx, recv=vy, mode=mode)
+    torch.cuda.synchronize()
+    at = {"hd_order": orc.hd_allreduce_at, "ring_order": orc.ring_allreduce_at,
+          "fused": orc.fused_allreduce_at}[mode]
+    want = torch.from_numpy(oracle_every_element(at, host(xs), dtype, count)).to(DEV)
+    equal_to_expected(vy, want, f"realigned {mode} n={n} {dtype}")
+
+
 @pytest.mark.parametrize("mode,n", [("ring", 5), ("fused", 5), ("ring_chained", 5), ("ring_order", 5),
                                     ("hd", 8), ("hd_order", 8)])
 def test_large_ragged_flat_reduce_scatter(vrc, orc, mode, n):

@@ -96,20 +96,93 @@ def test_fused_allreduce_one_wave_shapes(n):
                                                                       vectors)]
 
 
+def off_grid_shape(n):
+    """U consecutive tiles per wave (the largest U <= 8 with U x N <= 32, at
+    least 2) at 64 / (U x N) workgroups per CU, rounded down to a power of two."""
+    u = 8
+    while u > 2 and u * n > 32:
+        u //= 2
+    bpc = max(1, 64 // (u * n))
+    return 1 << (bpc.bit_length() - 1), u
+
+
 @pytest.mark.parametrize("n", list(range(2, 17)))
 def test_fused_allreduce_outputs_off_one_grid(n):
-    """Outputs on different offsets modulo 128 bytes: the largest U <= 8 with
-    U x N <= 32 consecutive tiles per wave, at 64 / (U x N) workgroups per CU."""
+    """Outputs on different offsets modulo 128 bytes, none in place: the
+    realigned kernel, which stores every output on its own 128-byte grid."""
     count = (4 << 30) // n // 2 // 64 * 64
     send, recv = wide(n)
     recv = [a + 2 * r for r, a in enumerate(recv)]
+    bpc, u = off_grid_shape(n)
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
+    assert launches(ops) == [("fused_allreduce_realigned", CUS * bpc, 1, 64, u)]
+    if n in (4, 8, 16):  # at 2 ranks the butterfly is the rank fold
+        ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_HD_ORDER)
+        assert launches(ops) == [("butterfly_allreduce_realigned", CUS * bpc, 1, 64, u)]
+
+
+@pytest.mark.parametrize("n", list(range(2, 17)))
+def test_ring_order_outputs_off_one_grid(n):
+    """The ring-order all-reduce takes its realigned variant on the same
+    terms (outputs on different 128-byte offsets, none in place, at least
+    64 MiB moved), at the fused kernel's realigned shape; in place, or below
+    64 MiB moved, the tile kernel."""
+    count = (4 << 30) // n // 2 // 64 * 64
+    send, recv = wide(n)
+    mixed = [a + 2 * r for r, a in enumerate(recv)]
+    bpc, u = off_grid_shape(n)
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, send, mixed, count, 1, vrc.VRC_BF16, vrc.VRC_RING_ORDER)
+    assert launches(ops) == [("ring_order_allreduce_realigned", CUS * bpc, 1, 64, u)]
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, mixed, mixed, count, 1, vrc.VRC_BF16, vrc.VRC_RING_ORDER)
+    assert launches(ops)[0][0] == "ring_order_allreduce"
+    small = (32 << 20) // (2 * n * 2)
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, send, mixed, small, 1, vrc.VRC_BF16, vrc.VRC_RING_ORDER)
+    assert launches(ops)[0][0] == "ring_order_allreduce"
+    # the memory-faithful chain keeps its kernel
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, send, mixed, count, 1, vrc.VRC_BF16, vrc.VRC_RING_CHAINED)
+    assert launches(ops)[0][0] == "chain_allreduce"
+
+
+@pytest.mark.parametrize("n", [2, 5, 8, 16])
+def test_in_place_outputs_off_one_grid_keep_the_tile_kernel(n):
+    """In place, the realigned stores would run ahead of the reads of the
+    next group: the tile kernel (consecutive tiles, unaligned stores) runs."""
+    count = (4 << 30) // n // 2 // 64 * 64
+    bufs = [(1 << 40) + r * (1 << 32) + 2 * r for r in range(n)]
     u = 8
-    while u * n > 32:
+    while u > 1 and u * n > 32:
         u //= 2
     bpc = 64 // (u * n)
     bpc = 1 << (bpc.bit_length() - 1)
-    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, bufs, bufs, count, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
     assert launches(ops) == [("fused_allreduce", CUS * bpc, 1, 64, u)]
+    # one output in place is enough
+    send, recv = wide(n)
+    recv = [a + 2 * r for r, a in enumerate(recv)]
+    recv[n - 1] = send[n - 1]
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
+    assert launches(ops)[0][0] == "fused_allreduce"
+
+
+@pytest.mark.parametrize("dtype", [vrc.VRC_BF16, vrc.VRC_FP16, vrc.VRC_FP32, vrc.VRC_INT32])
+def test_realigned_only_where_outputs_differ_modulo_128(dtype):
+    """Outputs 128 bytes apart modulo 256 share the 128-byte grid (no
+    realignment); one output 64 bytes off is enough to realign; at 8
+    ranks x 2 MiB (below 64 MiB moved) the launch-bound 256-lane kernel
+    runs whatever the offsets."""
+    n, esz = 8, ESZ[dtype]
+    count = (512 << 20) // esz
+    send, recv = wide(n)
+    shared = [a + 128 * (r % 2) for r, a in enumerate(recv)]
+    assert launches(vrc.plan(vrc.COLL_ALLREDUCE, send, shared, count, 1, dtype, vrc.VRC_FUSED)[0])[0][0] == \
+        "fused_allreduce"
+    one_off = list(recv)
+    one_off[3] += 64
+    assert launches(vrc.plan(vrc.COLL_ALLREDUCE, send, one_off, count, 1, dtype, vrc.VRC_FUSED)[0])[0][0] == \
+        "fused_allreduce_realigned"
+    small = (2 << 20) // esz
+    got = launches(vrc.plan(vrc.COLL_ALLREDUCE, send, one_off, small, 1, dtype, vrc.VRC_FUSED)[0])
+    assert got[0][0] == "fused_allreduce" and got[0][3] == 256
 
 
 def test_headline_shape():
@@ -293,9 +366,9 @@ def test_mixed_offsets_keep_the_full_grid(mode):
     aligned, nl = vrc.plan(vrc.COLL_ALLREDUCE, send, recv, count, 1, vrc.VRC_BF16, vrc.MODES[mode])
     mixed, nl2 = vrc.plan(vrc.COLL_ALLREDUCE, mixed_send, mixed_recv, count, 1, vrc.VRC_BF16, vrc.MODES[mode])
     assert nl2 == nl
-    if mode in ("fused", "hd_order"):
-        # the fused kernel takes its shape for outputs off one grid (test above)
-        assert [k[0] for k in launches(mixed)] == [k[0] for k in launches(aligned)]
+    if mode in ("fused", "hd_order", "ring_order"):
+        # the realigned variants (tests above)
+        assert [k[0] for k in launches(mixed)] == [k[0] + "_realigned" for k in launches(aligned)]
     else:
         assert launches(mixed) == launches(aligned)
     for kind, gx, gy, block, vec in launches(mixed):
