@@ -82,6 +82,19 @@ def recorded_traffic(workload: str, mode: str):
     return int(m_fetch.group(1)) + int(m_write.group(1))
 
 
+def recorded_mixed_stream():
+    """The L2-to-fabric latency and stall figures of the headline kernel's
+    mixed read/write stream (profiles/mixed_stream.stream_split.counters.md),
+    if they were taken on the current kernel sources."""
+    path = os.path.join(PROFILES, "mixed_stream.stream_split.counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = dict(re.findall(r"^([a-z_0-9]+):\s*([0-9a-f.]+)\s*$", open(path).read(), re.M))
+    if vals.pop("source_sha256_16", None) != kernel_source_hash():
+        return None
+    return {k: float(v) for k, v in vals.items()}
+
+
 def time_calls(fn, steps: int, warmup: int, torch):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -265,10 +278,11 @@ def run_suite(steps: int, torch, vrc, workloads) -> int:
     return 0
 
 
-def interleaved_us(torch, calls: dict, steps: int, rounds: int = 4) -> dict:
+def interleaved_us(torch, calls: dict, steps: int, rounds: int = 4, flush=None) -> dict:
     """Median HIP-event time (us) of each named call, the calls interleaved
     over `rounds` rounds in one process (the same buffers, the same DRAM
-    placement for every call of a pair)."""
+    placement for every call of a pair).  With `flush` (a device tensor),
+    each timed call follows an untimed write of it."""
     ms = {k: [] for k in calls}
     for name, fn in calls.items():
         for _ in range(3):
@@ -279,6 +293,8 @@ def interleaved_us(torch, calls: dict, steps: int, rounds: int = 4) -> dict:
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(max(1, steps // rounds))]
             for e0, e1 in evs:
+                if flush is not None:
+                    flush.zero_()
                 e0.record()
                 fn()
                 e1.record()
@@ -344,6 +360,72 @@ def run_offsets(steps: int, torch, vrc, workloads) -> int:
                "offset_over_aligned": round(o_ns / a_ns, 4)}
         print(json.dumps(rec), flush=True)
         log(f"offsets RS {mode:13s} aligned {t['aligned']:9.1f} us  ragged {t['offset']:9.1f} us  x{o_ns / a_ns:.3f}")
+    return 0
+
+
+def split_streams(torch, vrc, xs, outs, collective: str, steps: int, flush=None, dim: int = 0) -> dict:
+    """One collective beside the same bytes moved one direction at a time:
+    the inputs read by the runtime's reduction (torch.sum), the outputs
+    written by its fill kernel, and (all-reduce) each input copied into its
+    output by the runtime's device copy.  Times are medians of interleaved
+    HIP-event intervals on the same buffers."""
+    read_bytes = sum(x.numel() * x.element_size() for x in xs)
+    write_bytes = sum(y.numel() * y.element_size() for y in outs)
+
+    def collective_call():
+        if collective == "allreduce":
+            vrc.vrc_allreduce(xs, recv=outs, mode="fused")
+        else:
+            vrc.vrc_all_gather(xs, recv=outs, dim=dim, mode="fused")
+
+    def read_only():
+        for x in xs:
+            x.sum(dtype=torch.float32)
+
+    def write_only():
+        for y in outs:
+            y.fill_(1)
+
+    calls = {"collective": collective_call, "read_only": read_only, "write_only": write_only}
+    if collective == "allreduce":
+        calls["copy"] = lambda: [y.copy_(x) for x, y in zip(xs, outs)]
+    t = interleaved_us(torch, calls, steps, flush=flush)
+    rec = {"read_bytes": read_bytes, "write_bytes": write_bytes,
+           "collective_us": round(t["collective"], 2), "read_only_us": round(t["read_only"], 2),
+           "write_only_us": round(t["write_only"], 2),
+           "read_only_GB_per_s": round(read_bytes / t["read_only"] / 1e3, 1),
+           "write_only_GB_per_s": round(write_bytes / t["write_only"] / 1e3, 1),
+           "collective_GB_per_s": round((read_bytes + write_bytes) / t["collective"] / 1e3, 1),
+           "serialized_us": round(t["read_only"] + t["write_only"], 2),
+           "collective_over_serialized": round(t["collective"] / (t["read_only"] + t["write_only"]), 4)}
+    if "copy" in t:
+        rec["copy_us"] = round(t["copy"], 2)
+        rec["copy_GB_per_s"] = round((read_bytes + write_bytes) / t["copy"] / 1e3, 1)
+    return rec
+
+
+def run_stream_split(steps: int, torch, vrc, workloads) -> int:
+    """The headline all-reduce (8 x 512 MiB bf16) and the 8-rank fp16 heads
+    all-gather, each beside read-only, write-only (and copy) passes over the
+    same bytes (split_streams); the all-gather's calls each follow a 1 GiB
+    cache flush, as in the suite.  One JSON line per workload; run under
+    rocprofv3 --pmc for the per-kernel counters."""
+    dev = "cuda:0"
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    xs = workloads.make_inputs(w, dev)
+    ys = [torch.empty_like(x) for x in xs]
+    rec = split_streams(torch, vrc, xs, ys, "allreduce", steps)
+    print(json.dumps({"stream_split": w.name, **rec}), flush=True)
+    log(f"stream split {w.name}: {rec}")
+    del xs, ys
+    torch.cuda.empty_cache()
+    w = workloads.WORKLOADS["all_gather_fp16_n8_heads"]
+    xs = workloads.make_inputs(w, dev)
+    outs = vrc.vrc_all_gather(xs, dim=w.dim)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    rec = split_streams(torch, vrc, xs, outs, "all_gather", steps, flush=flush, dim=w.dim)
+    print(json.dumps({"stream_split": w.name, **rec}), flush=True)
+    log(f"stream split {w.name}: {rec}")
     return 0
 
 
@@ -543,37 +625,68 @@ def run_overlap_buckets(steps: int, mode: str, torch, vrc, workloads, only=None)
     return 0
 
 
+# The measured rows: (workload[@count], mode), every collective of every
+# workload in its fused and step-ring forms, plus the headline's other modes.
+PROFILE_ROWS = (
+    ("allreduce_int32_n4_4099", "fused"), ("allreduce_int32_n4_4099", "ring"),
+    ("allreduce_fp32_n8_16mib", "fused"), ("allreduce_fp32_n8_16mib", "ring"),
+    ("allreduce_fp16_n8_128mib@524288", "fused"), ("allreduce_fp16_n8_128mib@524288", "ring"),
+    ("allreduce_fp16_n8_128mib@8388608", "fused"), ("allreduce_fp16_n8_128mib@8388608", "ring"),
+    ("allreduce_fp16_n8_128mib", "fused"), ("allreduce_fp16_n8_128mib", "ring"),
+    ("allreduce_bf16_n8_512mib", "fused"), ("allreduce_bf16_n8_512mib", "ring"),
+    ("allreduce_bf16_n8_512mib", "ring_chained"), ("allreduce_bf16_n8_512mib", "ring_order"),
+    ("allreduce_bf16_n8_512mib", "hd"), ("allreduce_bf16_n8_512mib", "hd_order"),
+    ("all_gather_fp16_n8_heads", "fused"), ("all_gather_fp16_n8_heads", "ring"),
+    ("reduce_scatter_fp16_n8_act", "fused"), ("reduce_scatter_fp16_n8_act", "ring"),
+)
+
+
 def run_profile_case(case: str, steps: int, torch, vrc, workloads) -> int:
-    """`steps` calls of one workload in one mode, each after an untimed 1 GiB
-    write (the suite's cache flush), for rocprofv3 counter passes: the kernel
-    of interest is every dispatch whose name it bears.  `case` is
-    WORKLOAD[@COUNT]:MODE (COUNT overrides the per-rank element count, as the
-    sweep sizes of a workload)."""
+    """`steps` calls of each case, each call after an untimed 1 GiB write
+    (the suite's cache flush), for rocprofv3 passes: per-dispatch counters
+    then belong to the case whose line was printed last before them, and the
+    flush's fill kernel separates the calls.  `case` is WORKLOAD[@COUNT]:MODE
+    (COUNT overrides the per-rank element count, as the sweep sizes of a
+    workload), several joined by commas, or "rows" for PROFILE_ROWS.  One
+    JSON line per case, printed (and flushed) before its calls."""
     dev = "cuda:0"
-    name, mode = case.split(":")
-    count = None
-    if "@" in name:
-        name, count = name.split("@")
-    w = workloads.WORKLOADS[name]
-    if count is not None:
-        w = w.with_count(int(count))
-    xs = workloads.make_inputs(w, dev)
-    if w.collective == "allreduce":
-        outs = [torch.empty_like(x) for x in xs]
-        call = lambda: vrc.vrc_allreduce(xs, recv=outs, mode=mode)  # noqa: E731
-    elif w.collective == "reduce_scatter":
-        outs = vrc.vrc_reduce_scatter(xs, dim=w.dim)
-        call = lambda: vrc.vrc_reduce_scatter(xs, recv=outs, dim=w.dim, mode=mode)  # noqa: E731
-    else:
-        outs = vrc.vrc_all_gather(xs, dim=w.dim)
-        call = lambda: vrc.vrc_all_gather(xs, recv=outs, dim=w.dim, mode=mode)  # noqa: E731
+    cases = PROFILE_ROWS if case == "rows" else tuple(tuple(c.split(":")) for c in case.split(","))
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        flush.zero_()
-        call()
-    torch.cuda.synchronize()
-    print(json.dumps({"profile_case": case, "calls": steps, "alg_bytes_per_call": suite_bytes(w, mode)}), flush=True)
+    loaded = (None, None)
+    for idx, (name, mode) in enumerate(cases):
+        base, count = (name.split("@") + [None])[:2]
+        w = workloads.WORKLOADS[base]
+        if count is not None:
+            w = w.with_count(int(count))
+        if loaded[0] != name:
+            loaded = (None, None)
+            torch.cuda.empty_cache()
+            xs = workloads.make_inputs(w, dev)
+            if w.collective == "allreduce":
+                outs = [torch.empty_like(x) for x in xs]
+            elif w.collective == "reduce_scatter":
+                outs = vrc.vrc_reduce_scatter(xs, dim=w.dim)
+            else:
+                outs = vrc.vrc_all_gather(xs, dim=w.dim)
+            loaded = (name, (xs, outs))
+        xs, outs = loaded[1]
+
+        def call(w=w, xs=xs, outs=outs, mode=mode):
+            if w.collective == "allreduce":
+                vrc.vrc_allreduce(xs, recv=outs, mode=mode)
+            elif w.collective == "reduce_scatter":
+                vrc.vrc_reduce_scatter(xs, recv=outs, dim=w.dim, mode=mode)
+            else:
+                vrc.vrc_all_gather(xs, recv=outs, dim=w.dim, mode=mode)
+
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_case": f"{name}:{mode}", "index": idx, "calls": steps,
+                          "collective": w.collective, "n_ranks": w.n, "dtype": w.dtype,
+                          "elements_per_rank": w.count, "alg_bytes_per_call": suite_bytes(w, mode)}), flush=True)
+        for _ in range(steps):
+            flush.zero_()
+            call()
+        torch.cuda.synchronize()
     return 0
 
 
@@ -600,8 +713,12 @@ def main() -> int:
                     help="time operands off their destination's grid beside their aligned twins")
     ap.add_argument("--ag-sweep", action="store_true",
                     help="time the all-gather algorithms (ring, recursive doubling, tree, fused) by size")
+    ap.add_argument("--stream-split", action="store_true",
+                    help="time the headline all-reduce and the heads all-gather beside read-only, write-only "
+                         "and copy passes over the same bytes")
     ap.add_argument("--profile-case", default=None,
-                    help="WORKLOAD[@COUNT]:MODE -- run only this collective `--steps` times (for counter passes)")
+                    help="WORKLOAD[@COUNT]:MODE[,...] or 'rows' -- run only these collectives `--steps` times "
+                         "each (for counter passes)")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB (known HBM traffic: 1 GiB read, 1 GiB "
                          "written per launch), for calibrating rocprofv3 byte counters")
@@ -629,6 +746,8 @@ def main() -> int:
         return run_ag_sweep(args.steps, torch, vrc, workloads)
     if args.profile_case:
         return run_profile_case(args.profile_case, args.steps, torch, vrc, workloads)
+    if args.stream_split:
+        return run_stream_split(args.steps, torch, vrc, workloads)
     if args.overlap and args.buckets:
         only = tuple(int(v) for v in args.bucket_case.split(",")) if args.bucket_case else None
         return run_overlap_buckets(args.steps, args.mode, torch, vrc, workloads, only)
@@ -709,6 +828,18 @@ def main() -> int:
                                   "GB_per_s": round(copy_gbs, 2),
                                   "kernel_over_copy": round(achieved / copy_gbs, 4)}
         log(f"same-box copy: {extra['same_box_copy']}")
+
+        # The mixed stream against one-direction passes over the same bytes (split_streams), with the
+        # recorded L2-to-fabric counters: where the remaining gap to the HBM peak comes from.
+        split = split_streams(torch, vrc, xs, ys, "allreduce", max(8, min(args.steps, 20)))
+        extra["mixed_stream"] = {
+            "fused_GB_per_s": split["collective_GB_per_s"], "write_only_GB_per_s": split["write_only_GB_per_s"],
+            "copy_GB_per_s": split["copy_GB_per_s"], "write_only_what": "torch fill_ of the 8 outputs",
+            "counters": recorded_mixed_stream(),
+            "reading": "the L2 is busy nearly every cycle and the write path barely stalls, while read latency "
+                       "rises well above a read-only stream's: the half-read, half-write stream is bound by DRAM "
+                       "read/write turnaround, which the runtime's own copy of the same bytes hits harder"}
+        log(f"mixed stream: {extra['mixed_stream']}")
 
     # NCCL-style figures for context: algbw = S / t per rank buffer, busbw = algbw * 2(N-1)/N.
     algbw = size / (kavg * 1e-3) / 1e9

@@ -67,10 +67,14 @@
  *   Alignment   Any element-aligned pointer works, and every operand moves
  *               in 16-byte vectors whatever its offset.  A region's vectors
  *               start where its destination crosses a 128-byte boundary (the
- *               elements before it and the last partial vector run scalar);
- *               operands on other offsets cost some bandwidth (about 8 % for
- *               inputs; outputs on differing offsets, up to about 30 % for the
- *               single-launch all-reduce modes).
+ *               elements before it and the last partial vector run scalar).
+ *               Where the outputs of a single-launch all-reduce sit on
+ *               different offsets modulo 128 bytes, VRC_FUSED, VRC_HD_ORDER
+ *               and VRC_RING_ORDER store each output on its own 128-byte
+ *               grid (unless an output is its own input).  Operands on other
+ *               offsets cost some bandwidth: about 5-10 % for the all-reduce
+ *               with every input and output on its own offset; about 45 %
+ *               for VRC_RING_CHAINED, whose partials keep the reference grid.
  *   Errors      Argument errors return before anything is enqueued.
  *   Threads     Calls are re-entrant and thread-safe; calls that overlap on
  *               the same buffers race like any two kernels would.

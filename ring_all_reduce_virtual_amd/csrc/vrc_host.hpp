@@ -148,7 +148,12 @@ inline int fused_blocks_per_cu(uint64_t bytes_moved, int n)
 // inputs and outputs on offsets 2r bytes (ms; aligned U 1 at 4 per CU:
 // 1.532): rank fold U 4 at 2 per CU 1.781, U 2 at 2 per CU 1.798, U 4 at 1
 // per CU 1.814, U 1 at 4 per CU 2.017; the butterfly fold 1.770, 1.819, 2.743
-// and 2.021 (with one wave per CU it turns ALU-bound).
+// and 2.021 (with one wave per CU it turns ALU-bound).  Calls with no
+// output in place take the realigned kernels instead (realign_unroll, the
+// same U and workgroups per CU; 8 ranks, every operand on its own offset,
+// against the aligned call: rank fold 1.05-1.09x at 2 per CU, 1.12x at 4,
+// 1.14x at 3; butterfly 1.05-1.09x; ring order 1.10x); this shape remains
+// for in-place calls.
 // Below 64 MiB moved a call is launch-bound and keeps 256-lane workgroups,
 // 8 per CU, two vectors per rank one grid stride apart.
 struct FusedShape {

@@ -157,7 +157,8 @@ __global__ __launch_bounds__(B) void k_ring_step(StepArgsK<K> args)
 //  iteration and stores them back to back, so a 64-byte write block that an
 //  output off the vector grid splits between two of its tiles is filled by
 //  one wave at once, and the cache merges it; workgroups go to the XCDs in
-//  turn, U KiB each.
+//  turn, U KiB each.  (Outputs on different 128-byte offsets with none in
+//  place take k_fused_allreduce_realigned below instead.)
 //  B = 256: the U vectors of a lane are one grid stride apart.
 // ---------------------------------------------------------------------------
 struct FusedArArgs {

@@ -64,7 +64,37 @@ def test_recorded_traffic():
     assert abs(t / 8589934592 - 1) < 1e-3
 
 
+def test_recorded_mixed_stream():
+    """The mixed-stream counters come from the committed summary on the same
+    kernel sources; the figures the headline line carries are present and
+    plausible (fractions within [0, 1], latencies positive)."""
+    m = bench.recorded_mixed_stream()
+    if m is None:
+        pytest.skip("the committed counters were taken on other kernel sources; re-take them on the GPU")
+    for k in ("fused_read_latency_cycles", "fused_l2_busy", "fused_write_credit_stall",
+              "fused_too_many_write_requests_stall", "fused_reads_in_flight_per_channel"):
+        assert k in m
+    assert m["fused_read_latency_cycles"] > 0 and 0 <= m["fused_l2_busy"] <= 1
+    assert 0 <= m["fused_write_credit_stall"] <= 1 and 0 <= m["fused_too_many_write_requests_stall"] <= 1
+
+
 def test_host_info_fields():
     info = bench.host_info()
     assert info["nproc"] >= 1 and info["affinity"] >= 1
     json.dumps(info)
+
+
+def test_profile_rows_name_real_workloads_and_modes():
+    """Every counter row names a workload (or one of its sweep sizes) and a
+    mode the library has; every workload is covered in fused and ring form."""
+    import ring_all_reduce_virtual_amd as vrc
+    import workloads
+    seen = set()
+    for name, mode in bench.PROFILE_ROWS:
+        base, _, count = name.partition("@")
+        w = workloads.WORKLOADS[base]
+        assert not count or int(count) in w.sweep
+        assert mode in vrc.MODES
+        seen.add((base, mode))
+    for base in workloads.WORKLOADS:
+        assert (base, "fused") in seen and (base, "ring") in seen
