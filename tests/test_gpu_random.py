@@ -217,3 +217,44 @@ def test_random_large_reduce_scatter(vrc, orc, k):
     want = want_rs(orc, hx, dtype, mode)
     for c, y in enumerate(host(ys)):
         assert_bitwise(y, want[c], f"large case {k} {mode} {dtype} n={n} count={count} chunk {c}")
+
+
+# ---------------------------------------------------------------------------
+# The realigned single-launch all-reduces: outputs on random offsets within a
+# 128-byte line (every byte shift up to 127), inputs on their own offsets,
+# above 64 MiB moved, and now and then some ranks in place (which keeps the
+# tile kernel); vrc_plan names the kernel each case expects.
+# ---------------------------------------------------------------------------
+REALIGN_CASES = 12
+REALIGN_MODES = ("fused", "hd_order", "ring_order")
+
+
+@pytest.mark.parametrize("k", range(REALIGN_CASES))
+def test_random_realigned_allreduce(vrc, orc, k):
+    rng, dtype, mode, n, esz = draw_large(6, k, REALIGN_MODES)
+    per_line = 128 // esz
+    moved = int(rng.uniform(64, 128) * (1 << 20))
+    count = moved // (2 * n * esz) + int(rng.integers(0, 4096))
+    in_off = [int(v) for v in rng.integers(0, per_line, n)]
+    out_off = [int(v) for v in rng.integers(0, per_line, n)]
+    in_place = [bool(v) for v in (rng.random(n) < 0.15)] if k % 4 == 3 else [False] * n
+    xs = workloads.random_ranks(n, (count,), dtype, seed=input_seed(60000 + k), device=DEV)
+    xs = [place(x, o) for x, o in zip(xs, in_off)]
+    ys = [xs[r] if in_place[r] else empty_at((count,), xs[0].dtype, out_off[r]) for r in range(n)]
+    addrs = [y.data_ptr() for y in ys]
+    share = len({a % 128 for a in addrs}) == 1
+    realign = not share and not any(in_place)
+    base = {"fused": "fused_allreduce", "hd_order": "butterfly_allreduce" if n > 2 else "fused_allreduce",
+            "ring_order": "ring_order_allreduce"}[mode]
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, [x.data_ptr() for x in xs], addrs, count, 1,
+                      {"int32": vrc.VRC_INT32, "fp32": vrc.VRC_FP32, "fp16": vrc.VRC_FP16, "bf16": vrc.VRC_BF16}[dtype],
+                      vrc.MODES[mode])
+    print(f"random realigned allreduce case {k}: {mode} {dtype} n={n} count={count} in {in_off} out {out_off} "
+          f"in_place {sum(in_place)} -> {ops[0]['kind']}", flush=True)
+    assert [o["kind"] for o in ops] == [base + ("_realigned" if realign else "")]
+    hx = host(xs)
+    vrc.vrc_allreduce(xs, recv=ys, mode=mode)
+    torch.cuda.synchronize()
+    want = want_ar(orc, hx, dtype, mode)
+    for r, y in enumerate(host(ys)):
+        assert_bitwise(y, want[r], f"realigned case {k} {mode} {dtype} n={n} count={count} rank {r}")
