@@ -652,14 +652,14 @@ def run_profile_case(case: str, steps: int, torch, vrc, workloads) -> int:
     dev = "cuda:0"
     cases = PROFILE_ROWS if case == "rows" else tuple(tuple(c.split(":")) for c in case.split(","))
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    loaded = (None, None)
+    loaded = xs = outs = None
     for idx, (name, mode) in enumerate(cases):
         base, count = (name.split("@") + [None])[:2]
         w = workloads.WORKLOADS[base]
         if count is not None:
             w = w.with_count(int(count))
-        if loaded[0] != name:
-            loaded = (None, None)
+        if loaded is None or loaded[0] != name:
+            loaded = xs = outs = call = None  # drop the previous workload's buffers before allocating the next
             torch.cuda.empty_cache()
             xs = workloads.make_inputs(w, dev)
             if w.collective == "allreduce":
