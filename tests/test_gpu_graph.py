@@ -120,3 +120,44 @@ def test_captured_tree_all_gather(vrc, n):
         want = orc.tree_all_gather(host(fresh), "bf16", outer=3)
         for r in range(n):
             assert_bitwise(workloads.to_numpy(ag[r]), want[r], f"replay {rep} tree rank {r}")
+
+
+@pytest.mark.parametrize("mode", ["fused", "hd_order", "ring_order"])
+def test_captured_realigned_allreduce(vrc, mode):
+    """Outputs on eight different offsets modulo 128 bytes, above 64 MiB
+    moved: the realigned kernel (vrc_plan says so) captured and replayed,
+    with the eager program's own work between replays."""
+    print(f"graph realigned allreduce {mode}", flush=True)
+    orc = oracle.get()
+    n, count = 8, 2 * (1 << 20) + 77  # bf16: 64 MiB + moved
+    xs = workloads.random_ranks(n, count, "bf16", seed=502, device=DEV, sigma=1e-2)
+    ys = []
+    for r in range(n):
+        off = (11 * r + 3) % 64  # elements: 2-byte shifts across the whole line
+        buf = torch.zeros(count + 64, dtype=torch.bfloat16, device=DEV)
+        ys.append(buf[off:off + count])
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, [x.data_ptr() for x in xs], [y.data_ptr() for y in ys], count, 1,
+                      vrc.VRC_BF16, vrc.MODES[mode])
+    assert ops[0]["kind"].endswith("_realigned")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        vrc.vrc_allreduce(xs, recv=ys, mode=mode)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        vrc.vrc_allreduce(xs, recv=ys, mode=mode)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        fresh = workloads.random_ranks(n, count, "bf16", seed=800 + rep, device=DEV, sigma=1e-2)
+        for x, f in zip(xs, fresh):
+            x.copy_(f)
+        for y in ys:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = oracle_allreduce(orc, host(fresh), "bf16", mode)
+        for r in range(n):
+            assert_bitwise(workloads.to_numpy(ys[r]), want[r], f"replay {rep} realigned {mode} rank {r}")
