@@ -407,6 +407,32 @@ def test_more_than_2_to_31_elements_per_rank(vrc, orc, mode):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("mode", ["fused", "hd_order", "ring_order"])
+def test_realigned_past_2_to_31_elements_per_rank(vrc, orc, mode):
+    """64-bit indexing in the realigned kernels: 2^31 + 7 bf16 elements per
+    rank, 2 ranks, outputs 74 bytes apart modulo 128 (vrc_plan confirms the
+    realigned launch); sampled elements, ends and the 2^31 boundary."""
+    say(f"realigned 2^31+7 elements {mode}")
+    count = (1 << 31) + 7
+    xs = small_int_bf16(count, 2, 410)
+    bufs = [torch.empty(count + 64, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    ys = [bufs[0][:count], bufs[1][37:37 + count]]
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, [x.data_ptr() for x in xs], [y.data_ptr() for y in ys], count, 1,
+                      vrc.VRC_BF16, vrc.MODES[mode])
+    assert ops[0]["kind"].endswith("_realigned"), ops[0]["kind"]
+    vrc.vrc_allreduce(xs, recv=ys, mode=mode)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(410)
+    idx = np.unique(np.concatenate([
+        rng.integers(0, count, 200000), np.arange(0, 256), np.arange(count - 256, count),
+        np.arange((1 << 31) - 256, (1 << 31) + 7), np.arange(count // 2 - 256, count // 2 + 256)])).astype(np.int64)
+    want = as_f32(xs[0], idx) + as_f32(xs[1], idx)  # small integers: every order gives the exact sum
+    for r in range(2):
+        assert np.array_equal(as_f32(ys[r], idx), want), f"{mode} rank {r}"
+    del xs, ys, bufs
+    torch.cuda.empty_cache()
+
+
 def small_int_bf16(count, n, seed):
     """n bf16 tensors of small integers: any summation order gives the exact sum."""
     g = torch.Generator(device=DEV).manual_seed(seed)
