@@ -726,7 +726,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs N virtual ranks on ONE GPU; --gpus must be 1 "
+        print("bench.py: the library runs N virtual ranks on ONE GPU; --gpus must be 1 "
               f"(got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
         return 2
 
