@@ -3,7 +3,8 @@
  * Python and no PyTorch: rank buffers come from hipMalloc and the HIP
  * runtime is /opt/rocm's.  Every collective runs in every mode on int32 and
  * on fp32 holding small integers, whose sums are exact in any order, and is
- * checked against the sum computed here.  Prints "ok" and exits 0, or
+ * checked against the sum computed here; so is the bucketed all-reduce, with
+ * and without its per-bucket events.  Prints "ok" and exits 0, or
  * prints the first mismatch and exits 1.
  */
 #include <hip/hip_runtime_api.h>
@@ -25,6 +26,35 @@
     } while (0)
 
 static int32_t value(int r, size_t i) { return (int32_t)((i * 2654435761u + (unsigned)r * 40503u) % 61u) - 30; }
+
+/* Every rank's all-reduce output against the exact sums. */
+static int check_sums(vrc_dtype_t dt, void* const* y, size_t count, const int64_t* want, unsigned char* got,
+                      const char* what, int mode)
+{
+    const size_t esz = 4;
+    for (int r = 0; r < N; r++) {
+        CHECK_HIP(hipMemcpy(got, y[r], count * esz, hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < count; i++) {
+            int64_t v;
+            if (dt == VRC_INT32) {
+                int32_t t;
+                memcpy(&t, got + i * esz, 4);
+                v = t;
+            } else {
+                float f;
+                memcpy(&f, got + i * esz, 4);
+                v = (int64_t)f;
+                if ((float)v != f) v = INT64_MIN;
+            }
+            if (v != want[i]) {
+                fprintf(stderr, "%s dtype %d mode %d rank %d element %zu: %lld != %lld\n", what, (int)dt, mode, r, i,
+                        (long long)v, (long long)want[i]);
+                return 1;
+            }
+        }
+    }
+    return 0;
+}
 
 static int run_dtype(vrc_dtype_t dt, size_t count)
 {
@@ -146,6 +176,41 @@ static int run_dtype(vrc_dtype_t dt, size_t count)
                 }
             }
         }
+    }
+    /* The bucketed all-reduce on its own stream: buckets of 100,003 elements
+     * (the last one shorter), each gated by an event recorded on that stream,
+     * and the same call with no events. */
+    {
+        const size_t bucket = 100003;
+        const int nb = (int)((count + bucket - 1) / bucket);
+        hipStream_t s;
+        CHECK_HIP(hipStreamCreate(&s));
+        vrc_event_t* ev = (vrc_event_t*)malloc((size_t)nb * sizeof *ev);
+        if (!ev) return 2;
+        for (int k = 0; k < nb; k++) {
+            hipEvent_t e;
+            CHECK_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+            CHECK_HIP(hipEventRecord(e, s));
+            ev[k] = (vrc_event_t)e;
+        }
+        const vrc_mode_t bmodes[] = {VRC_FUSED, VRC_RING, VRC_SELECT};
+        for (size_t m = 0; m < sizeof(bmodes) / sizeof(bmodes[0]); m++) {
+            for (int with_events = 0; with_events < 2; with_events++) {
+                for (int r = 0; r < N; r++) CHECK_HIP(hipMemsetAsync(y[r], 0, count * esz, s));
+                vrc_status_t st = vrc_allreduce_bucketed((const void* const*)x, y, N, count, dt, VRC_SUM, bmodes[m],
+                                                         bucket, with_events ? ev : NULL, with_events ? nb : 0,
+                                                         (vrc_stream_t)s);
+                if (st != VRC_OK) {
+                    fprintf(stderr, "vrc_allreduce_bucketed mode %d: %s\n", (int)bmodes[m], vrc_status_string(st));
+                    return 1;
+                }
+                CHECK_HIP(hipStreamSynchronize(s));
+                if (check_sums(dt, y, count, want, got, "bucketed all-reduce", (int)bmodes[m])) return 1;
+            }
+        }
+        for (int k = 0; k < nb; k++) CHECK_HIP(hipEventDestroy((hipEvent_t)ev[k]));
+        free(ev);
+        CHECK_HIP(hipStreamDestroy(s));
     }
     for (int r = 0; r < N; r++) {
         CHECK_HIP(hipFree(x[r]));
