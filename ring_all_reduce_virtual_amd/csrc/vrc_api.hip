@@ -13,6 +13,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <cstring>
 
 // The C ABI keeps default visibility; everything else in the library is hidden.
 #pragma GCC visibility push(default)
@@ -88,12 +89,29 @@ vrc_status_t check_buffers(const void* const* send, void* const* recv, int n, ui
 // them (at most count * 16 ranks * 4 bytes) then fits in 64 bits.
 constexpr uint64_t kMaxCount = 1ull << 56;
 
-vrc_status_t check_common(const void* const* send, void* const* recv, int n, uint64_t count, vrc_dtype_t dtype)
+// The enum arguments of the C ABI hold whatever int a C caller passes.  In
+// C++ an enum object whose value lies outside its enumerators' range may not
+// be read as that enum, so every entry point reads them as plain ints (from
+// the object's bytes) and the implementations check the ints before turning
+// them back into enums.
+template <class E>
+int raw(const E& e)
+{
+    static_assert(sizeof(E) == sizeof(int), "the C enums of vrc.h are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
+bool dtype_valid(int d) { return d >= VRC_INT32 && d <= VRC_BF16; }
+bool mode_valid(int m) { return m >= VRC_RING && m <= VRC_TREE; }
+
+vrc_status_t check_common(const void* const* send, void* const* recv, int n, uint64_t count, int dtype)
 {
     if (!send || !recv) return VRC_ERR_INVALID_ARG;
     if (n < 1 || n > kMaxRanks) return VRC_ERR_INVALID_ARG;
     if (count > kMaxCount) return VRC_ERR_INVALID_ARG;
-    if (esize(dtype) == 0) return VRC_ERR_UNSUPPORTED;
+    if (!dtype_valid(dtype)) return VRC_ERR_UNSUPPORTED;
     return VRC_OK;
 }
 
@@ -120,12 +138,6 @@ vrc_status_t run(Coll coll, vrc_mode_t mode, vrc_dtype_t dt, const void* const* 
     case VRC_BF16: return run_typed<vrc::BF16>(coll, mode, x, y, n, count, outer, cus, st);
     }
     return VRC_ERR_UNSUPPORTED;
-}
-
-bool mode_ok(vrc_mode_t m)
-{
-    return m == VRC_RING || m == VRC_FUSED || m == VRC_RING_CHAINED || m == VRC_RING_ORDER || m == VRC_HD ||
-           m == VRC_HD_ORDER || m == VRC_SELECT || m == VRC_TREE;
 }
 
 // VRC_SELECT: halving-doubling for power-of-two rank counts and inputs of at
@@ -155,62 +167,33 @@ bool ranks_ok_for(vrc_mode_t m, int n)
     return (n & (n - 1)) == 0;
 }
 
-}  // namespace
-
-// ============================================================================
-// C ABI
-// ============================================================================
-extern "C" {
-
-vrc_status_t vrc_plan(vrc_coll_t coll, const void* const* send, void* const* recv, int nranks, size_t count,
-                      size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_op_desc* ops, int cap, int* n_ops,
-                      int* n_launches)
-{
-    if (!n_ops || !n_launches || cap < 0 || (cap > 0 && !ops)) return VRC_ERR_INVALID_ARG;
-    Plan plan = {ops, cap, 0, 0};
-    g_plan = &plan;
-    vrc_status_t rc = VRC_ERR_UNSUPPORTED;
-    switch (coll) {
-    case VRC_COLL_ALLREDUCE: rc = vrc_allreduce(send, recv, nranks, count, dtype, VRC_SUM, mode, nullptr); break;
-    case VRC_COLL_REDUCE_SCATTER:
-        rc = vrc_reduce_scatter(send, recv, nranks, count, outer, dtype, VRC_SUM, mode, nullptr);
-        break;
-    case VRC_COLL_ALL_GATHER: rc = vrc_all_gather(send, recv, nranks, count, outer, dtype, mode, nullptr); break;
-    case VRC_COLL_ALLREDUCE_BUCKETED:
-        rc = vrc_allreduce_bucketed(send, recv, nranks, count, dtype, VRC_SUM, mode, outer, nullptr, 0, nullptr);
-        break;
-    }
-    g_plan = nullptr;
-    *n_ops = plan.n;
-    *n_launches = plan.launches;
-    if (rc == VRC_OK && plan.n > cap) return VRC_ERR_INVALID_ARG;
-    return rc;
-}
-
-vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
-                           vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, vrc_stream_t stream)
+// The collectives, on validated int arguments (see raw()).
+vrc_status_t allreduce_impl(const void* const* send, void* const* recv, int nranks, size_t count, int dtype, int op,
+                            int mode_raw, hipStream_t stream)
 {
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
-    if (op != VRC_SUM || !mode_ok(mode) || mode == VRC_TREE) return VRC_ERR_UNSUPPORTED;
-    const uint64_t bytes = (uint64_t)count * (uint64_t)esize(dtype);
-    mode = resolve_mode(mode, nranks, bytes, Coll::AR);
+    if (op != VRC_SUM || !mode_valid(mode_raw) || mode_raw == VRC_TREE) return VRC_ERR_UNSUPPORTED;
+    const vrc_dtype_t dt = static_cast<vrc_dtype_t>(dtype);
+    const uint64_t bytes = (uint64_t)count * (uint64_t)esize(dt);
+    const vrc_mode_t mode = resolve_mode(static_cast<vrc_mode_t>(mode_raw), nranks, bytes, Coll::AR);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     uint64_t rb[kMaxRanks];
     for (int r = 0; r < nranks; r++) rb[r] = bytes;
     rc = check_buffers(send, recv, nranks, bytes, rb, true);
     if (rc) return rc;
     if (count == 0) return VRC_OK;
-    return run(Coll::AR, mode, dtype, send, recv, nranks, count, 1, (hipStream_t)stream);
+    return run(Coll::AR, mode, dt, send, recv, nranks, count, 1, stream);
 }
 
-vrc_status_t vrc_allreduce_bucketed(const void* const* send, void* const* recv, int nranks, size_t count,
-                                    vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, size_t bucket,
-                                    const vrc_event_t* ready, int nready, vrc_stream_t stream)
+vrc_status_t bucketed_impl(const void* const* send, void* const* recv, int nranks, size_t count, int dtype, int op,
+                           int mode_raw, size_t bucket, const vrc_event_t* ready, int nready, hipStream_t stream)
 {
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
-    if (op != VRC_SUM || !mode_ok(mode) || mode == VRC_TREE) return VRC_ERR_UNSUPPORTED;
+    if (op != VRC_SUM || !mode_valid(mode_raw) || mode_raw == VRC_TREE) return VRC_ERR_UNSUPPORTED;
+    const vrc_dtype_t dt = static_cast<vrc_dtype_t>(dtype);
+    const vrc_mode_t mode = static_cast<vrc_mode_t>(mode_raw);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (bucket == 0) return VRC_ERR_INVALID_ARG;
     const uint64_t nb = count == 0 ? 0 : (count - 1) / bucket + 1;
@@ -218,7 +201,7 @@ vrc_status_t vrc_allreduce_bucketed(const void* const* send, void* const* recv, 
     if (ready)
         for (uint64_t k = 0; k < nb; k++)
             if (!ready[k]) return VRC_ERR_INVALID_ARG;
-    const int E = esize(dtype);
+    const int E = esize(dt);
     uint64_t rb[kMaxRanks];
     for (int r = 0; r < nranks; r++) rb[r] = (uint64_t)count * E;
     rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, true);
@@ -228,28 +211,28 @@ vrc_status_t vrc_allreduce_bucketed(const void* const* send, void* const* recv, 
     for (uint64_t k = 0; k < nb; k++) {
         const uint64_t off = k * bucket, len = count - off < bucket ? count - off : bucket;
         if (ready && !g_plan) {
-            const hipError_t e = hipStreamWaitEvent((hipStream_t)stream, (hipEvent_t)ready[k], 0);
+            const hipError_t e = hipStreamWaitEvent(stream, (hipEvent_t)ready[k], 0);
             if (e != hipSuccess) return hip_fail(e);
         }
         for (int r = 0; r < nranks; r++) {
             xs[r] = static_cast<const char*>(send[r]) + off * E;
             ys[r] = static_cast<char*>(recv[r]) + off * E;
         }
-        rc = run(Coll::AR, resolve_mode(mode, nranks, len * E, Coll::AR), dtype, xs, ys, nranks, len, 1, (hipStream_t)stream);
+        rc = run(Coll::AR, resolve_mode(mode, nranks, len * E, Coll::AR), dt, xs, ys, nranks, len, 1, stream);
         if (rc) return rc;
     }
     return VRC_OK;
 }
 
-vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int nranks, size_t count,
-                                size_t outer, vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode,
-                                vrc_stream_t stream)
+vrc_status_t reduce_scatter_impl(const void* const* send, void* const* recv, int nranks, size_t count, size_t outer,
+                                 int dtype, int op, int mode_raw, hipStream_t stream)
 {
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
-    if (op != VRC_SUM || !mode_ok(mode) || mode == VRC_TREE) return VRC_ERR_UNSUPPORTED;
-    const int E = esize(dtype);
-    mode = resolve_mode(mode, nranks, (uint64_t)count * E, Coll::RS);
+    if (op != VRC_SUM || !mode_valid(mode_raw) || mode_raw == VRC_TREE) return VRC_ERR_UNSUPPORTED;
+    const vrc_dtype_t dt = static_cast<vrc_dtype_t>(dtype);
+    const int E = esize(dt);
+    const vrc_mode_t mode = resolve_mode(static_cast<vrc_mode_t>(mode_raw), nranks, (uint64_t)count * E, Coll::RS);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     if (outer > 1 && (count / outer) % (uint64_t)nranks != 0) return VRC_ERR_INVALID_ARG;
@@ -266,17 +249,18 @@ vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int 
     rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, false);
     if (rc) return rc;
     if (count == 0) return VRC_OK;
-    return run(Coll::RS, mode, dtype, send, recv, nranks, count, outer, (hipStream_t)stream);
+    return run(Coll::RS, mode, dt, send, recv, nranks, count, outer, stream);
 }
 
-vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nranks, size_t count,
-                            size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_stream_t stream)
+vrc_status_t all_gather_impl(const void* const* send, void* const* recv, int nranks, size_t count, size_t outer,
+                             int dtype, int mode_raw, hipStream_t stream)
 {
     vrc_status_t rc = check_common(send, recv, nranks, count, dtype);
     if (rc) return rc;
-    if (!mode_ok(mode)) return VRC_ERR_UNSUPPORTED;
-    const int E = esize(dtype);
-    mode = resolve_mode(mode, nranks, (uint64_t)count * E, Coll::AG);
+    if (!mode_valid(mode_raw)) return VRC_ERR_UNSUPPORTED;
+    const vrc_dtype_t dt = static_cast<vrc_dtype_t>(dtype);
+    const int E = esize(dt);
+    const vrc_mode_t mode = resolve_mode(static_cast<vrc_mode_t>(mode_raw), nranks, (uint64_t)count * E, Coll::AG);
     if (!ranks_ok_for(mode, nranks)) return VRC_ERR_INVALID_ARG;
     if (outer == 0 || count % outer != 0) return VRC_ERR_INVALID_ARG;
     uint64_t rb[kMaxRanks];
@@ -284,7 +268,66 @@ vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nran
     rc = check_buffers(send, recv, nranks, (uint64_t)count * E, rb, false);
     if (rc) return rc;
     if (count == 0) return VRC_OK;
-    return run(Coll::AG, mode, dtype, send, recv, nranks, count, outer, (hipStream_t)stream);
+    return run(Coll::AG, mode, dt, send, recv, nranks, count, outer, stream);
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+vrc_status_t vrc_plan(vrc_coll_t coll, const void* const* send, void* const* recv, int nranks, size_t count,
+                      size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_op_desc* ops, int cap, int* n_ops,
+                      int* n_launches)
+{
+    if (!n_ops || !n_launches || cap < 0 || (cap > 0 && !ops)) return VRC_ERR_INVALID_ARG;
+    Plan plan = {ops, cap, 0, 0};
+    g_plan = &plan;
+    vrc_status_t rc = VRC_ERR_UNSUPPORTED;
+    const int dt = raw(dtype), md = raw(mode);
+    switch (raw(coll)) {
+    case VRC_COLL_ALLREDUCE: rc = allreduce_impl(send, recv, nranks, count, dt, VRC_SUM, md, nullptr); break;
+    case VRC_COLL_REDUCE_SCATTER: rc = reduce_scatter_impl(send, recv, nranks, count, outer, dt, VRC_SUM, md, nullptr); break;
+    case VRC_COLL_ALL_GATHER: rc = all_gather_impl(send, recv, nranks, count, outer, dt, md, nullptr); break;
+    case VRC_COLL_ALLREDUCE_BUCKETED:
+        rc = bucketed_impl(send, recv, nranks, count, dt, VRC_SUM, md, outer, nullptr, 0, nullptr);
+        break;
+    default: break;
+    }
+    g_plan = nullptr;
+    *n_ops = plan.n;
+    *n_launches = plan.launches;
+    if (rc == VRC_OK && plan.n > cap) return VRC_ERR_INVALID_ARG;
+    return rc;
+}
+
+vrc_status_t vrc_allreduce(const void* const* send, void* const* recv, int nranks, size_t count,
+                           vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, vrc_stream_t stream)
+{
+    return allreduce_impl(send, recv, nranks, count, raw(dtype), raw(op), raw(mode), (hipStream_t)stream);
+}
+
+vrc_status_t vrc_allreduce_bucketed(const void* const* send, void* const* recv, int nranks, size_t count,
+                                    vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode, size_t bucket,
+                                    const vrc_event_t* ready, int nready, vrc_stream_t stream)
+{
+    return bucketed_impl(send, recv, nranks, count, raw(dtype), raw(op), raw(mode), bucket, ready, nready,
+                         (hipStream_t)stream);
+}
+
+vrc_status_t vrc_reduce_scatter(const void* const* send, void* const* recv, int nranks, size_t count,
+                                size_t outer, vrc_dtype_t dtype, vrc_op_t op, vrc_mode_t mode,
+                                vrc_stream_t stream)
+{
+    return reduce_scatter_impl(send, recv, nranks, count, outer, raw(dtype), raw(op), raw(mode), (hipStream_t)stream);
+}
+
+vrc_status_t vrc_all_gather(const void* const* send, void* const* recv, int nranks, size_t count,
+                            size_t outer, vrc_dtype_t dtype, vrc_mode_t mode, vrc_stream_t stream)
+{
+    return all_gather_impl(send, recv, nranks, count, outer, raw(dtype), raw(mode), (hipStream_t)stream);
 }
 
 vrc_status_t vrc_chunk_range(size_t count, int nranks, int chunk, size_t* offset, size_t* length)
@@ -299,7 +342,7 @@ vrc_status_t vrc_chunk_range(size_t count, int nranks, int chunk, size_t* offset
 
 const char* vrc_status_string(vrc_status_t status)
 {
-    switch (status) {
+    switch (raw(status)) {
     case VRC_OK: return "VRC_OK: success";
     case VRC_ERR_INVALID_ARG: return "VRC_ERR_INVALID_ARG: invalid argument (null pointer, nranks or shape)";
     case VRC_ERR_UNSUPPORTED: return "VRC_ERR_UNSUPPORTED: unknown dtype, op or mode";
