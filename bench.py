@@ -814,6 +814,23 @@ def main() -> int:
                 extra[f"{other}_mode"]["note"] = "bytes issued; L2 serves the partial re-reads"
             log(f"{other} mode: {extra[f'{other}_mode']}")
 
+        # In place (every rank's output is its input), as a data-parallel gradient all-reduce calls it.
+        # It runs on copies, so the timed inputs stay as drawn; each call's sums feed the next call.
+        zs = [x.clone() for x in xs]
+
+        def step_in_place():
+            vrc.vrc_allreduce(zs, recv=zs, mode=args.mode)
+
+        k4 = max(3, min(args.steps, 10))
+        wall4, kms4 = time_calls(step_in_place, k4, 2, torch)
+        kavg4 = sum(kms4) / len(kms4)
+        extra["in_place"] = {"steps": k4, "ms_per_step": round(wall4 * 1e3 / k4, 5), "kernel_ms_avg": round(kavg4, 5),
+                             "GB_per_s": round(nbytes / (kavg4 * 1e-3) / 1e9, 2),
+                             "note": "recv = send on copies of the inputs; timing only (the sums compound)"}
+        log(f"in place: {extra['in_place']}")
+        zs = None
+        torch.cuda.empty_cache()
+
         # The same bytes moved by the runtime's own device copy, on the same buffers in the same process:
         # how close the kernel comes to what this machine's HBM gives a plain N-in/N-out stream.
         def copy_step():
