@@ -160,10 +160,16 @@ def plan(coll: int, send, recv, count: int, outer: int, dtype: int, mode: int):
     a list of dicts with launch, kind, a, b, d, rows, width, strides and the
     launch geometry (grid_x, grid_y, block, vectors) for a 256-CU device."""
     cap = 4096
-    ops = (OpDesc * cap)()
     n_ops, n_launches = C.c_int(), C.c_int()
-    st = _lib.vrc_plan(coll, _ptr_array(send), _ptr_array(recv), len(send), count, outer, dtype, mode, ops, cap,
-                       C.byref(n_ops), C.byref(n_launches))
+    while True:
+        ops = (OpDesc * cap)()
+        st = _lib.vrc_plan(coll, _ptr_array(send), _ptr_array(recv), len(send), count, outer, dtype, mode, ops, cap,
+                           C.byref(n_ops), C.byref(n_launches))
+        # A plan longer than `cap` reports its full length: ask again with room for all of it.
+        if st == VRC_ERR_INVALID_ARG and n_ops.value > cap:
+            cap = n_ops.value
+            continue
+        break
     if st != VRC_OK:
         raise VrcError(st, "vrc_plan")
     out = []
