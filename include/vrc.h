@@ -75,7 +75,11 @@
  *               offsets cost some bandwidth: about 5-10 % for the all-reduce
  *               with every input and output on its own offset; about 45 %
  *               for VRC_RING_CHAINED, whose partials keep the reference grid.
- *   Errors      Argument errors return before anything is enqueued.
+ *   Errors      Argument errors return before anything is enqueued.  After
+ *               each launch the library reads (and so clears) the calling
+ *               thread's last HIP error: a failed launch returns VRC_ERR_HIP
+ *               with its code in vrc_last_hip_error(), and so does an error
+ *               that an earlier HIP call left pending on the thread.
  *   Threads     Calls are re-entrant and thread-safe; calls that overlap on
  *               the same buffers race like any two kernels would.
  *   Runtime     The library calls the HIP runtime (libamdhip64.so.7) that is
