@@ -639,6 +639,12 @@ PROFILE_ROWS = (
     ("all_gather_fp16_n8_heads", "fused"), ("all_gather_fp16_n8_heads", "ring"),
     ("reduce_scatter_fp16_n8_act", "fused"), ("reduce_scatter_fp16_n8_act", "ring"),
 )
+# The headline all-reduce with every operand on its own offset (rank r's input r elements and its output
+# 3r mod 8 elements into fresh buffers, as in --offsets), in every all-reduce mode: the single-launch modes
+# run their realigned kernels here.
+OFFSET_SUFFIX = "+offsets"
+PROFILE_OFFSET_ROWS = tuple(("allreduce_bf16_n8_512mib" + OFFSET_SUFFIX, m)
+                            for m in ("fused", "hd_order", "ring_order", "ring_chained", "ring"))
 
 
 def run_profile_case(case: str, steps: int, torch, vrc, workloads) -> int:
@@ -647,23 +653,33 @@ def run_profile_case(case: str, steps: int, torch, vrc, workloads) -> int:
     then belong to the case whose line was printed last before them, and the
     flush's fill kernel separates the calls.  `case` is WORKLOAD[@COUNT]:MODE
     (COUNT overrides the per-rank element count, as the sweep sizes of a
-    workload), several joined by commas, or "rows" for PROFILE_ROWS.  One
-    JSON line per case, printed (and flushed) before its calls."""
+    workload; a "+offsets" suffix on an all-reduce workload puts every
+    operand on its own offset, as --offsets does), several joined by commas,
+    "rows" for PROFILE_ROWS or "offsets" for PROFILE_OFFSET_ROWS.  One JSON
+    line per case, printed (and flushed) before its calls."""
     dev = "cuda:0"
-    cases = PROFILE_ROWS if case == "rows" else tuple(tuple(c.split(":")) for c in case.split(","))
+    cases = {"rows": PROFILE_ROWS, "offsets": PROFILE_OFFSET_ROWS}.get(case)
+    cases = cases or tuple(tuple(c.split(":")) for c in case.split(","))
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     loaded = xs = outs = None
     for idx, (name, mode) in enumerate(cases):
-        base, count = (name.split("@") + [None])[:2]
+        shifted = name.endswith(OFFSET_SUFFIX)
+        plain = name[:len(name) - len(OFFSET_SUFFIX)] if shifted else name
+        base, count = (plain.split("@") + [None])[:2]
         w = workloads.WORKLOADS[base]
         if count is not None:
             w = w.with_count(int(count))
+        if shifted and w.collective != "allreduce":
+            raise ValueError(f"{name}: operand offsets are profiled for all-reduce workloads only")
         if loaded is None or loaded[0] != name:
             loaded = xs = outs = call = None  # drop the previous workload's buffers before allocating the next
             torch.cuda.empty_cache()
             xs = workloads.make_inputs(w, dev)
             if w.collective == "allreduce":
                 outs = [torch.empty_like(x) for x in xs]
+                if shifted:
+                    xs = offset_views(torch, xs, list(range(w.n)))
+                    outs = offset_views(torch, outs, [3 * r % 8 for r in range(w.n)])
             elif w.collective == "reduce_scatter":
                 outs = vrc.vrc_reduce_scatter(xs, dim=w.dim)
             else:
@@ -717,8 +733,8 @@ def main() -> int:
                     help="time the headline all-reduce and the heads all-gather beside read-only, write-only "
                          "and copy passes over the same bytes")
     ap.add_argument("--profile-case", default=None,
-                    help="WORKLOAD[@COUNT]:MODE[,...] or 'rows' -- run only these collectives `--steps` times "
-                         "each (for counter passes)")
+                    help="WORKLOAD[@COUNT][+offsets]:MODE[,...], 'rows' or 'offsets' -- run only these "
+                         "collectives `--steps` times each (for counter passes)")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run torch's device copy of 1 GiB (known HBM traffic: 1 GiB read, 1 GiB "
                          "written per launch), for calibrating rocprofv3 byte counters")

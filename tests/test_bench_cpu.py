@@ -98,3 +98,16 @@ def test_profile_rows_name_real_workloads_and_modes():
         seen.add((base, mode))
     for base in workloads.WORKLOADS:
         assert (base, "fused") in seen and (base, "ring") in seen
+
+
+def test_profile_offset_rows_are_headline_all_reduces():
+    """The mixed-offset counter rows run the headline workload, with every
+    operand on its own offset, in every all-reduce mode that has its own
+    kernel family (the realigned ones among them)."""
+    import ring_all_reduce_virtual_amd as vrc
+    modes = set()
+    for name, mode in bench.PROFILE_OFFSET_ROWS:
+        assert name == workloads.HEADLINE + bench.OFFSET_SUFFIX
+        assert mode in vrc.REDUCE_MODES
+        modes.add(mode)
+    assert {"fused", "hd_order", "ring_order", "ring_chained", "ring"} <= modes
