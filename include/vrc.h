@@ -96,7 +96,7 @@
 extern "C" {
 #endif
 
-#define VRC_VERSION 104 /* 1.0.4: realigned fused all-reduce launches in vrc_plan */
+#define VRC_VERSION 105 /* 1.0.5: phased fused all-reduce launches in vrc_plan */
 #define VRC_MAX_RANKS 16
 
 struct ihipStream_t;
@@ -305,7 +305,9 @@ typedef enum {
     VRC_OP_BUTTERFLY_REDUCE_SCATTER = 11,
     VRC_OP_FUSED_ALLREDUCE_REALIGNED = 12,   /* VRC_FUSED, outputs on different 128-byte offsets */
     VRC_OP_BUTTERFLY_ALLREDUCE_REALIGNED = 13, /* VRC_HD_ORDER, outputs on different 128-byte offsets */
-    VRC_OP_RING_ORDER_ALLREDUCE_REALIGNED = 14 /* VRC_RING_ORDER, outputs on different 128-byte offsets */
+    VRC_OP_RING_ORDER_ALLREDUCE_REALIGNED = 14, /* VRC_RING_ORDER, outputs on different 128-byte offsets */
+    VRC_OP_FUSED_ALLREDUCE_PHASED = 15,     /* VRC_FUSED, large calls from 6 ranks: read, then write, by phases */
+    VRC_OP_BUTTERFLY_ALLREDUCE_PHASED = 16  /* VRC_HD_ORDER, the same at 8 and 16 ranks */
 } vrc_op_kind_t;
 
 typedef struct {

@@ -94,6 +94,8 @@ struct Tuning {
     int chain_block;          // 0: policy; else lanes per single-launch ring all-reduce workgroup (64 or 256)
     int step_block;           // 0: size policy; else lanes per step workgroup (64, with one vector per lane, or 256)
     int realign;              // 1: outputs on different 128-byte offsets take the realigned fused kernel; 0: never
+    int phased;               // 1: large fused all-reduces take the phased kernel (phased_phases); 0: never
+    int phase_wait;           // 1: the phased kernel's workgroups meet between phases; 0: they never wait
 };
 
 inline const Tuning& tuning()
@@ -103,7 +105,8 @@ inline const Tuning& tuning()
                              env_int("VRC_CHAIN_BLOCKS_PER_CU", 0, 1, 64), env_int("VRC_UNROLL", 0, 1, 8),
                              env_int("VRC_STEP_NT", -1, 0, 2), env_int("VRC_STEP_UNROLL", 0, 1, 2),
                              env_int("VRC_FUSED_BLOCK", 0, 64, 256), env_int("VRC_CHAIN_BLOCK", 0, 64, 256),
-                             env_int("VRC_STEP_BLOCK", 0, 64, 256), env_int("VRC_REALIGN", 1, 0, 1)};
+                             env_int("VRC_STEP_BLOCK", 0, 64, 256), env_int("VRC_REALIGN", 1, 0, 1),
+                             env_int("VRC_PHASED", 1, 0, 1), env_int("VRC_PHASE_WAIT", 1, 0, 1)};
     return t;
 }
 
@@ -202,6 +205,36 @@ inline FusedShape fused_ar_shape(uint64_t bytes_moved, int n, bool outputs_share
 // per rank count: the largest U <= 8 with U x N <= 32, at least 2 (a group
 // of U tiles re-reads 128 bytes of the next group, 1/(8U) of its reads).
 constexpr int realign_unroll(int n) { return 8 * n <= 32 ? 8 : (4 * n <= 32 ? 4 : 2); }
+
+// The phased fused all-reduce (k_fused_allreduce_phased): sums held per lane
+// between a phase's reads and its writes, in registers (64 up to 8 ranks;
+// 32 above, where the N loads in flight need the room) and in LDS (32:
+// 128 KiB per workgroup).  The butterfly of 16-bit types rounds every
+// partial and keeps more values live: 32 and 16.  More would spill to
+// memory (the compiler then stops using the AGPRs).
+constexpr int phased_regs(int n, bool narrow_butterfly = false)
+{
+    return narrow_butterfly ? (n <= 8 ? 32 : 16) : (n <= 8 ? 64 : 32);
+}
+constexpr int kPhasedLds = 32;
+
+// Whole phases of the phased kernel for `nvb` vectors per rank, or 0 where
+// the one-wave kernel stays.  A phase reads N x 256 lanes per CU x K
+// vectors: 576 MiB at 6 ranks, 768 MiB at 8, 1 GiB at 16 on 256 CUs (the
+// 16-bit butterfly: 512 MiB at 8, 768 MiB at 16).  It
+// runs from 6 ranks and at least 3 whole phases.  Measured on MI355X against
+// the one-wave kernel, bf16, bit-identical outputs (time ratio, one process,
+// four interleaved rounds): 8 x 512 MiB 0.946-0.963, 8 x 1 GiB 0.935,
+// 12 x 341 MiB 0.860, 6 x 682 MiB 0.954, 16 x 256 MiB 0.973; and where it is
+// not taken, 8 x 256 MiB 0.969 (2 phases), 8 x 128 MiB 1.003 (1),
+// 16 x 128 MiB 1.008 (2), 4 x 512 MiB 1.030 (384 MiB phases).
+inline uint64_t phased_phases(int n, uint64_t nvb, int cus, bool narrow_butterfly = false)
+{
+    if (!tuning().phased || n < 6) return 0;
+    const uint64_t per_phase = (uint64_t)cus * kBlock * (uint64_t)(phased_regs(n, narrow_butterfly) + kPhasedLds);
+    const uint64_t p = nvb / per_phase;
+    return p >= 3 ? p : 0;
+}
 
 // Workgroups per CU of the realigned fused all-reduce: 64 / (U x N) rounded
 // down to a power of two, at least 1.

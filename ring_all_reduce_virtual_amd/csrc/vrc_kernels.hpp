@@ -315,6 +315,130 @@ __global__ __launch_bounds__(B) void k_fused_allreduce(FusedArArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Phased fused all-reduce: one 256-lane workgroup per CU, one wave per SIMD.
+// Half reads and half writes make the DRAM turn its bus around between read
+// and write bursts, and writes held in the Infinity Cache behind L2 drain
+// among later reads unless a run of writes is much longer than that cache.
+// So every lane folds K = KR + KL vectors of every input (KR sums held in
+// registers, KL in LDS; N * K * 16 bytes of reads per lane, 0.5-1 GiB per
+// phase over the grid), the grid meets, and every lane then writes its K
+// sums to all N outputs.
+//
+// The meeting only shapes the timing: a lane reads and writes its own
+// vectors only, so a late or skipped meeting cannot change any result.  A
+// workgroup waits at most as long as its own read phase took (at least
+// kPhaseWaitFloor ticks); one that gives up once stops waiting for the rest
+// of the launch, so a grid that is not all resident (a busy GPU, another
+// such launch at the same time) costs bounded time and finishes.
+// ---------------------------------------------------------------------------
+
+// Arrivals at the phased kernels' meetings on this device since the library
+// was loaded (64 bits: never wraps).  Every launch has one workgroup per CU,
+// G of them, and each adds G per meeting, so between launches the count is a
+// multiple of G and count / G numbers the meetings.  Each translation unit
+// (one per element type) has its own count.
+static __device__ unsigned long long g_phase_arrivals;
+
+// 20 us of the 100 MHz wall clock gfx950 reports.
+constexpr uint64_t kPhaseWaitFloor = 2000;
+
+__device__ __forceinline__ void phase_meet(uint64_t G, uint64_t limit, bool& waiting)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned long long seen =
+            __hip_atomic_fetch_add(&g_phase_arrivals, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (waiting) {
+            const unsigned long long all = (seen / G + 1) * G;
+            const uint64_t t0 = wall_clock64();
+            while (__hip_atomic_load(&g_phase_arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < all) {
+                if (wall_clock64() - t0 > limit) {
+                    waiting = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Vector v of a phase belongs to lane ((w * G + b) * 64 + l) for wave w of
+// workgroup b, lane l, so consecutive 1 KiB tiles go to consecutive
+// workgroups (consecutive XCDs), as in the one-wave kernel above.  The
+// vectors after the last whole phase and the scalar head and tail follow
+// with the grid-stride loops.  `wait` = 0 skips every meeting.
+template <class T, int N, int KR, int KL, bool NT, class Fold = RankFold>
+__global__ __launch_bounds__(kBlock, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fused_allreduce_phased(FusedArArgs a, uint64_t phases, uint32_t wait)
+{
+    constexpr int K = KR + KL;
+    __shared__ u32x4 held[KL * kBlock];
+    const uint64_t G = gridDim.x;
+    const uint64_t L = G * kBlock;
+    const uint64_t lane = (((uint64_t)(threadIdx.x >> 6)) * G + blockIdx.x) * 64 + (threadIdx.x & 63);
+    constexpr uint64_t E = T::ESZ;
+    const uint64_t body = a.g.head * E;
+    bool waiting = wait != 0;
+
+    for (uint64_t p = 0; p < phases; p++) {
+        const uint64_t base = p * L * K + lane;
+        const uint64_t t_read = wall_clock64();
+        u32x4 s[KR];
+#pragma unroll
+        for (int k = 0; k < KR; k++) {
+            u32x4 in[N];
+#pragma unroll
+            for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + (base + k * L) * 16);
+            issue_loads_first();
+            s[k] = Fold::template vec<T, N>(in);
+            __asm__ __volatile__("" : "+v"(s[k]));  // keep the sum in a register until the write phase
+        }
+#pragma unroll
+        for (int k = 0; k < KL; k++) {
+            u32x4 in[N];
+#pragma unroll
+            for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + (base + (KR + k) * L) * 16);
+            issue_loads_first();
+            held[k * kBlock + threadIdx.x] = Fold::template vec<T, N>(in);
+        }
+        const uint64_t took = wall_clock64() - t_read;
+        phase_meet(G, took > kPhaseWaitFloor ? took : kPhaseWaitFloor, waiting);
+#pragma unroll
+        for (int k = 0; k < KR; k++)
+#pragma unroll
+            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + (base + k * L) * 16, s[k]);
+#pragma unroll
+        for (int k = 0; k < KL; k++) {
+            const u32x4 f = held[k * kBlock + threadIdx.x];
+#pragma unroll
+            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + (base + (KR + k) * L) * 16, f);
+        }
+    }
+
+    for (uint64_t v = phases * L * K + lane; v < a.g.nvb; v += L) {
+        u32x4 in[N];
+#pragma unroll
+        for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
+        issue_loads_first();
+        const u32x4 f = Fold::template vec<T, N>(in);
+#pragma unroll
+        for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, f);
+    }
+
+    const uint64_t ns = a.g.head + a.g.tail;
+    for (uint64_t k = (uint64_t)blockIdx.x * kBlock + threadIdx.x; k < ns; k += L) {
+        const uint64_t i = (k < a.g.head) ? k : a.g.head + a.g.nvb * T::VEC + (k - a.g.head);
+        typename T::S in[N];
+#pragma unroll
+        for (int r = 0; r < N; r++) in[r] = load_s<T>(a.src[r] + i * E);
+        const typename T::S s = Fold::template scalar<T, N>(in);
+#pragma unroll
+        for (int r = 0; r < N; r++) store_s<T>(a.dst[r] + i * E, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fused all-reduce for outputs on different 128-byte offsets (one-wave
 // workgroups, no output overlapping an input).  The loads follow one
 // reference grid; output r is stored `shift[r]` bytes later, on its own

@@ -300,6 +300,43 @@ struct Launch {
         return check_launch();
     }
 
+    // The phased fused all-reduce: one 256-lane workgroup per CU, `phases`
+    // whole phases (phased_phases), then the rest of the vectors and the
+    // scalar head and tail.
+    template <class Fold>
+    static vrc_status_t fused_allreduce_phased(const vrc::FusedArArgs& a, int n, uint64_t count, uint64_t phases,
+                                               int cus, hipStream_t st)
+    {
+        constexpr bool butterfly = std::is_same<Fold, vrc::Butterfly>::value;
+        constexpr bool nb = butterfly && T::ESZ == 2;
+        const dim3 grid((unsigned)cus);
+        if (g_plan)
+            return plan_single(butterfly ? VRC_OP_BUTTERFLY_ALLREDUCE_PHASED : VRC_OP_FUSED_ALLREDUCE_PHASED, count,
+                               grid, kBlock, phased_regs(n, nb) + kPhasedLds);
+        const uint32_t wait = (uint32_t)tuning().phase_wait;
+#define VRC_PHASED(K)                                                                                                 \
+    hipLaunchKernelGGL((vrc::k_fused_allreduce_phased<T, K, phased_regs(K, nb), kPhasedLds, true, Fold>), grid,    \
+                       dim3(kBlock), 0, st, a, phases, wait)
+        if constexpr (butterfly) {
+            switch (n) {
+            case 8: VRC_PHASED(8); break;
+            case 16: VRC_PHASED(16); break;
+            default: return VRC_ERR_INVALID_ARG;
+            }
+        } else {
+            switch (n) {
+#define VRC_CASE(K) \
+    case K: VRC_PHASED(K); break;
+                VRC_CASE(6) VRC_CASE(7) VRC_CASE(8) VRC_CASE(9) VRC_CASE(10) VRC_CASE(11) VRC_CASE(12) VRC_CASE(13)
+                VRC_CASE(14) VRC_CASE(15) VRC_CASE(16)
+#undef VRC_CASE
+            default: return VRC_ERR_INVALID_ARG;
+            }
+        }
+#undef VRC_PHASED
+        return check_launch();
+    }
+
     template <class Fold = vrc::RankFold>
     static vrc_status_t fused_allreduce(const char* const* x, char* const* y, int n, uint64_t count, int cus,
                                         hipStream_t st)
@@ -322,6 +359,14 @@ struct Launch {
         bool share = true;  // every output on the vector grid
         for (int r = 0; r < n; r++)
             if (out[r] % kGridAlign != ref % kGridAlign) share = false;
+        if (share) {
+            // Every output on one 128-byte grid: large calls read and write in
+            // phases (the butterfly needs a power of two: 8 or 16 ranks here).
+            constexpr bool butterfly = std::is_same<Fold, vrc::Butterfly>::value;
+            const bool fold_ok = !butterfly || n == 8 || n == 16;
+            const uint64_t phases = fold_ok ? phased_phases(n, a.g.nvb, cus, butterfly && T::ESZ == 2) : 0;
+            if (phases) return fused_allreduce_phased<Fold>(a, n, count, phases, cus, st);
+        }
         const uint64_t work = a.g.nvb > a.g.head + a.g.tail ? a.g.nvb : a.g.head + a.g.tail;
         const FusedShape sh = fused_ar_shape(2 * (uint64_t)n * count * E, n, share);
         if (!share && sh.block == 64 && tuning().realign) {

@@ -10,11 +10,13 @@ sources), and checks what the kernels are meant to be:
   all-reduce kernels of 10 ranks and up that hold more than 256 registers;
   every kernel is compiled for 64-lane waves;
 * LDS is used only by the realigned all-reduce kernels, at most 8,320 bytes
-  per workgroup (one group of sums);
+  per workgroup (one group of sums), and by the phased ones, 128 KiB (32
+  sums per lane);
 * every vector memory access is a global_* or ds_* instruction: no flat_
   access (it would count against the LDS counter and force coarser waits),
-  and no store or atomic of any other kind (the scalar unit only loads the
-  kernel arguments);
+  and no store or atomic of any other kind than global stores and the
+  phased kernels' 64-bit atomic add of their meeting count (the scalar unit
+  only loads the kernel arguments and reads the clock);
 * the headline kernel (bf16, 8 ranks, one-wave workgroups, one tile per
   wave) fits 128 VGPRs, so four of its workgroups per CU run as one wave
   per SIMD with room to spare."""
@@ -97,17 +99,32 @@ def test_no_scratch_no_memory_spills(code_objects):
             assert k["wave"] == 64, k["name"]
             if k["vgpr_spill"] or k["agpr"]:
                 assert k["vgpr_spill"] <= k["agpr"], k["name"]
-                assert "k_fused_allreduce" in k["name"] and k["name"].endswith("ELi256EEEvNS_11FusedArArgsE"), k["name"]
+                assert "k_fused_allreduce" in k["name"] and (k["name"].endswith("ELi256EEEvNS_11FusedArArgsE")
+                                                             or "phased" in k["name"]), k["name"]
     assert total > 1000
 
 
-def test_lds_only_in_the_realigned_kernels(code_objects):
+def test_lds_only_in_the_realigned_and_phased_kernels(code_objects):
     for obj in code_objects:
         for k in kernels(obj):
             if "realigned" in k["name"]:
                 assert 0 < k["lds"] <= 8320, k
+            elif "phased" in k["name"]:
+                assert k["lds"] == 32 * 256 * 16, k  # 32 sums per lane of a 256-lane workgroup
             else:
                 assert k["lds"] == 0, k
+
+
+def test_phased_kernels_fit_one_wave_per_simd(code_objects):
+    """The phased kernels hold their sums in registers: at most 512 (VGPRs and
+    AGPRs together, one wave per SIMD) and none spilled to memory."""
+    found = 0
+    for obj in code_objects:
+        for k in kernels(obj):
+            if "phased" in k["name"]:
+                found += 1
+                assert k["vgpr"] <= 512 and k["private"] == 0, k
+    assert found == 4 * (11 + 2)  # four element types: rank fold at 6-16 ranks, butterfly at 8 and 16
 
 
 def test_memory_instructions_are_global_or_lds(code_objects):
@@ -115,7 +132,9 @@ def test_memory_instructions_are_global_or_lds(code_objects):
         ops = mnemonics(obj)
         assert not [m for m in ops if m.startswith(("flat_", "scratch_", "buffer_"))]
         writes = [m for m in ops if "store" in m or "atomic" in m]
-        assert writes and all(m.startswith("global_store_") for m in writes), sorted(writes)
+        # the phased kernels' meeting count is the one atomic: a 64-bit vector add
+        assert writes and all(m.startswith("global_store_") or m == "global_atomic_add_x2" for m in writes), \
+            sorted(writes)
         loads = [m for m in ops if "load" in m]
         assert all(m.startswith(("global_load_", "s_load_")) for m in loads), sorted(loads)
         lds = [m for m in ops if m.startswith("ds_")]

@@ -83,10 +83,11 @@ FUSED_SHAPES = {2: (2, 8), 3: (2, 4), 4: (1, 8), 5: (2, 2), 6: (2, 2), 7: (2, 2)
 
 @pytest.mark.parametrize("n", list(range(2, 17)))
 def test_fused_allreduce_one_wave_shapes(n):
-    """8 GiB moved: one-wave workgroups taking U consecutive tiles, by rank
-    count: U 8 at 2 per CU (2 ranks), U 4 at 2 (3), U 8 at 1 (4), U 2 at 2
-    (5-7), U 1 at 4 (8) and at 2 (9-16)."""
-    count = (4 << 30) // n // 2 // 64 * 64
+    """2 GiB moved (above 64 MiB, under three phases of the phased kernel):
+    one-wave workgroups taking U consecutive tiles, by rank count: U 8 at 2
+    per CU (2 ranks), U 4 at 2 (3), U 8 at 1 (4), U 2 at 2 (5-7), U 1 at 4
+    (8) and at 2 (9-16)."""
+    count = (1 << 30) // n // 2 // 64 * 64
     bpc, vectors = FUSED_SHAPES.get(n, (2, 1))
     assert vectors * n <= 32
     got = plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_FUSED)
@@ -175,7 +176,7 @@ def test_realigned_only_where_outputs_differ_modulo_128(dtype):
     send, recv = wide(n)
     shared = [a + 128 * (r % 2) for r, a in enumerate(recv)]
     assert launches(vrc.plan(vrc.COLL_ALLREDUCE, send, shared, count, 1, dtype, vrc.VRC_FUSED)[0])[0][0] == \
-        "fused_allreduce"
+        "fused_allreduce_phased"  # one grid: no realignment (and large enough to run in phases)
     one_off = list(recv)
     one_off[3] += 64
     assert launches(vrc.plan(vrc.COLL_ALLREDUCE, send, one_off, count, 1, dtype, vrc.VRC_FUSED)[0])[0][0] == \
@@ -186,8 +187,54 @@ def test_realigned_only_where_outputs_differ_modulo_128(dtype):
 
 
 def test_headline_shape():
-    """8 ranks x 512 MiB bf16: 1,024 one-wave workgroups, one vector per rank per lane."""
-    assert plan_ar(8, 268435456, vrc.VRC_BF16, vrc.VRC_FUSED) == [("fused_allreduce", 1024, 1, 64, 1)]
+    """8 ranks x 512 MiB bf16: the phased kernel, one 256-lane workgroup per
+    CU, 96 sums per lane per phase (5 phases)."""
+    assert plan_ar(8, 268435456, vrc.VRC_BF16, vrc.VRC_FUSED) == [("fused_allreduce_phased", 256, 1, 256, 96)]
+
+
+def phased_k(n, dtype=vrc.VRC_BF16, butterfly=False):
+    """Sums per lane per phase: 64 in registers up to 8 ranks, 32 above (16-bit
+    butterfly: 32 and 16), plus 32 in LDS."""
+    narrow = butterfly and ESZ[dtype] == 2
+    regs = (32 if n <= 8 else 16) if narrow else (64 if n <= 8 else 32)
+    return regs + 32
+
+
+@pytest.mark.parametrize("n", list(range(2, 17)))
+def test_phased_from_six_ranks_and_three_phases(n):
+    """8 GiB moved, every output on one 128-byte grid: the phased kernel from
+    6 ranks (there a phase reads 576 MiB or more), the one-wave kernel below."""
+    count = (4 << 30) // n // 2 // 64 * 64
+    got = plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_FUSED)
+    if n >= 6:
+        assert got == [("fused_allreduce_phased", CUS, 1, 256, phased_k(n))]
+    else:
+        assert got[0][0] == "fused_allreduce" and got[0][3] == 64
+    if n in (8, 16):
+        for dtype in (vrc.VRC_BF16, vrc.VRC_FP32):
+            assert plan_ar(n, count * 2 // ESZ[dtype], dtype, vrc.VRC_HD_ORDER) == [
+                ("butterfly_allreduce_phased", CUS, 1, 256, phased_k(n, dtype, butterfly=True))]
+
+
+@pytest.mark.parametrize("n", [6, 8, 16])
+def test_phased_needs_three_whole_phases(n):
+    """Exactly three phases' vectors per rank take the phased kernel; one
+    vector less keeps the one-wave kernel."""
+    per_phase = CUS * 256 * phased_k(n)  # 16-byte vectors
+    at = 3 * per_phase * 8  # bf16 elements
+    assert plan_ar(n, at, vrc.VRC_BF16, vrc.VRC_FUSED)[0][0] == "fused_allreduce_phased"
+    assert plan_ar(n, at - 8, vrc.VRC_BF16, vrc.VRC_FUSED)[0][0] == "fused_allreduce"
+
+
+def test_phased_in_place_and_with_a_ragged_tail():
+    """In place (every output its input, one grid) and with a count that
+    leaves a partial phase, a partial vector and an unaligned head, the
+    phased kernel still runs: its lanes write only what they read."""
+    n = 8
+    count = 268435456 + 12345
+    bufs = [(1 << 40) + r * (1 << 32) + 6 for r in range(n)]
+    ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, bufs, bufs, count, 1, vrc.VRC_BF16, vrc.VRC_FUSED)
+    assert launches(ops) == [("fused_allreduce_phased", CUS, 1, 256, 96)]
 
 
 def test_fused_allreduce_launch_bound_shape_below_64_mib():
@@ -287,7 +334,8 @@ def test_ring_steps_launch_bound_below_64_mib():
 
 
 def test_environment_overrides_reach_the_plan():
-    """VRC_FUSED_BLOCK / VRC_FUSED_BLOCKS_PER_CU / VRC_UNROLL,
+    """VRC_PHASED=0 keeps large fused all-reduces on the grid-stride kernels,
+    whose shape VRC_FUSED_BLOCK / VRC_FUSED_BLOCKS_PER_CU / VRC_UNROLL set;
     VRC_CHAIN_BLOCK / VRC_CHAIN_BLOCKS_PER_CU and VRC_STEP_BLOCK replace the
     policy (read once per process, so a child process checks them)."""
     code = (
@@ -298,7 +346,8 @@ def test_environment_overrides_reach_the_plan():
         "r,_=v.plan(v.COLL_ALLREDUCE,s[:4],d[:4],536870912,1,v.VRC_BF16,v.VRC_RING)\n"
         "print(f[0]['grid_x'],f[0]['block'],f[0]['vectors'],c[0]['grid_x'],c[0]['block'],r[0]['block'])\n")
     env = dict(os.environ, VRC_FUSED_BLOCK="256", VRC_FUSED_BLOCKS_PER_CU="1", VRC_UNROLL="2",
-               VRC_CHAIN_BLOCK="256", VRC_CHAIN_BLOCKS_PER_CU="4", VRC_STEP_BLOCK="256", PYTHONPATH=ROOT)
+               VRC_CHAIN_BLOCK="256", VRC_CHAIN_BLOCKS_PER_CU="4", VRC_STEP_BLOCK="256", VRC_PHASED="0",
+               PYTHONPATH=ROOT)
     out = subprocess.run([sys.executable, "-c", code], env=env, check=True, capture_output=True, text=True,
                          cwd=ROOT).stdout.split()
     assert list(map(int, out)) == [256, 256, 2, 1024, 256, 256]
@@ -367,8 +416,9 @@ def test_mixed_offsets_keep_the_full_grid(mode):
     mixed, nl2 = vrc.plan(vrc.COLL_ALLREDUCE, mixed_send, mixed_recv, count, 1, vrc.VRC_BF16, vrc.MODES[mode])
     assert nl2 == nl
     if mode in ("fused", "hd_order", "ring_order"):
-        # the realigned variants (tests above)
-        assert [k[0] for k in launches(mixed)] == [k[0] + "_realigned" for k in launches(aligned)]
+        # the realigned variants (tests above); the aligned fused and butterfly calls run in phases
+        assert [k[0] for k in launches(mixed)] == [k[0].replace("_phased", "") + "_realigned"
+                                                   for k in launches(aligned)]
     else:
         assert launches(mixed) == launches(aligned)
     for kind, gx, gy, block, vec in launches(mixed):
