@@ -103,7 +103,7 @@
 extern "C" {
 #endif
 
-#define VRC_VERSION 105 /* 1.0.5: phased fused all-reduce launches in vrc_plan */
+#define VRC_VERSION 106 /* 1.0.6: phased fused, butterfly and ring-order all-reduce launches in vrc_plan */
 #define VRC_MAX_RANKS 16
 
 struct ihipStream_t;
@@ -134,8 +134,9 @@ typedef enum { VRC_SUM = 0 } vrc_op_t;
  *                     after it is stored, so the cache serves most of those
  *                     reads.
  *   VRC_RING_ORDER    one launch with the fused traffic (read N, write N):
- *                     the ring's partials stay in registers.  For the
- *                     all-gather it equals VRC_FUSED.
+ *                     the ring's partials stay in registers, in phases from
+ *                     6 ranks as VRC_FUSED.  For the all-gather it equals
+ *                     VRC_FUSED.
  * Halving-doubling [TP] (nranks must be a power of two, else
  * VRC_ERR_INVALID_ARG): recursive halving reduce-scatter with distances N/2,
  * N/4, ..., 1 (rank r pairs with r XOR d, keeps the half of its block range
@@ -321,7 +322,8 @@ typedef enum {
     VRC_OP_BUTTERFLY_ALLREDUCE_REALIGNED = 13, /* VRC_HD_ORDER, outputs on different 128-byte offsets */
     VRC_OP_RING_ORDER_ALLREDUCE_REALIGNED = 14, /* VRC_RING_ORDER, outputs on different 128-byte offsets */
     VRC_OP_FUSED_ALLREDUCE_PHASED = 15,     /* VRC_FUSED, large calls from 6 ranks: read, then write, by phases */
-    VRC_OP_BUTTERFLY_ALLREDUCE_PHASED = 16  /* VRC_HD_ORDER, the same at 8 and 16 ranks */
+    VRC_OP_BUTTERFLY_ALLREDUCE_PHASED = 16, /* VRC_HD_ORDER, the same at 8 and 16 ranks */
+    VRC_OP_RING_ORDER_ALLREDUCE_PHASED = 17 /* VRC_RING_ORDER, the same from 6 ranks */
 } vrc_op_kind_t;
 
 typedef struct {

@@ -53,7 +53,7 @@ class VrcError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 105  # VRC_VERSION of include/vrc.h that these mirrors follow
+ABI_VERSION = 106  # VRC_VERSION of include/vrc.h that these mirrors follow
 
 
 class OpDesc(C.Structure):
@@ -69,7 +69,8 @@ OP_KINDS = {0: "add", 1: "copy", 2: "fused_allreduce", 3: "fused_reduce_scatter"
             5: "chain_allreduce", 6: "chain_reduce_scatter", 7: "chain_all_gather", 8: "ring_order_allreduce",
             9: "ring_order_reduce_scatter", 10: "butterfly_allreduce", 11: "butterfly_reduce_scatter",
             12: "fused_allreduce_realigned", 13: "butterfly_allreduce_realigned",
-            14: "ring_order_allreduce_realigned", 15: "fused_allreduce_phased", 16: "butterfly_allreduce_phased"}
+            14: "ring_order_allreduce_realigned", 15: "fused_allreduce_phased", 16: "butterfly_allreduce_phased",
+            17: "ring_order_allreduce_phased"}
 
 
 def _load():

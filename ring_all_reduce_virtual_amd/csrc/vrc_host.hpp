@@ -7,6 +7,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <type_traits>
 
 #include "vrc.h"
 #include "vrc_kernels.hpp"
@@ -217,6 +218,22 @@ constexpr int phased_regs(int n, bool narrow_butterfly = false)
     return narrow_butterfly ? (n <= 8 ? 32 : 16) : (n <= 8 ? 64 : 32);
 }
 constexpr int kPhasedLds = 32;
+
+// The phased ring-order all-reduce rounds every partial like the butterfly;
+// its per-slot chunk lookup and rank rotation add code to every slot, and
+// past a size the compiler stops unrolling the slot loop, which leaves the
+// register sums in scratch memory.  Sums in registers: per element type and
+// rank count, a count that compiles without scratch (from a sweep over
+// 16-64, less where the 160 KiB of LDS sums below pushed a kernel past 512
+// registers); 40 more per lane (160 KiB per workgroup) in LDS.
+template <class T>
+constexpr int ring_order_phased_regs(int n)
+{
+    if constexpr (std::is_same<T, BF16>::value) return n <= 7 ? 32 : n <= 9 ? 24 : n <= 14 ? 16 : 0;
+    if constexpr (std::is_same<T, F16>::value) return n <= 8 ? 40 : n <= 11 ? 32 : n <= 15 ? 24 : 16;
+    return 40;
+}
+constexpr int kRingOrderPhasedLds = 40;
 
 // Whole phases of the phased kernel for `nvb` vectors per rank, or 0 where
 // the one-wave kernel stays.  A phase reads N x 256 lanes per CU x K

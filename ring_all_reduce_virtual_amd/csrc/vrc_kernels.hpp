@@ -837,6 +837,105 @@ __global__ __launch_bounds__(B) void k_ring_chain_allreduce(ChainArgs a)
     }
 }
 
+// Phased ring-order all-reduce: the phased fused kernel's schedule (one
+// 256-lane workgroup per CU; read K slots, meet, write them) over the tiles
+// of the kernel above.  Slot k of phase p is tile (p K + k) W + w for wave w
+// of the W in the grid, so the chunk, and with it the rank rotation that
+// fixes the ring's fold order, is uniform over a wave's slot.  Lanes past a
+// chunk's last vector (its last tile may be partial) load and fold that last
+// vector and store its sum there again: the bits the owning lane of the same
+// wave stores, which keeps every slot free of branches.  The tiles after the
+// last whole phase take the loop above; so do the scalar heads and tails.
+template <class T, int N, int KR, int KL, bool NT>
+__global__ __launch_bounds__(kBlock, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_ring_order_allreduce_phased(ChainArgs a, uint64_t phases, uint32_t wait)
+{
+    constexpr int K = KR + KL;
+    constexpr uint64_t W = 64;
+    constexpr uint64_t E = T::ESZ;
+    __shared__ u32x4 held[KL * kBlock];
+    const uint64_t G = gridDim.x;
+    const uint64_t WV = G * (kBlock / W);
+    const uint64_t lane = threadIdx.x % W;
+    const uint64_t wave = ((uint64_t)(threadIdx.x / W)) * G + blockIdx.x;
+    bool waiting = wait != 0;
+
+    // Byte offset of a slot's vector in every rank buffer, and its chunk.
+    auto slot = [&](uint64_t t, int& c) {
+        c = __builtin_amdgcn_readfirstlane(range_of<N>(t, a.tile0));
+        const uint64_t nvb = a.ch[c].g.nvb;
+        uint64_t v = (t - a.tile0[c]) * W + lane;
+        v = v < nvb ? v : nvb - 1;
+        return (a.ch[c].off + a.ch[c].g.head) * E + v * 16;
+    };
+    auto fold = [&](int c, uint64_t o) {
+        u32x4 x[N];
+#pragma unroll
+        for (int i = 0; i < N; i++) x[i] = ld16<NT>(a.src[(c + i) % N] + o);
+        issue_loads_first();
+        u32x4 f = x[0];
+#pragma unroll
+        for (int i = 1; i < N; i++) f = add_v<T>(f, x[i]);
+        return f;
+    };
+
+    for (uint64_t p = 0; p < phases; p++) {
+        const uint64_t t0 = p * K * WV + wave;
+        const uint64_t t_read = wall_clock64();
+        u32x4 s[KR > 0 ? KR : 1];
+#pragma unroll
+        for (int k = 0; k < KR; k++) {
+            int c;
+            const uint64_t o = slot(t0 + k * WV, c);
+            s[k] = fold(c, o);
+            __asm__ __volatile__("" : "+v"(s[k]));  // keep the sum in a register until the write phase
+        }
+#pragma unroll
+        for (int k = 0; k < KL; k++) {
+            int c;
+            const uint64_t o = slot(t0 + (KR + k) * WV, c);
+            held[k * kBlock + threadIdx.x] = fold(c, o);
+        }
+        const uint64_t took = wall_clock64() - t_read;
+        phase_meet(G, took > kPhaseWaitFloor ? took : kPhaseWaitFloor, waiting);
+#pragma unroll
+        for (int k = 0; k < KR; k++) {
+            int c;
+            const uint64_t o = slot(t0 + k * WV, c);
+#pragma unroll
+            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + o, s[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < KL; k++) {
+            int c;
+            const uint64_t o = slot(t0 + (KR + k) * WV, c);
+            const u32x4 f = held[k * kBlock + threadIdx.x];
+#pragma unroll
+            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + o, f);
+        }
+    }
+
+    const char* in[N];
+    char* out[N];
+    for (uint64_t t = phases * K * WV + wave; t < a.tile0[N]; t += WV) {
+        const int c = __builtin_amdgcn_readfirstlane(range_of<N>(t, a.tile0));
+        rotate_ranks<N>(a, c, in, out);
+        const uint64_t v = (t - a.tile0[c]) * W + lane;
+        if (v < a.ch[c].g.nvb) chain_block<N, false, VecIO<T, NT>>(in, out, (a.ch[c].off + a.ch[c].g.head) * E + v * 16);
+    }
+    for (uint64_t cw = wave; cw < (uint64_t)N; cw += WV) {
+        const int c = __builtin_amdgcn_readfirstlane((int)cw);
+        const ChainChunk& k = a.ch[c];
+        const uint64_t ns = k.g.head + k.g.tail;
+        if (lane >= ns) continue;
+        rotate_ranks<N>(a, c, in, out);
+        for (uint64_t j = lane; j < ns; j += W) {
+            const uint64_t col = (j < k.g.head) ? j : k.g.head + k.g.nvb * T::VEC + (j - k.g.head);
+            chain_block<N, false, ScalarIO<T>>(in, out, (k.off + col) * E);
+        }
+    }
+}
+
 // Ring-order all-reduce for outputs on different 128-byte offsets (one-wave
 // workgroups, no output in place): the realigned stores of the fused
 // kernel, chunk by chunk.  A group of U tiles lies inside one chunk, whose

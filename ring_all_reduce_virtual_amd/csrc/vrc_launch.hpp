@@ -738,15 +738,21 @@ struct Launch {
             a.ch[c] = {off, 1, len, 0, split_rows(write_ref(out, n), len, E)};
             a.tile0[c + 1] = a.tile0[c] + (a.ch[c].g.nvb + 63) / 64;
         }
+        bool share = true;  // every output on one 128-byte grid (the chunks start at the same element of every buffer)
+        for (int r = 0; r < n; r++) share = share && (uintptr_t)y[r] % kGridAlign == (uintptr_t)y[0] % kGridAlign;
+        if (!MEM && share) {
+            // Large calls read and write in phases, like the fused kernel.
+            const uint64_t per_phase =
+                (uint64_t)cus * (kBlock / 64) * (uint64_t)(ring_order_phased_regs<T>(n) + kRingOrderPhasedLds);
+            const uint64_t phases = tuning().phased && n >= 6 ? a.tile0[n] / per_phase : 0;
+            if (phases >= 3) return ring_order_phased(a, n, count, phases, cus, st);
+        }
         if (!MEM && tuning().realign && chain_ar_shape(MEM, n).block == 64) {
             // Outputs on different 128-byte offsets, none in place: every
             // output stored on its own grid (the chunks start at the same
             // element of every buffer, so one test covers all chunks).
-            bool share = true, in_place = false;
-            for (int r = 0; r < n; r++) {
-                share = share && (uintptr_t)y[r] % kGridAlign == (uintptr_t)y[0] % kGridAlign;
-                in_place = in_place || x[r] == y[r];
-            }
+            bool in_place = false;
+            for (int r = 0; r < n; r++) in_place = in_place || x[r] == y[r];
             if (!share && !in_place && 2 * (uint64_t)n * count * E >= 64 * kMiB)
                 return ring_order_realigned(a, n, count, cus, st);
         }
@@ -766,6 +772,33 @@ struct Launch {
             hipLaunchKernelGGL((vrc::k_ring_chain_allreduce<T, K, MEM, true>), grid, dim3(kBlock), 0, st, a); \
         break;
             VRC_FOR_N(VRC_CASE)
+#undef VRC_CASE
+        default: return VRC_ERR_INVALID_ARG;
+        }
+        return check_launch();
+    }
+
+    // The phased ring-order all-reduce: one 256-lane workgroup per CU,
+    // `phases` whole phases of tiles, then the rest of the tiles and the
+    // scalar heads and tails; ring_order_phased_regs<T>(n) sums per lane in
+    // registers and kRingOrderPhasedLds in LDS.
+    static vrc_status_t ring_order_phased(const vrc::ChainArgs& a, int n, uint64_t count, uint64_t phases, int cus,
+                                          hipStream_t st)
+    {
+        const dim3 grid((unsigned)cus);
+        if (g_plan)
+            return plan_single(VRC_OP_RING_ORDER_ALLREDUCE_PHASED, count, grid, kBlock,
+                               ring_order_phased_regs<T>(n) + kRingOrderPhasedLds);
+        const uint32_t wait = (uint32_t)tuning().phase_wait;
+        switch (n) {
+#define VRC_CASE(K)                                                                                              \
+    case K:                                                                                                      \
+        hipLaunchKernelGGL((vrc::k_ring_order_allreduce_phased<T, K, ring_order_phased_regs<T>(K),                \
+                                                               kRingOrderPhasedLds, true>),                      \
+                           grid, dim3(kBlock), 0, st, a, phases, wait);                                          \
+        break;
+            VRC_CASE(6) VRC_CASE(7) VRC_CASE(8) VRC_CASE(9) VRC_CASE(10) VRC_CASE(11) VRC_CASE(12) VRC_CASE(13)
+            VRC_CASE(14) VRC_CASE(15) VRC_CASE(16)
 #undef VRC_CASE
         default: return VRC_ERR_INVALID_ARG;
         }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     header = open(os.path.join(ROOT, "include", "vrc.h")).read()
     declared = int(re.search(r"#define VRC_VERSION (\d+)", header).group(1))
-    assert vrc.version() == declared == vrc.ABI_VERSION == 105
+    assert vrc.version() == declared == vrc.ABI_VERSION == 106
     for st in range(5):
         assert vrc.lib().vrc_status_string(st).decode().startswith("VRC_")
     assert b"unknown" in vrc.lib().vrc_status_string(99)

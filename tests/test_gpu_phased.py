@@ -1,10 +1,10 @@
 """The phased fused all-reduce on the GPU, against the oracle.
 
-Large fused (and halving-doubling single-launch) all-reduces from 6 ranks
-read and write in phases: one 256-lane workgroup per CU folds K vectors per
+Large fused, single-launch halving-doubling and ring-order all-reduces from
+6 ranks read and write in phases: one 256-lane workgroup per CU folds K vectors per
 lane of every input, the grid meets, then every lane writes its sums.  These
 cases are large enough for at least three phases (vrc_plan confirms the
-phased launch), and cover every element type, 6 to 16 ranks, both folds, in
+phased launch), and cover every element type, 6 to 16 ranks, all three folds, in
 place, a partial last phase, a partial vector and a scalar head; every
 element of every output is compared with the oracle's per-element form.
 The meetings only shape the timing: runs with them switched off, two calls
@@ -48,15 +48,21 @@ def orc():
 
 
 def sums_per_lane(n, dtype, mode):
+    if mode == "ring_order":  # registers by element type, plus 40 in LDS
+        regs = {"bf16": 32 if n <= 7 else 24 if n <= 9 else 16 if n <= 14 else 0,
+                "fp16": 40 if n <= 8 else 32 if n <= 11 else 24 if n <= 15 else 16}.get(dtype, 40)
+        return regs + 40
     narrow = mode == "hd_order" and ESZ[dtype] == 2
     return ((32 if n <= 8 else 16) if narrow else (64 if n <= 8 else 32)) + 32
 
 
 def phased_count(n, dtype, mode, extra):
     """Elements per rank for three whole phases after a scalar head of up to
-    one 128-byte line, plus `extra` elements."""
+    one 128-byte line (per chunk for the ring order, whose phases count each
+    chunk's tiles), plus `extra` elements."""
     per_vector = 16 // ESZ[dtype]
-    return 3 * CUS * 256 * sums_per_lane(n, dtype, mode) * per_vector + 128 // ESZ[dtype] + extra
+    heads = n if mode == "ring_order" else 1
+    return 3 * CUS * 256 * sums_per_lane(n, dtype, mode) * per_vector + heads * 128 // ESZ[dtype] + extra
 
 
 def shifted(ts, shift):
@@ -78,6 +84,11 @@ CASES = [  # (n, dtype, mode, extra elements, head shift in elements, in place)
     (16, "int32", "fused", 5, 0, True),
     (8, "bf16", "hd_order", 1000, 7, False),
     (16, "fp32", "hd_order", 3, 2, False),
+    (6, "fp32", "ring_order", 4099, 3, False),
+    (8, "bf16", "ring_order", 77, 5, True),
+    (12, "fp16", "ring_order", 12345, 1, False),
+    (16, "bf16", "ring_order", 31, 0, False),
+    (9, "int32", "ring_order", 7, 2, False),
 ]
 
 
@@ -91,12 +102,12 @@ def test_phased_allreduce_every_element(vrc, orc, n, dtype, mode, extra, shift, 
     vy = vx if in_place else shifted([torch.zeros_like(x) for x in xs], shift)
     ops, _ = vrc.plan(vrc.COLL_ALLREDUCE, [v.data_ptr() for v in vx], [v.data_ptr() for v in vy], count, 1,
                       CODES[dtype], vrc.MODES[mode])
-    kind = ("butterfly" if mode == "hd_order" else "fused") + "_allreduce_phased"
+    kind = {"hd_order": "butterfly", "ring_order": "ring_order"}.get(mode, "fused") + "_allreduce_phased"
     assert [(o["kind"], o["grid_x"], o["block"], o["vectors"]) for o in ops] == [
         (kind, CUS, 256, sums_per_lane(n, dtype, mode))]
     vrc.vrc_allreduce(vx, recv=vy, mode=mode)
     torch.cuda.synchronize()
-    at = orc.hd_allreduce_at if mode == "hd_order" else orc.fused_allreduce_at
+    at = {"hd_order": orc.hd_allreduce_at, "ring_order": orc.ring_allreduce_at}.get(mode, orc.fused_allreduce_at)
     want = torch.from_numpy(oracle_every_element(at, hx, dtype, count)).to(DEV)
     equal_to_expected(vy, want, f"phased {mode} n={n} {dtype}")
     del xs, vx, vy, want

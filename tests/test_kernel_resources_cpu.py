@@ -11,7 +11,7 @@ sources), and checks what the kernels are meant to be:
   every kernel is compiled for 64-lane waves;
 * LDS is used only by the realigned all-reduce kernels, at most 8,320 bytes
   per workgroup (one group of sums), and by the phased ones, 128 KiB (32
-  sums per lane);
+  sums per lane; the ring-order one 160 KiB, 40 sums);
 * every vector memory access is a global_* or ds_* instruction: no flat_
   access (it would count against the LDS counter and force coarser waits),
   and no store or atomic of any other kind than global stores and the
@@ -99,8 +99,8 @@ def test_no_scratch_no_memory_spills(code_objects):
             assert k["wave"] == 64, k["name"]
             if k["vgpr_spill"] or k["agpr"]:
                 assert k["vgpr_spill"] <= k["agpr"], k["name"]
-                assert "k_fused_allreduce" in k["name"] and (k["name"].endswith("ELi256EEEvNS_11FusedArArgsE")
-                                                             or "phased" in k["name"]), k["name"]
+                assert ("k_fused_allreduce" in k["name"] and k["name"].endswith("ELi256EEEvNS_11FusedArArgsE")
+                        or "phased" in k["name"]), k["name"]
     assert total > 1000
 
 
@@ -109,6 +109,8 @@ def test_lds_only_in_the_realigned_and_phased_kernels(code_objects):
         for k in kernels(obj):
             if "realigned" in k["name"]:
                 assert 0 < k["lds"] <= 8320, k
+            elif "ring_order_allreduce_phased" in k["name"]:
+                assert k["lds"] == 40 * 256 * 16, k  # 40 sums per lane of a 256-lane workgroup
             elif "phased" in k["name"]:
                 assert k["lds"] == 32 * 256 * 16, k  # 32 sums per lane of a 256-lane workgroup
             else:
@@ -124,7 +126,7 @@ def test_phased_kernels_fit_one_wave_per_simd(code_objects):
             if "phased" in k["name"]:
                 found += 1
                 assert k["vgpr"] <= 512 and k["private"] == 0, k
-    assert found == 4 * (11 + 2)  # four element types: rank fold at 6-16 ranks, butterfly at 8 and 16
+    assert found == 4 * (11 + 2 + 11)  # per element type: rank fold at 6-16 ranks, butterfly at 8 and 16, ring order at 6-16
 
 
 def test_memory_instructions_are_global_or_lds(code_objects):

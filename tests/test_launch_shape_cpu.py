@@ -253,12 +253,48 @@ def test_fused_allreduce_launch_bound_shape_below_64_mib():
 
 @pytest.mark.parametrize("n,per_cu_order", [(2, 8), (3, 4), (8, 4), (16, 4)])
 def test_single_launch_ring_one_wave(n, per_cu_order):
-    """Ring order: one-wave workgroups, 4 per CU (8 at 2 ranks); the
+    """2 GiB moved (under three phases of the phased ring-order kernel): ring
+    order on one-wave workgroups, 4 per CU (8 at 2 ranks); the
     memory-faithful chain: 16 per CU."""
-    count = (4 << 30) // n // 2 // 64 * 64
+    count = (1 << 30) // n // 2 // 64 * 64
     assert plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_RING_ORDER) == [
         ("ring_order_allreduce", CUS * per_cu_order, 1, 64, 1)]
     assert plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_RING_CHAINED) == [("chain_allreduce", CUS * 16, 1, 64, 1)]
+
+
+RING_ORDER_REGS = {  # sums per lane in registers of the phased ring-order kernel, by element type
+    vrc.VRC_BF16: lambda n: 32 if n <= 7 else 24 if n <= 9 else 16 if n <= 14 else 0,
+    vrc.VRC_FP16: lambda n: 40 if n <= 8 else 32 if n <= 11 else 24 if n <= 15 else 16,
+    vrc.VRC_FP32: lambda n: 40,
+    vrc.VRC_INT32: lambda n: 40,
+}
+
+
+@pytest.mark.parametrize("dtype", [vrc.VRC_BF16, vrc.VRC_FP16, vrc.VRC_FP32, vrc.VRC_INT32])
+@pytest.mark.parametrize("n", list(range(2, 17)))
+def test_ring_order_phased_from_six_ranks(n, dtype):
+    """8 GiB moved, one output grid: the phased ring-order kernel from 6
+    ranks (one 256-lane workgroup per CU, the table's register sums plus 40 in
+    LDS per lane), the one-wave kernel below."""
+    count = (4 << 30) // n // ESZ[dtype] // 64 * 64
+    got = plan_ar(n, count, dtype, vrc.VRC_RING_ORDER)
+    if n >= 6:
+        assert got == [("ring_order_allreduce_phased", CUS, 1, 256, RING_ORDER_REGS[dtype](n) + 40)]
+    else:
+        assert got[0][0] == "ring_order_allreduce"
+
+
+@pytest.mark.parametrize("n", [6, 8, 16])
+def test_ring_order_phased_needs_three_whole_phases(n):
+    """Phases count tiles (a chunk's last tile may be partial): exactly three
+    phases' tiles take the phased kernel, one tile fewer does not."""
+    k = RING_ORDER_REGS[vrc.VRC_BF16](n) + 40
+    tiles = 3 * CUS * 4 * k
+    per_chunk = -(-tiles // n)  # whole tiles of 512 bf16 elements in every chunk
+    count = per_chunk * n * 512
+    assert plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_RING_ORDER)[0][0] == "ring_order_allreduce_phased"
+    fewer = (3 * CUS * 4 * k - 1) // n * n * 512  # whole tiles below three phases
+    assert plan_ar(n, fewer, vrc.VRC_BF16, vrc.VRC_RING_ORDER)[0][0] == "ring_order_allreduce"
 
 
 def test_single_launch_ring_small_grid_covers_every_chunk():
