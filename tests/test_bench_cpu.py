@@ -56,12 +56,13 @@ def test_suite_bytes_per_collective():
 def test_recorded_traffic():
     """roofline.traffic comes from the committed counter summary, only while
     it was taken on the kernel sources in the tree; its bytes are within
-    0.1 % of the headline's algorithmic 2*N*S."""
+    0.2 % of the headline's algorithmic 2*N*S (the phased kernel's meetings
+    add about 0.1 %: device-scope polls and atomics of its meeting count)."""
     assert bench.recorded_traffic(workloads.HEADLINE, "select") is None
     t = bench.recorded_traffic(workloads.HEADLINE, "fused")
     if t is None:
         pytest.skip("the committed counters were taken on other kernel sources; re-take them on the GPU")
-    assert abs(t / 8589934592 - 1) < 1e-3
+    assert abs(t / 8589934592 - 1) < 2e-3
 
 
 def test_recorded_mixed_stream():
