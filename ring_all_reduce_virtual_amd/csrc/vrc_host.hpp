@@ -97,6 +97,7 @@ struct Tuning {
     int realign;              // 1: outputs on different 128-byte offsets take the realigned fused kernel; 0: never
     int phased;               // 1: large fused all-reduces take the phased kernel (phased_phases); 0: never
     int phase_wait;           // 1: the phased kernel's workgroups meet between phases; 0: they never wait
+    int phase_skew;           // 1: odd workgroups of the phased kernel hold fewer sums (phased_skew); 0: all hold K
 };
 
 inline const Tuning& tuning()
@@ -107,7 +108,8 @@ inline const Tuning& tuning()
                              env_int("VRC_STEP_NT", -1, 0, 2), env_int("VRC_STEP_UNROLL", 0, 1, 2),
                              env_int("VRC_FUSED_BLOCK", 0, 64, 256), env_int("VRC_CHAIN_BLOCK", 0, 64, 256),
                              env_int("VRC_STEP_BLOCK", 0, 64, 256), env_int("VRC_REALIGN", 1, 0, 1),
-                             env_int("VRC_PHASED", 1, 0, 1), env_int("VRC_PHASE_WAIT", 1, 0, 1)};
+                             env_int("VRC_PHASED", 1, 0, 1), env_int("VRC_PHASE_WAIT", 1, 0, 1),
+                             env_int("VRC_PHASE_SKEW", 1, 0, 1)};
     return t;
 }
 
@@ -235,21 +237,48 @@ constexpr int ring_order_phased_regs(int n)
 }
 constexpr int kRingOrderPhasedLds = 40;
 
+// LDS sums fewer per lane for the odd workgroups of the phased ring-order
+// kernel, as phased_skew for the fused one.
+inline int ring_order_phased_skew(int cus) { return tuning().phase_skew && cus % 8 == 0 ? 8 : 0; }
+
+// LDS sums fewer per lane for the odd workgroups of the phased kernel (0:
+// every workgroup holds K).  On MI355X the workgroups of odd index (odd XCDs)
+// issued a phase's stores in 125-151 us where the even ones took 97-109 us
+// (8 x 512 MiB bf16, per-workgroup wall-clock timelines), and every phase
+// waited for the slowest.  Measured against no skew in one process on the
+// same buffers, bf16, over six runs: at 8 ranks (96 sums per lane) 16 fewer
+// gave +2.0-2.5 % (8 fewer +0.8 %, 24 fewer was slower); at 6, 12 and 16 ranks
+// 8 fewer gave +1.4-2 %; the even workgroups lighter instead was 3-4 % slower.
+// It needs a grid of whole XCD rounds (a multiple of 8 workgroups).
+inline int phased_skew(int n, int cus, bool narrow_butterfly = false)
+{
+    if (!tuning().phase_skew || cus % 8 != 0) return 0;
+    return n == 8 && !narrow_butterfly ? 16 : 8;
+}
+
+// Vectors per rank that one phase of the phased kernel covers.
+inline uint64_t phased_vectors(int n, int cus, bool narrow_butterfly = false)
+{
+    const uint64_t lanes = (uint64_t)cus * kBlock;
+    const uint64_t k = (uint64_t)(phased_regs(n, narrow_butterfly) + kPhasedLds);
+    const uint64_t skew = (uint64_t)phased_skew(n, cus, narrow_butterfly);
+    return (k - skew) * lanes + skew * (lanes / 2);
+}
+
 // Whole phases of the phased kernel for `nvb` vectors per rank, or 0 where
 // the one-wave kernel stays.  A phase reads N x 256 lanes per CU x K
-// vectors: 576 MiB at 6 ranks, 768 MiB at 8, 1 GiB at 16 on 256 CUs (the
-// 16-bit butterfly: 512 MiB at 8, 768 MiB at 16).  It
+// vectors (less the skew above): 576 MiB at 6 ranks, 768 MiB at 8, 1 GiB at
+// 16 on 256 CUs (the 16-bit butterfly: 512 MiB at 8, 768 MiB at 16).  It
 // runs from 6 ranks and at least 3 whole phases.  Measured on MI355X against
 // the one-wave kernel, bf16, bit-identical outputs (time ratio, one process,
-// four interleaved rounds): 8 x 512 MiB 0.946-0.963, 8 x 1 GiB 0.935,
-// 12 x 341 MiB 0.860, 6 x 682 MiB 0.954, 16 x 256 MiB 0.973; and where it is
-// not taken, 8 x 256 MiB 0.969 (2 phases), 8 x 128 MiB 1.003 (1),
-// 16 x 128 MiB 1.008 (2), 4 x 512 MiB 1.030 (384 MiB phases).
+// four interleaved rounds, before the skew): 8 x 512 MiB 0.946-0.963,
+// 8 x 1 GiB 0.935, 12 x 341 MiB 0.860, 6 x 682 MiB 0.954, 16 x 256 MiB 0.973;
+// and where it is not taken, 8 x 256 MiB 0.969 (2 phases), 8 x 128 MiB 1.003
+// (1), 16 x 128 MiB 1.008 (2), 4 x 512 MiB 1.030 (384 MiB phases).
 inline uint64_t phased_phases(int n, uint64_t nvb, int cus, bool narrow_butterfly = false)
 {
     if (!tuning().phased || n < 6) return 0;
-    const uint64_t per_phase = (uint64_t)cus * kBlock * (uint64_t)(phased_regs(n, narrow_butterfly) + kPhasedLds);
-    const uint64_t p = nvb / per_phase;
+    const uint64_t p = nvb / phased_vectors(n, cus, narrow_butterfly);
     return p >= 3 ? p : 0;
 }
 

@@ -363,60 +363,87 @@ __device__ __forceinline__ void phase_meet(uint64_t G, uint64_t limit, bool& wai
     __syncthreads();
 }
 
-// Vector v of a phase belongs to lane ((w * G + b) * 64 + l) for wave w of
-// workgroup b, lane l, so consecutive 1 KiB tiles go to consecutive
-// workgroups (consecutive XCDs), as in the one-wave kernel above.  The
-// vectors after the last whole phase and the scalar head and tail follow
-// with the grid-stride loops.  `wait` = 0 skips every meeting.
+// Slot k of lane ((w * G + b) * 64 + l), for wave w of workgroup b and lane
+// l, is vector k * L + that lane of its phase (L lanes in the grid), so
+// consecutive 1 KiB tiles go to consecutive workgroups (consecutive XCDs),
+// as in the one-wave kernel above.  With `skew` > 0 (G a multiple of 8) the
+// workgroups of odd index hold `skew` fewer LDS sums than the others: every
+// workgroup holds the first K - skew slots in that layout, and the even
+// workgroups' last `skew` slots follow them, L / 2 lanes wide (lane
+// ((w * G/2 + b/2) * 64 + l)).  On MI355X the workgroups on odd XCDs issue
+// their stores more slowly than those on even ones, and the lighter share
+// evens out the time each spends on a phase.  The vectors after the last
+// whole phase and the scalar head and tail follow with the grid-stride
+// loops.  `wait` = 0 skips every meeting.
 template <class T, int N, int KR, int KL, bool NT, class Fold = RankFold>
 __global__ __launch_bounds__(kBlock, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_fused_allreduce_phased(FusedArArgs a, uint64_t phases, uint32_t wait)
+void k_fused_allreduce_phased(FusedArArgs a, uint64_t phases, uint32_t wait, uint32_t skew)
 {
     constexpr int K = KR + KL;
     __shared__ u32x4 held[KL * kBlock];
     const uint64_t G = gridDim.x;
     const uint64_t L = G * kBlock;
-    const uint64_t lane = (((uint64_t)(threadIdx.x >> 6)) * G + blockIdx.x) * 64 + (threadIdx.x & 63);
+    const uint64_t w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const uint64_t lane = (w * G + blockIdx.x) * 64 + l;
+    const uint64_t lane_even = (w * (G / 2) + (blockIdx.x >> 1)) * 64 + l;
+    const uint64_t shared_slots = (uint64_t)K - skew;
+    const int held_here = (blockIdx.x & 1) ? KL - (int)skew : KL;
+    const uint64_t per_phase = shared_slots * L + (uint64_t)skew * (L / 2);
     constexpr uint64_t E = T::ESZ;
     const uint64_t body = a.g.head * E;
     bool waiting = wait != 0;
 
     for (uint64_t p = 0; p < phases; p++) {
-        const uint64_t base = p * L * K + lane;
+        const uint64_t start = p * per_phase;
+        // vector of LDS slot k (register slots k < KR <= K - skew are at start + k * L + lane)
+        auto held_at = [&](int k) -> uint64_t {
+            const uint64_t slot = (uint64_t)(KR + k);
+            return slot < shared_slots ? start + slot * L + lane
+                                       : start + shared_slots * L + (slot - shared_slots) * (L / 2) + lane_even;
+        };
         const uint64_t t_read = wall_clock64();
         u32x4 s[KR];
 #pragma unroll
         for (int k = 0; k < KR; k++) {
             u32x4 in[N];
+            const uint64_t v = start + k * L + lane;
 #pragma unroll
-            for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + (base + k * L) * 16);
+            for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
             issue_loads_first();
             s[k] = Fold::template vec<T, N>(in);
             __asm__ __volatile__("" : "+v"(s[k]));  // keep the sum in a register until the write phase
         }
 #pragma unroll
         for (int k = 0; k < KL; k++) {
-            u32x4 in[N];
+            if (k < held_here) {
+                u32x4 in[N];
+                const uint64_t v = held_at(k);
 #pragma unroll
-            for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + (base + (KR + k) * L) * 16);
-            issue_loads_first();
-            held[k * kBlock + threadIdx.x] = Fold::template vec<T, N>(in);
+                for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
+                issue_loads_first();
+                held[k * kBlock + threadIdx.x] = Fold::template vec<T, N>(in);
+            }
         }
         const uint64_t took = wall_clock64() - t_read;
         phase_meet(G, took > kPhaseWaitFloor ? took : kPhaseWaitFloor, waiting);
 #pragma unroll
-        for (int k = 0; k < KR; k++)
+        for (int k = 0; k < KR; k++) {
+            const uint64_t v = start + k * L + lane;
 #pragma unroll
-            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + (base + k * L) * 16, s[k]);
+            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, s[k]);
+        }
 #pragma unroll
         for (int k = 0; k < KL; k++) {
-            const u32x4 f = held[k * kBlock + threadIdx.x];
+            if (k < held_here) {
+                const u32x4 f = held[k * kBlock + threadIdx.x];
+                const uint64_t v = held_at(k);
 #pragma unroll
-            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + (base + (KR + k) * L) * 16, f);
+                for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + body + v * 16, f);
+            }
         }
     }
 
-    for (uint64_t v = phases * L * K + lane; v < a.g.nvb; v += L) {
+    for (uint64_t v = phases * per_phase + lane; v < a.g.nvb; v += L) {
         u32x4 in[N];
 #pragma unroll
         for (int r = 0; r < N; r++) in[r] = ld16<NT>(a.src[r] + body + v * 16);
@@ -838,17 +865,19 @@ __global__ __launch_bounds__(B) void k_ring_chain_allreduce(ChainArgs a)
 }
 
 // Phased ring-order all-reduce: the phased fused kernel's schedule (one
-// 256-lane workgroup per CU; read K slots, meet, write them) over the tiles
-// of the kernel above.  Slot k of phase p is tile (p K + k) W + w for wave w
-// of the W in the grid, so the chunk, and with it the rank rotation that
-// fixes the ring's fold order, is uniform over a wave's slot.  Lanes past a
+// 256-lane workgroup per CU; read K slots, meet, write them, the odd
+// workgroups `skew` slots fewer) over the tiles of the kernel above.  Slot k
+// of a phase is tile k W + w of it for wave w of the W in the grid (the even
+// workgroups' last `skew` slots: W / 2 tiles per slot, after the others), so
+// the chunk, and with it the rank rotation that fixes the ring's fold order,
+// is uniform over a wave's slot.  Lanes past a
 // chunk's last vector (its last tile may be partial) load and fold that last
 // vector and store its sum there again: the bits the owning lane of the same
 // wave stores, which keeps every slot free of branches.  The tiles after the
 // last whole phase take the loop above; so do the scalar heads and tails.
 template <class T, int N, int KR, int KL, bool NT>
 __global__ __launch_bounds__(kBlock, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_ring_order_allreduce_phased(ChainArgs a, uint64_t phases, uint32_t wait)
+void k_ring_order_allreduce_phased(ChainArgs a, uint64_t phases, uint32_t wait, uint32_t skew)
 {
     constexpr int K = KR + KL;
     constexpr uint64_t W = 64;
@@ -858,6 +887,10 @@ void k_ring_order_allreduce_phased(ChainArgs a, uint64_t phases, uint32_t wait)
     const uint64_t WV = G * (kBlock / W);
     const uint64_t lane = threadIdx.x % W;
     const uint64_t wave = ((uint64_t)(threadIdx.x / W)) * G + blockIdx.x;
+    const uint64_t wave_even = ((uint64_t)(threadIdx.x / W)) * (G / 2) + (blockIdx.x >> 1);
+    const uint64_t shared_slots = (uint64_t)K - skew;
+    const int held_here = (blockIdx.x & 1) ? KL - (int)skew : KL;
+    const uint64_t per_phase = shared_slots * WV + (uint64_t)skew * (WV / 2);
     bool waiting = wait != 0;
 
     // Byte offset of a slot's vector in every rank buffer, and its chunk.
@@ -880,44 +913,53 @@ void k_ring_order_allreduce_phased(ChainArgs a, uint64_t phases, uint32_t wait)
     };
 
     for (uint64_t p = 0; p < phases; p++) {
-        const uint64_t t0 = p * K * WV + wave;
+        const uint64_t t0 = p * per_phase;
+        // tile of LDS slot k (register slots k < KR <= K - skew are tile t0 + k * WV + wave)
+        auto held_tile = [&](int k) -> uint64_t {
+            const uint64_t j = (uint64_t)(KR + k);
+            return j < shared_slots ? t0 + j * WV + wave : t0 + shared_slots * WV + (j - shared_slots) * (WV / 2) + wave_even;
+        };
         const uint64_t t_read = wall_clock64();
         u32x4 s[KR > 0 ? KR : 1];
 #pragma unroll
         for (int k = 0; k < KR; k++) {
             int c;
-            const uint64_t o = slot(t0 + k * WV, c);
+            const uint64_t o = slot(t0 + k * WV + wave, c);
             s[k] = fold(c, o);
             __asm__ __volatile__("" : "+v"(s[k]));  // keep the sum in a register until the write phase
         }
 #pragma unroll
         for (int k = 0; k < KL; k++) {
-            int c;
-            const uint64_t o = slot(t0 + (KR + k) * WV, c);
-            held[k * kBlock + threadIdx.x] = fold(c, o);
+            if (k < held_here) {
+                int c;
+                const uint64_t o = slot(held_tile(k), c);
+                held[k * kBlock + threadIdx.x] = fold(c, o);
+            }
         }
         const uint64_t took = wall_clock64() - t_read;
         phase_meet(G, took > kPhaseWaitFloor ? took : kPhaseWaitFloor, waiting);
 #pragma unroll
         for (int k = 0; k < KR; k++) {
             int c;
-            const uint64_t o = slot(t0 + k * WV, c);
+            const uint64_t o = slot(t0 + k * WV + wave, c);
 #pragma unroll
             for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + o, s[k]);
         }
 #pragma unroll
         for (int k = 0; k < KL; k++) {
-            int c;
-            const uint64_t o = slot(t0 + (KR + k) * WV, c);
-            const u32x4 f = held[k * kBlock + threadIdx.x];
+            if (k < held_here) {
+                int c;
+                const uint64_t o = slot(held_tile(k), c);
+                const u32x4 f = held[k * kBlock + threadIdx.x];
 #pragma unroll
-            for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + o, f);
+                for (int r = 0; r < N; r++) st16<NT>(a.dst[r] + o, f);
+            }
         }
     }
 
     const char* in[N];
     char* out[N];
-    for (uint64_t t = phases * K * WV + wave; t < a.tile0[N]; t += WV) {
+    for (uint64_t t = phases * per_phase + wave; t < a.tile0[N]; t += WV) {
         const int c = __builtin_amdgcn_readfirstlane(range_of<N>(t, a.tile0));
         rotate_ranks<N>(a, c, in, out);
         const uint64_t v = (t - a.tile0[c]) * W + lane;

@@ -314,9 +314,10 @@ struct Launch {
             return plan_single(butterfly ? VRC_OP_BUTTERFLY_ALLREDUCE_PHASED : VRC_OP_FUSED_ALLREDUCE_PHASED, count,
                                grid, kBlock, phased_regs(n, nb) + kPhasedLds);
         const uint32_t wait = (uint32_t)tuning().phase_wait;
+        const uint32_t skew = (uint32_t)phased_skew(n, cus, nb);
 #define VRC_PHASED(K)                                                                                                 \
     hipLaunchKernelGGL((vrc::k_fused_allreduce_phased<T, K, phased_regs(K, nb), kPhasedLds, true, Fold>), grid,    \
-                       dim3(kBlock), 0, st, a, phases, wait)
+                       dim3(kBlock), 0, st, a, phases, wait, skew)
         if constexpr (butterfly) {
             switch (n) {
             case 8: VRC_PHASED(8); break;
@@ -742,8 +743,9 @@ struct Launch {
         for (int r = 0; r < n; r++) share = share && (uintptr_t)y[r] % kGridAlign == (uintptr_t)y[0] % kGridAlign;
         if (!MEM && share) {
             // Large calls read and write in phases, like the fused kernel.
+            const uint64_t waves = (uint64_t)cus * (kBlock / 64), skew = (uint64_t)ring_order_phased_skew(cus);
             const uint64_t per_phase =
-                (uint64_t)cus * (kBlock / 64) * (uint64_t)(ring_order_phased_regs<T>(n) + kRingOrderPhasedLds);
+                waves * ((uint64_t)(ring_order_phased_regs<T>(n) + kRingOrderPhasedLds) - skew) + waves / 2 * skew;
             const uint64_t phases = tuning().phased && n >= 6 ? a.tile0[n] / per_phase : 0;
             if (phases >= 3) return ring_order_phased(a, n, count, phases, cus, st);
         }
@@ -789,13 +791,13 @@ struct Launch {
         if (g_plan)
             return plan_single(VRC_OP_RING_ORDER_ALLREDUCE_PHASED, count, grid, kBlock,
                                ring_order_phased_regs<T>(n) + kRingOrderPhasedLds);
-        const uint32_t wait = (uint32_t)tuning().phase_wait;
+        const uint32_t wait = (uint32_t)tuning().phase_wait, skew = (uint32_t)ring_order_phased_skew(cus);
         switch (n) {
 #define VRC_CASE(K)                                                                                              \
     case K:                                                                                                      \
         hipLaunchKernelGGL((vrc::k_ring_order_allreduce_phased<T, K, ring_order_phased_regs<T>(K),                \
                                                                kRingOrderPhasedLds, true>),                      \
-                           grid, dim3(kBlock), 0, st, a, phases, wait);                                          \
+                           grid, dim3(kBlock), 0, st, a, phases, wait, skew);                                    \
         break;
             VRC_CASE(6) VRC_CASE(7) VRC_CASE(8) VRC_CASE(9) VRC_CASE(10) VRC_CASE(11) VRC_CASE(12) VRC_CASE(13)
             VRC_CASE(14) VRC_CASE(15) VRC_CASE(16)

@@ -7,8 +7,9 @@ cases are large enough for at least three phases (vrc_plan confirms the
 phased launch), and cover every element type, 6 to 16 ranks, all three folds, in
 place, a partial last phase, a partial vector and a scalar head; every
 element of every output is compared with the oracle's per-element form.
-The meetings only shape the timing: runs with them switched off, two calls
-at once on two streams, and replays of a captured graph give the same bits."""
+The meetings only shape the timing: runs with them switched off, or with
+every workgroup holding the same number of sums, two calls at once on two
+streams, and replays of a captured graph give the same bits."""
 import os
 import subprocess
 import sys
@@ -187,17 +188,21 @@ assert ops[0]["kind"] == "fused_allreduce_phased", ops[0]["kind"]
 vrc.vrc_allreduce(xs, recv=ys, mode="fused")
 torch.cuda.synchronize()
 want = torch.from_numpy(oracle_every_element(oracle.get().fused_allreduce_at, host(xs), "bf16", count)).to("cuda:0")
-equal_to_expected(ys, want, "phased without meetings")
+equal_to_expected(ys, want, "phased, one setting off")
 print("ok", flush=True)
 """
 
 
-def test_phased_without_meetings(vrc):
-    """VRC_PHASE_WAIT=0 (read once per process, so a child process runs it):
-    no workgroup ever waits at a meeting, and the outputs are the same bits."""
+@pytest.mark.parametrize("var", ["VRC_PHASE_WAIT", "VRC_PHASE_SKEW"])
+def test_phased_without_meetings_or_skew(vrc, var):
+    """VRC_PHASE_WAIT=0 (no workgroup ever waits at a meeting) and
+    VRC_PHASE_SKEW=0 (every workgroup holds all its sums, so the phases cover
+    other vectors): read once per process, so a child process runs each; the
+    outputs are the same bits."""
     count = phased_count(8, "bf16", "fused", 4097)
-    say(f"phased all-reduce without meetings (child process): count={count}")
-    env = dict(os.environ, VRC_PHASE_WAIT="0", PYTHONPATH=ROOT)
+    say(f"phased all-reduce with {var}=0 (child process): count={count}")
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    env[var] = "0"
     r = subprocess.run([sys.executable, "-c", CHILD, ROOT, str(count)], env=env, capture_output=True, text=True,
                        timeout=240, cwd=ROOT)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]

@@ -216,14 +216,45 @@ def test_phased_from_six_ranks_and_three_phases(n):
                 ("butterfly_allreduce_phased", CUS, 1, 256, phased_k(n, dtype, butterfly=True))]
 
 
+def phased_skew(n, dtype=vrc.VRC_BF16, butterfly=False):
+    """LDS sums fewer per lane in the odd workgroups: 16 at 8 ranks (96 sums
+    per lane), 8 elsewhere."""
+    narrow = butterfly and ESZ[dtype] == 2
+    return 16 if n == 8 and not narrow else 8
+
+
+def phased_vectors(n, skew):
+    """16-byte vectors per rank in one phase: every lane's first K - skew
+    slots, then the even workgroups' last `skew` slots."""
+    return CUS * 256 * (phased_k(n) - skew) + CUS * 128 * skew
+
+
 @pytest.mark.parametrize("n", [6, 8, 16])
 def test_phased_needs_three_whole_phases(n):
     """Exactly three phases' vectors per rank take the phased kernel; one
     vector less keeps the one-wave kernel."""
-    per_phase = CUS * 256 * phased_k(n)  # 16-byte vectors
-    at = 3 * per_phase * 8  # bf16 elements
+    at = 3 * phased_vectors(n, phased_skew(n)) * 8  # bf16 elements
     assert plan_ar(n, at, vrc.VRC_BF16, vrc.VRC_FUSED)[0][0] == "fused_allreduce_phased"
     assert plan_ar(n, at - 8, vrc.VRC_BF16, vrc.VRC_FUSED)[0][0] == "fused_allreduce"
+
+
+def test_phase_skew_off_restores_whole_slots():
+    """VRC_PHASE_SKEW=0 (read once per process, so a child process checks it):
+    every workgroup holds all K sums, so three phases need three times
+    256 x 256 x K vectors per rank."""
+    code = (
+        "import sys, ring_all_reduce_virtual_amd as v\n"
+        "n=int(sys.argv[1]); at=int(sys.argv[2])\n"
+        "s=[(1<<40)+r*(1<<33) for r in range(n)]; d=[(1<<42)+r*(1<<33) for r in range(n)]\n"
+        "a,_=v.plan(v.COLL_ALLREDUCE,s,d,at,1,v.VRC_BF16,v.VRC_FUSED)\n"
+        "b,_=v.plan(v.COLL_ALLREDUCE,s,d,at-8,1,v.VRC_BF16,v.VRC_FUSED)\n"
+        "print(a[0]['kind'],b[0]['kind'])\n")
+    env = dict(os.environ, VRC_PHASE_SKEW="0", PYTHONPATH=ROOT)
+    for n in (6, 8):
+        at = 3 * phased_vectors(n, 0) * 8
+        out = subprocess.run([sys.executable, "-c", code, str(n), str(at)], env=env, check=True,
+                             capture_output=True, text=True, cwd=ROOT).stdout.split()
+        assert out == ["fused_allreduce_phased", "fused_allreduce"], (n, out)
 
 
 def test_phased_in_place_and_with_a_ragged_tail():
@@ -287,13 +318,14 @@ def test_ring_order_phased_from_six_ranks(n, dtype):
 @pytest.mark.parametrize("n", [6, 8, 16])
 def test_ring_order_phased_needs_three_whole_phases(n):
     """Phases count tiles (a chunk's last tile may be partial): exactly three
-    phases' tiles take the phased kernel, one tile fewer does not."""
-    k = RING_ORDER_REGS[vrc.VRC_BF16](n) + 40
-    tiles = 3 * CUS * 4 * k
+    phases' tiles take the phased kernel, one tile fewer does not.  A phase
+    holds K tiles per wave, less 8 in the odd workgroups."""
+    k, skew = RING_ORDER_REGS[vrc.VRC_BF16](n) + 40, 8
+    tiles = 3 * (CUS * 4 * (k - skew) + CUS * 2 * skew)
     per_chunk = -(-tiles // n)  # whole tiles of 512 bf16 elements in every chunk
     count = per_chunk * n * 512
     assert plan_ar(n, count, vrc.VRC_BF16, vrc.VRC_RING_ORDER)[0][0] == "ring_order_allreduce_phased"
-    fewer = (3 * CUS * 4 * k - 1) // n * n * 512  # whole tiles below three phases
+    fewer = (tiles - 1) // n * n * 512  # whole tiles below three phases
     assert plan_ar(n, fewer, vrc.VRC_BF16, vrc.VRC_RING_ORDER)[0][0] == "ring_order_allreduce"
 
 
