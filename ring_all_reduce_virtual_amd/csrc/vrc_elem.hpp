@@ -76,6 +76,16 @@ __device__ __forceinline__ void reload_fence() { __asm__ __volatile__("" ::: "me
 // instead of 5.4).
 __device__ __forceinline__ void issue_loads_first() { __builtin_amdgcn_sched_barrier(0); }
 
+// Wait until at most W vector memory operations of this wave are outstanding
+// (the gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt 7 and
+// lgkmcnt 15 wait on nothing).
+template <int W>
+__device__ __forceinline__ void wait_vmem_below()
+{
+    static_assert(W >= 0 && W < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (W & 15) | ((W >> 4) << 14));
+}
+
 struct I32 {
     using S = uint32_t;  // stored bits
     using A = uint32_t;  // accumulator

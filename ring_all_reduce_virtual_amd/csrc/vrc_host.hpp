@@ -76,7 +76,8 @@ inline int env_int(const char* name, int dflt, int lo, int hi)
 //    workgroups, one per CU (two at 2 ranks) once the whole operation moves
 //    >= 4 GiB, 2 per CU from 1 GiB, 8 per CU below that, where the Infinity
 //    Cache holds much of the data and latency hiding matters more than open
-//    DRAM rows; fused all-gather: 16 per CU (ag_blocks_per_cu);
+//    DRAM rows; fused all-gather: 32 per CU with one store in flight per
+//    wave up to 2 GiB written, 16 per CU above (ag_shape);
 //  - ring and halving-doubling steps: by the bytes a step moves and its number
 //    of per-rank operations (step_shape), workgroups counted over all of them.
 // Loads and stores carry the non-temporal hint (measured faster for this
@@ -98,6 +99,7 @@ struct Tuning {
     int phased;               // 1: large fused all-reduces take the phased kernel (phased_phases); 0: never
     int phase_wait;           // 1: the phased kernel's workgroups meet between phases; 0: they never wait
     int phase_skew;           // 1: odd workgroups of the phased kernel hold fewer sums (phased_skew); 0: all hold K
+    int ag_throttle;          // -1: size policy (ag_shape); 1: the fused all-gather keeps one store in flight per wave; 0: never
 };
 
 inline const Tuning& tuning()
@@ -109,7 +111,7 @@ inline const Tuning& tuning()
                              env_int("VRC_FUSED_BLOCK", 0, 64, 256), env_int("VRC_CHAIN_BLOCK", 0, 64, 256),
                              env_int("VRC_STEP_BLOCK", 0, 64, 256), env_int("VRC_REALIGN", 1, 0, 1),
                              env_int("VRC_PHASED", 1, 0, 1), env_int("VRC_PHASE_WAIT", 1, 0, 1),
-                             env_int("VRC_PHASE_SKEW", 1, 0, 1)};
+                             env_int("VRC_PHASE_SKEW", 1, 0, 1), env_int("VRC_AG_THROTTLE", -1, 0, 1)};
     return t;
 }
 
@@ -382,16 +384,30 @@ inline int chain_rs_flat_blocks_per_cu()
     return 16;
 }
 
-// The fused all-gather reads each input once and stores it N times: 16
-// workgroups per CU at every size.  Measured on MI355X in one process on the
-// same buffers (us, 8 / 16 per CU): 8 x 5 MiB fp16 heads 77.2 / 75.2 and
-// 81.4 / 77.0 (cache flushed); 8 x 64 MiB 953 / 943; 16 x 5 MiB 292 / 289;
-// 4 x 5 MiB 24.6 / 24.8.  One-wave workgroups were slower (79-89 us on the
-// heads).
-inline int ag_blocks_per_cu()
+// The fused all-gather reads each input once and stores it N times.  Up to
+// 2 GiB written, each wave keeps one store in flight (it waits for the
+// previous store before the next) and the grid has 32 workgroups per CU;
+// above that, stores go back to back at 16 per CU.  Measured on MI355X,
+// fp16, each call after a cache-evicting write (us; back to back at 16 per
+// CU / one store in flight at 32 per CU, three processes each): 8 x 5 MiB
+// heads 74.4-75.0 / 71.1-71.7 (in one process on the same buffers
+// 75.8-76.0 / 69.6-71.0), 8 x 1 MiB 17.0-17.2 / 15.3-15.7, 4 x 5 MiB
+// 23.1-23.8 / 21.9-22.2, 16 x 5 MiB (1.25 GiB written) 300-302 / 288-289,
+// 4 x 64 MiB 265-282 / 254-265, 2 x 256 MiB 310-312 / 307-310, 8 x 16 MiB
+// 235-237 / 235-236; and at 4 GiB written and more 8 x 64 MiB 953-957 /
+// 954-958, 16 x 16 MiB 924-928 / 936-940, 8 x 128 MiB 1,890-1,892 /
+// 1,915-1,918.  Back to back, more workgroups were slower (the heads at 32
+// per CU: 77.6-84.5 us).
+struct AgShape {
+    int blocks_per_cu;
+    bool one_store_in_flight;
+};
+
+inline AgShape ag_shape(uint64_t bytes_written)
 {
-    if (tuning().fused_blocks_per_cu) return tuning().fused_blocks_per_cu;
-    return 16;
+    const bool throttle = tuning().ag_throttle >= 0 ? tuning().ag_throttle != 0 : bytes_written <= 2 * kGiB;
+    const int bpc = tuning().fused_blocks_per_cu ? tuning().fused_blocks_per_cu : (throttle ? 32 : 16);
+    return {bpc, throttle};
 }
 
 // Memory-faithful chains wait on their own stores between steps, so they

@@ -661,7 +661,9 @@ struct FusedAgArgs {
     RowSplit g[kMaxRanks];  // per source rank (its slab offset sets the alignment)
 };
 
-template <class T, bool NT>
+// THROTTLE: each store waits for the wave's previous one, so a wave keeps
+// one store in flight and the grid's many waves carry the stream.
+template <class T, bool NT, bool THROTTLE = false>
 __global__ __launch_bounds__(kBlock) void k_fused_all_gather(FusedAgArgs a)
 {
     const int q = blockIdx.y;
@@ -677,7 +679,10 @@ __global__ __launch_bounds__(kBlock) void k_fused_all_gather(FusedAgArgs a)
         const uint64_t col = (v - row * g.nvb) * 16 + g.head * E;
         const u32x4 x = ld16<NT>(a.src[q] + row * a.width * E + col);
         const uint64_t dof = (row * s_dst + slab) * E + col;
-        for (int r = 0; r < a.n; r++) st16<NT>(a.dst[r] + dof, x);
+        for (int r = 0; r < a.n; r++) {
+            st16<NT>(a.dst[r] + dof, x);
+            if constexpr (THROTTLE) wait_vmem_below<0>();
+        }
     }
     const uint64_t ns = a.rows * (g.head + g.tail);
     for (uint64_t k = tid; k < ns; k += nthreads) {

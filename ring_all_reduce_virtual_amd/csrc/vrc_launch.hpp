@@ -544,9 +544,13 @@ struct Launch {
             const uint64_t w = outer * (a.g[q].nvb + a.g[q].head + a.g[q].tail);
             if (w > work) work = w;
         }
-        const dim3 grid(grid_x(cus, work, n, ag_blocks_per_cu()), (unsigned)n);
+        const AgShape sh = ag_shape((uint64_t)n * n * count * E);
+        const dim3 grid(grid_x(cus, work, n, sh.blocks_per_cu), (unsigned)n);
         if (g_plan) return plan_single(VRC_OP_FUSED_ALL_GATHER, count, grid, kBlock, 1);
-        hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
+        if (sh.one_store_in_flight)
+            hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true, true>), grid, dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((vrc::k_fused_all_gather<T, true>), grid, dim3(kBlock), 0, st, a);
         return check_launch();
     }
 

@@ -339,16 +339,23 @@ def test_single_launch_ring_small_grid_covers_every_chunk():
     assert gx == max(tiles, 4)
 
 
-def test_fused_all_gather_sixteen_per_cu():
-    """8 x [1, 5, 4096, 128] fp16 heads: 256-lane workgroups, 16 per CU over
-    the 8 source rows."""
-    n, count, esz = 8, 5 * 4096 * 128, 2
+@pytest.mark.parametrize("n,count,per_cu", [
+    (8, 5 * 4096 * 128, 32),   # the heads: 320 MiB written, one store in flight per wave, 32 per CU
+    (16, 5 << 19, 32),         # 16 x 5 MiB: 1.25 GiB written
+    (8, 16 << 20, 32),         # 8 x 32 MiB: exactly 2 GiB written
+    (8, (16 << 20) + 8, 16),   # just above 2 GiB written: stores back to back, 16 per CU
+    (8, 64 << 20, 16),         # 8 x 128 MiB
+])
+def test_fused_all_gather_grid(n, count, per_cu):
+    """fp16 all-gathers: 256-lane workgroups over the n source rows, 32 per
+    CU up to 2 GiB written and 16 above."""
+    esz = 2
     send, _ = wide(n)
     recv = gather_out(n, count, esz)
     ops, nl = vrc.plan(vrc.COLL_ALL_GATHER, send, recv, count, 1, vrc.VRC_FP16, vrc.VRC_FUSED)
     nv = count * esz // 16
     assert nl == 1
-    assert launches(ops) == [("fused_all_gather", min((nv + 255) // 256, CUS * 16 // n), n, 256, 1)]
+    assert launches(ops) == [("fused_all_gather", min((nv + 255) // 256, CUS * per_cu // n), n, 256, 1)]
 
 
 @pytest.mark.parametrize("n,count,dtype,add_shape,copy_shape", [
