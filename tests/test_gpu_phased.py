@@ -83,8 +83,10 @@ CASES = [  # (n, dtype, mode, extra elements, head shift in elements, in place)
     (7, "bf16", "fused", 777, 5, True),
     (12, "fp16", "fused", 99, 1, False),
     (16, "int32", "fused", 5, 0, True),
+    (8, "fp32", "fused", 513, 2, False),
     (8, "bf16", "hd_order", 1000, 7, False),
     (16, "fp32", "hd_order", 3, 2, False),
+    (16, "fp16", "hd_order", 4097, 4, True),
     (6, "fp32", "ring_order", 4099, 3, False),
     (8, "bf16", "ring_order", 77, 5, True),
     (12, "fp16", "ring_order", 12345, 1, False),
