@@ -871,8 +871,9 @@ def main() -> int:
             "counters": recorded_mixed_stream(),
             "reading": "the kernel reads each phase (0.5-1 GiB) before it writes it, so its reads wait about as "
                        "long as a read-only stream's instead of queueing behind DRAM read/write turnarounds; the rest "
-                       "of the gap to the read-then-write bound is the meetings, the turn at each phase boundary and "
-                       "fewer reads in flight"}
+                       "of the gap to the read-then-write bound is the meetings, the turn at each phase boundary, "
+                       "the odd XCDs' slower stores (their workgroups hold fewer sums per phase) and fewer reads in "
+                       "flight"}
         log(f"mixed stream: {extra['mixed_stream']}")
 
     # NCCL-style figures for context: algbw = S / t per rank buffer, busbw = algbw * 2(N-1)/N.
