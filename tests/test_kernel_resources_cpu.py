@@ -148,3 +148,46 @@ def test_headline_kernel_registers(code_objects):
     assert len(found) == 1
     k = found[0]
     assert k["agpr"] == 0 and k["vgpr"] <= 128 and k["lds"] == 0
+
+
+def functions(obj):
+    """Disassembly per function: name -> list of instruction lines."""
+    text = subprocess.run([TOOLS["llvm-objdump"], "-d", "--no-show-raw-insn", str(obj)], check=True,
+                          capture_output=True, text=True).stdout
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(.+)>:$", line)
+        if m:
+            cur = out.setdefault(m.group(1), [])
+        elif cur is not None and line.strip() and not line.strip().startswith(";"):
+            cur.append(line.strip())
+    return out
+
+
+def next_memory_step(body, i):
+    """The first global access or s_waitcnt after instruction i."""
+    for ins in body[i + 1:]:
+        if ins.startswith(("global_", "s_waitcnt")):
+            return ins
+    return ""
+
+
+def test_throttled_all_gather_waits_after_every_store(code_objects):
+    """The fused all-gather's throttled form waits for each 16-byte store
+    (vmcnt(0)) before the wave's next memory access; the plain form never
+    waits for a store before the next one."""
+    seen = {True: 0, False: 0}
+    for obj in code_objects:
+        for name, body in functions(obj).items():
+            if "k_fused_all_gather" not in name:
+                continue
+            throttled = name.endswith("Lb1ELb1EEEvNS_11FusedAgArgsE")
+            stores = [i for i, ins in enumerate(body) if ins.startswith("global_store_dwordx4")]
+            assert stores, name
+            after = [next_memory_step(body, i) for i in stores]
+            if throttled:
+                assert all(a.startswith("s_waitcnt") and "vmcnt(0)" in a for a in after), (name, after)
+            else:  # at most a wait for the next output pointer (lgkmcnt), never for the store
+                assert not any("vmcnt" in a for a in after), (name, after)
+            seen[throttled] += 1
+    assert seen == {True: 4, False: 4}  # both forms, one per element type
