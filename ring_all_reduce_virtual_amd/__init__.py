@@ -212,22 +212,24 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _check_ranks(tensors, what):
-    # One pass, with rank 0's attributes read once: this check is most of the
-    # host cost of a small call.
+def _check_ranks(tensors, what) -> int:
+    """Validate one tensor per rank; return their device index.  One pass,
+    with rank 0's attributes read once and device indices compared as ints:
+    this check is most of the host cost of a small call."""
     if not isinstance(tensors, (list, tuple)) or not tensors:
         raise ValueError(f"{what}: expected a non-empty list of tensors, one per rank")
     if len(tensors) > MAX_RANKS:
         raise ValueError(f"{what}: at most {MAX_RANKS} ranks")
     t0 = tensors[0]
-    dtype, shape, device = t0.dtype, t0.shape, t0.device
-    if device.type != "cuda":
+    if not t0.is_cuda:
         raise ValueError(f"{what}: tensors must live on the GPU")
+    dtype, shape, dev = t0.dtype, t0.shape, t0.get_device()
     for t in tensors:
-        if t.dtype is not dtype or t.shape != shape or t.device != device:
+        if t.dtype is not dtype or t.shape != shape or t.get_device() != dev:
             raise ValueError(f"{what}: all ranks need the same dtype, shape and device")
         if not t.is_contiguous():
             raise ValueError(f"{what}: tensors must be contiguous")
+    return dev
 
 
 def _mode(mode) -> int:
@@ -238,14 +240,23 @@ def _mode(mode) -> int:
 
 def _stream(stream, device) -> int:
     """The HIP stream to enqueue on: the given one, else the current stream
-    of the tensors' device (which must be the current device, since the
-    library launches on the current device)."""
+    of the tensors' device (`device`: a torch.device or its index), which
+    must be the current device, since the library launches on the current
+    device.  torch's raw current-stream query, where it has one, returns the
+    same handle as torch.cuda.current_stream(...).cuda_stream at a fraction
+    of the cost."""
     torch = _torch()
-    if device.index is not None and device.index != torch.cuda.current_device():
-        raise ValueError(f"tensors live on {device} but the current device is cuda:{torch.cuda.current_device()}; "
+    idx = device if isinstance(device, int) else device.index
+    cur = torch.cuda.current_device()
+    if idx is not None and idx != cur:
+        raise ValueError(f"tensors live on cuda:{idx} but the current device is cuda:{cur}; "
                          "call inside torch.cuda.device(...)")
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(cur)
+    return torch.cuda.current_stream(cur).cuda_stream
 
 
 def _same_device(send, recv, what):
@@ -271,15 +282,16 @@ def vrc_allreduce(send, recv=None, mode: str = "fused", stream=None):
     ``recv=None`` allocates outputs; ``recv=send`` runs in place.
     """
     torch = _torch()
-    _check_ranks(send, "vrc_allreduce")
+    dev = _check_ranks(send, "vrc_allreduce")
     if recv is None:
         recv = [torch.empty_like(t) for t in send]
-    _check_ranks(recv, "vrc_allreduce")
-    if len(recv) != len(send) or recv[0].shape != send[0].shape or recv[0].dtype != send[0].dtype:
-        raise ValueError("vrc_allreduce: recv must match send")
-    _same_device(send, recv, "vrc_allreduce")
+    elif recv is not send:  # in place (the same list) needs no second check
+        _check_ranks(recv, "vrc_allreduce")
+        if len(recv) != len(send) or recv[0].shape != send[0].shape or recv[0].dtype != send[0].dtype:
+            raise ValueError("vrc_allreduce: recv must match send")
+        _same_device(send, recv, "vrc_allreduce")
     st = raw_allreduce([t.data_ptr() for t in send], [t.data_ptr() for t in recv], send[0].numel(),
-                       _dtype_code(send[0]), _mode(mode), _stream(stream, send[0].device))
+                       _dtype_code(send[0]), _mode(mode), _stream(stream, dev))
     if st != VRC_OK:
         raise VrcError(st, "vrc_allreduce")
     return recv

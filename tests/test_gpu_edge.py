@@ -357,6 +357,31 @@ def test_side_stream(vrc, orc):
         assert_bitwise(workloads.to_numpy(ys[3]), oracle_ar(orc, hx, "bf16", m)[3], f"side stream {m}")
 
 
+def test_binding_enqueues_on_the_current_stream(vrc):
+    """The binding's stream lookup returns the handle of torch's current
+    stream, on the default stream and inside a side-stream context, and an
+    explicit stream wins."""
+    say("binding stream lookup")
+    dev = torch.cuda.current_device()
+    assert vrc._stream(None, dev) == torch.cuda.current_stream().cuda_stream
+    assert vrc._stream(None, torch.device(DEV)) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert vrc._stream(None, dev) == s.cuda_stream != torch.cuda.default_stream().cuda_stream
+    assert vrc._stream(s, dev) == s.cuda_stream
+
+
+def test_in_place_list_through_the_binding(vrc, orc):
+    """recv given as the very list of inputs: the sums land in the inputs."""
+    say("in place, same list")
+    xs = workloads.random_ranks(8, 12345, "fp32", seed=409, device=DEV)
+    hx = host(xs)
+    ys = vrc.vrc_allreduce(xs, recv=xs, mode="fused")
+    torch.cuda.synchronize()
+    assert ys is xs
+    assert_bitwise(workloads.to_numpy(xs[5]), oracle_ar(orc, hx, "fp32", "fused")[5], "in place, same list")
+
+
 def test_errors_through_the_binding(vrc):
     say("errors")
     xs = workloads.random_ranks(4, 1000, "fp32", seed=408, device=DEV)
