@@ -498,3 +498,39 @@ def test_mixed_offsets_keep_the_full_grid(mode):
         assert launches(mixed) == launches(aligned)
     for kind, gx, gy, block, vec in launches(mixed):
         assert gx * gy * block >= CUS * 64, kind
+
+
+def phase_layout(g, kr, kl, skew, lanes_per_wg=256):
+    """Vector index (within a phase) of every (workgroup, lane, slot) that the
+    phased kernels' skewed layout assigns: slot k of lane j at k * L + j for
+    the first K - skew slots, then the even workgroups' last `skew` slots,
+    L / 2 lanes wide; the odd workgroups hold `skew` fewer LDS slots."""
+    import numpy as np
+    k = kr + kl
+    L = g * lanes_per_wg
+    b = np.arange(g)[:, None]
+    t = np.arange(lanes_per_wg)[None, :]
+    w, l = t // 64, t % 64
+    lane = (w * g + b) * 64 + l                    # [g, lanes]
+    lane_even = (w * (g // 2) + b // 2) * 64 + l
+    shared = k - skew
+    out = []
+    for s in range(k):
+        # every workgroup holds slot s below K - skew; above it only the even ones
+        take = np.ones((g, 1), bool) if s < shared else (b % 2 == 0)
+        v = s * L + lane if s < shared else shared * L + (s - shared) * (L // 2) + lane_even
+        out.append(np.broadcast_to(v, (g, lanes_per_wg))[np.broadcast_to(take, (g, lanes_per_wg))])
+    return np.concatenate(out), shared * L + skew * (L // 2)
+
+
+@pytest.mark.parametrize("g", [8, 32, 256])
+@pytest.mark.parametrize("kr,kl,skew", [(64, 32, 16), (32, 32, 8), (16, 32, 8), (24, 40, 8), (0, 40, 8),
+                                        (64, 32, 0)])
+def test_skewed_phase_layout_covers_every_vector_once(g, kr, kl, skew):
+    """For grids of whole XCD rounds, the skewed layout hands every vector of
+    a phase to exactly one (workgroup, lane, slot), and a phase holds
+    (K - skew) * L + skew * L / 2 vectors."""
+    import numpy as np
+    v, per_phase = phase_layout(g, kr, kl, skew)
+    assert v.size == per_phase
+    assert np.array_equal(np.sort(v), np.arange(per_phase))
